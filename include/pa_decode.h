@@ -1,0 +1,171 @@
+/*
+ * pa_decode.h -- C ABI of the MI355X (gfx950) paged-KV GQA decode-attention
+ * library libpa_decode.so.
+ *
+ * Operation (one decode step, one query token per sequence):
+ *   for every sequence b and query head h, with G = num_q_heads / num_kv_heads
+ *   and KV head g = floor(h / G), over the visible keys j in [lo_b, n_b):
+ *     s_j      = scale * q[b,h,:] . K_b[j,g,:]
+ *     out[b,h] = sum_j softmax(s)_j * V_b[j,g,:]
+ *     lse[b,h] = ln sum_j exp(s_j)                      (natural log)
+ *   where n_b = context_lens[b] and lo_b = max(0, n_b - sliding_window) when a
+ *   window is set (the window holds the W most recent keys, current one
+ *   included), else 0.  n_b - lo_b == 0 gives out = 0, lse = -inf.
+ *   Passages: output and LSE of paged-KV decode attention with a shuffled page
+ *   table, sliding window and batch > 1 -- TVM PR #20426, section
+ *   "Correctness"; K/V gathered per page through a block table and the
+ *   [kv_h, gqa] -> [H] head grouping -- the paged_attention_v2_pytorch.py
+ *   commit page, "KV gather" and the scores@V broadcast.
+ *
+ * How it is computed: the context is cut into partitions; one workgroup per
+ * (sequence, KV head, partition) keeps an online-softmax state (running max,
+ * denominator, weighted V) for all G query heads of the group, reading each
+ * K/V page once; a second kernel merges the partition states by log-sum-exp
+ * rescaling, (max, denominator) first and then the weighted outputs (the
+ * commit page's "Phase 1: Per-partition attention" / "Phase 2: Cross-
+ * partition reduction"; TVM PR #20426, section "Change", third bullet).  When
+ * a single partition covers every context the merge is skipped and the
+ * partial kernel writes out/lse itself (the host-side switch of TVM PR
+ * #20426, section "Change": short contexts keep a single-pass kernel).
+ *
+ * Conventions for every entry point:
+ *   - Returns PA_DECODE_OK (0) or a negative pa_decode_status.  No C++
+ *     exception crosses the ABI.
+ *   - All argument validation happens on the host before any HIP call.
+ *   - Device pointers are caller-owned; the library keeps none of them after
+ *     a call returns and never allocates device memory during pa_decode_run.
+ *   - pa_decode_run is asynchronous on the caller's HIP stream: no host
+ *     synchronisation, no allocation.  Calls on one handle from several host
+ *     threads must be serialised by the caller.
+ */
+#ifndef PA_DECODE_H
+#define PA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    PA_DECODE_OK = 0,
+    PA_DECODE_INVALID_ARG = -1,         /* null pointer, bad size, bad stride */
+    PA_DECODE_UNSUPPORTED = -2,         /* head_dim / page_size / dtype / G not built */
+    PA_DECODE_WORKSPACE_TOO_SMALL = -3, /* args.workspace_bytes below the plan's need */
+    PA_DECODE_HIP_ERROR = -4,           /* a HIP call failed; see pa_decode_last_hip_error */
+};
+
+/* Element types of q, the K/V caches and out (all three share one type). */
+enum {
+    PA_DTYPE_F32 = 0,
+    PA_DTYPE_F16 = 1,
+    PA_DTYPE_BF16 = 2,
+};
+
+/* Static problem description, fixed at pa_decode_create.
+ * Supported: head_dim in {64, 128, 256}; page_size 16; dtype in
+ * {F32 (head_dim 64 only), F16, BF16}; G = num_q_heads / num_kv_heads an
+ * integer in [1, 16]. */
+typedef struct pa_decode_desc {
+    int32_t num_q_heads;     /* Hq > 0 */
+    int32_t num_kv_heads;    /* Hkv > 0, divides Hq */
+    int32_t head_dim;        /* D */
+    int32_t page_size;       /* tokens per page */
+    int32_t dtype;           /* PA_DTYPE_* of q, k/v cache and out */
+    int32_t max_batch;       /* upper bound of args.batch */
+    int32_t max_context_len; /* upper bound of args.max_context_len */
+    int32_t device;          /* HIP device ordinal the handle runs on */
+} pa_decode_desc;
+
+/* Per-call arguments.  Element strides are in elements of the cache dtype. */
+typedef struct pa_decode_args {
+    const void* q;              /* device, [batch, Hq, D] contiguous */
+    const void* k_cache;        /* device, paged keys: element (page, kv, slot, d) at */
+    const void* v_cache;        /*   page*kv_stride_page + kv*kv_stride_head +      */
+                                /*   slot*kv_stride_slot + d (d contiguous);          */
+                                /*   [num_pages, Hkv, page_size, D] contiguous is     */
+                                /*   strides (Hkv*ps*D, ps*D, D); [num_pages, ps, Hkv, D] */
+                                /*   works too.  K and V share the strides.           */
+    int64_t kv_stride_page;
+    int64_t kv_stride_head;
+    int64_t kv_stride_slot;
+    int32_t num_pages;          /* pages in the pool (page ids must be < num_pages) */
+    const int32_t* page_table;  /* device, int32 [batch, pt_stride]; entry j of row b is */
+                                /*   the page of tokens [j*ps, (j+1)*ps) of sequence b   */
+    int32_t pt_stride;          /* row stride of page_table, >= ceil(max_context_len/ps) */
+    const int32_t* context_lens;/* device, int32 [batch], 0 <= n_b <= max_context_len */
+    int32_t batch;              /* B, 0 <= B <= desc.max_batch */
+    int32_t max_context_len;    /* host upper bound of context_lens (used to plan) */
+    float scale;                /* multiplies q.k */
+    int32_t sliding_window;     /* <= 0: no window; else keys [n_b - W, n_b) */
+    int32_t partition_size;     /* 0: planner's choice; else tokens per partition, */
+                                /*   a positive multiple of page_size */
+    void* out;                  /* device, [batch, Hq, D] contiguous, desc.dtype */
+    float* lse;                 /* device, float32 [batch, Hq], may be NULL */
+    void* workspace;            /* device scratch of >= workspace_bytes needed by the */
+    size_t workspace_bytes;     /*   plan (pa_decode_workspace_size); may be NULL/0   */
+                                /*   when that size is 0                              */
+} pa_decode_args;
+
+/* The plan pa_decode_run derives from (batch, max_context_len, window,
+ * partition_size) and the device's compute-unit count. */
+typedef struct pa_decode_plan {
+    int32_t split;              /* 1: partial kernel + merge kernel; 0: partial only */
+    int32_t partition_size;     /* S, tokens per partition */
+    int32_t num_partitions;     /* partitions per (sequence, KV head) in the grid */
+    int32_t waves_per_group;    /* waves per workgroup of the partial kernel */
+    int32_t pages_per_block;    /* pages each wave holds in flight per step */
+    int32_t grid_partial[3];    /* partial kernel grid (x = partition, y = KV head, z = b) */
+    int32_t block_partial;      /* threads per workgroup of the partial kernel */
+    int32_t grid_merge[3];      /* merge kernel grid (0s when split == 0) */
+    int32_t block_merge;
+    int32_t num_cus;            /* compute units the plan was made for */
+    int64_t workspace_bytes;    /* bytes of workspace the plan needs */
+} pa_decode_plan;
+
+typedef struct pa_decode_handle_s* pa_decode_handle;
+
+/* Validate desc, read the device's properties and return a handle.
+ * Errors: INVALID_ARG (null pointer, non-positive sizes, Hq % Hkv != 0),
+ * UNSUPPORTED (shape or dtype not built), HIP_ERROR (no such device). */
+int pa_decode_create(const pa_decode_desc* desc, pa_decode_handle* handle);
+
+/* Release the handle (host memory only).  NULL is accepted. */
+int pa_decode_destroy(pa_decode_handle handle);
+
+/* Bytes of device workspace pa_decode_run needs for these sizes
+ * (partition_size 0 = the planner's choice).  Pure host computation. */
+int pa_decode_workspace_size(pa_decode_handle handle, int32_t batch, int32_t max_context_len,
+                             int32_t sliding_window, int32_t partition_size, size_t* bytes);
+
+/* Run one decode step on `stream` (a hipStream_t; NULL = the null stream).
+ * Errors: INVALID_ARG / UNSUPPORTED / WORKSPACE_TOO_SMALL from host checks,
+ * HIP_ERROR when a launch fails.  Page ids, context lengths and page-table
+ * rows live in device memory and are the caller's contract: every page id
+ * read (rows b, entries [lo_b/ps, ceil(n_b/ps))) must be < num_pages and
+ * n_b <= max_context_len.  Entries past ceil(n_b/ps), keys before lo_b and
+ * slots past n_b are never read, so they may hold anything. */
+int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* stream);
+
+/* The plan of the last successful pa_decode_run on this handle. */
+int pa_decode_last_plan(pa_decode_handle handle, pa_decode_plan* plan);
+
+/* Plan without a handle or device (pure host): the same planner that
+ * pa_decode_run uses, for a given compute-unit count. */
+int pa_decode_plan_query(const pa_decode_desc* desc, int32_t num_cus, int32_t batch,
+                         int32_t max_context_len, int32_t sliding_window,
+                         int32_t partition_size, pa_decode_plan* plan);
+
+/* Last hipError_t recorded on the handle (0 when none). */
+int pa_decode_last_hip_error(pa_decode_handle handle);
+
+/* Static text for a status code. */
+const char* pa_decode_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_DECODE_H */

@@ -1,0 +1,289 @@
+"""Thin ctypes binding of libpa_decode.so (include/pa_decode.h).
+
+The functions carry the C names and only marshal arguments; every step of the
+decode-attention computation runs in the library's HIP kernels.  PyTorch is
+used for device memory and streams only (``PagedDecode`` allocates out, lse
+and the workspace with torch and passes raw pointers).  There is no fallback:
+if the library is missing or fails, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch  # loaded first so the library binds to the same HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa_decode.so")
+
+PA_DECODE_OK = 0
+PA_DECODE_INVALID_ARG = -1
+PA_DECODE_UNSUPPORTED = -2
+PA_DECODE_WORKSPACE_TOO_SMALL = -3
+PA_DECODE_HIP_ERROR = -4
+
+PA_DTYPE_F32 = 0
+PA_DTYPE_F16 = 1
+PA_DTYPE_BF16 = 2
+
+DTYPE_CODE = {torch.float32: PA_DTYPE_F32, torch.float16: PA_DTYPE_F16,
+              torch.bfloat16: PA_DTYPE_BF16}
+
+# Symbols include/pa_decode.h declares.
+EXPORTED = ["pa_decode_create", "pa_decode_destroy", "pa_decode_workspace_size",
+            "pa_decode_run", "pa_decode_last_plan", "pa_decode_plan_query",
+            "pa_decode_last_hip_error", "pa_decode_status_string"]
+
+
+class PaDecodeDesc(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("max_context_len", ctypes.c_int32), ("device", ctypes.c_int32)]
+
+
+class PaDecodeArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p),
+                ("v_cache", ctypes.c_void_p), ("kv_stride_page", ctypes.c_int64),
+                ("kv_stride_head", ctypes.c_int64), ("kv_stride_slot", ctypes.c_int64),
+                ("num_pages", ctypes.c_int32), ("page_table", ctypes.c_void_p),
+                ("pt_stride", ctypes.c_int32), ("context_lens", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("sliding_window", ctypes.c_int32),
+                ("partition_size", ctypes.c_int32), ("out", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class PaDecodePlan(ctypes.Structure):
+    _fields_ = [("split", ctypes.c_int32), ("partition_size", ctypes.c_int32),
+                ("num_partitions", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
+                ("pages_per_block", ctypes.c_int32), ("grid_partial", ctypes.c_int32 * 3),
+                ("block_partial", ctypes.c_int32), ("grid_merge", ctypes.c_int32 * 3),
+                ("block_merge", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {"split": self.split, "partition_size": self.partition_size,
+                "num_partitions": self.num_partitions, "waves_per_group": self.waves_per_group,
+                "pages_per_block": self.pages_per_block,
+                "grid_partial": list(self.grid_partial), "block_partial": self.block_partial,
+                "grid_merge": list(self.grid_merge), "block_merge": self.block_merge,
+                "num_cus": self.num_cus, "workspace_bytes": self.workspace_bytes}
+
+
+class PaDecodeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (what, pa_decode_status_string(status), status))
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: Optional[str] = None):
+    """Load libpa_decode.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError("libpa_decode.so is not built (%s); run "
+                               "`python -m paged_kv_decode_amd.build`" % p)
+        lib = ctypes.CDLL(p)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        lib.pa_decode_create.argtypes = [ctypes.POINTER(PaDecodeDesc), ctypes.POINTER(vp)]
+        lib.pa_decode_destroy.argtypes = [vp]
+        lib.pa_decode_workspace_size.argtypes = [vp, i32, i32, i32, i32,
+                                                 ctypes.POINTER(ctypes.c_size_t)]
+        lib.pa_decode_run.argtypes = [vp, ctypes.POINTER(PaDecodeArgs), vp]
+        lib.pa_decode_last_plan.argtypes = [vp, ctypes.POINTER(PaDecodePlan)]
+        lib.pa_decode_plan_query.argtypes = [ctypes.POINTER(PaDecodeDesc), i32, i32, i32, i32,
+                                             i32, ctypes.POINTER(PaDecodePlan)]
+        lib.pa_decode_last_hip_error.argtypes = [vp]
+        lib.pa_decode_status_string.argtypes = [ctypes.c_int]
+        lib.pa_decode_status_string.restype = ctypes.c_char_p
+        for name in EXPORTED:
+            if name != "pa_decode_status_string":
+                getattr(lib, name).restype = ctypes.c_int
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _check(status: int, what: str):
+    if status != PA_DECODE_OK:
+        raise PaDecodeError(status, what)
+
+
+def pa_decode_status_string(status: int) -> str:
+    return load_library().pa_decode_status_string(int(status)).decode()
+
+
+def pa_decode_create(desc: PaDecodeDesc) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(load_library().pa_decode_create(ctypes.byref(desc), ctypes.byref(h)),
+           "pa_decode_create")
+    return h
+
+
+def pa_decode_destroy(handle) -> None:
+    _check(load_library().pa_decode_destroy(handle), "pa_decode_destroy")
+
+
+def pa_decode_workspace_size(handle, batch: int, max_context_len: int, sliding_window: int = 0,
+                             partition_size: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().pa_decode_workspace_size(handle, batch, max_context_len,
+                                                   sliding_window, partition_size,
+                                                   ctypes.byref(n)),
+           "pa_decode_workspace_size")
+    return int(n.value)
+
+
+def pa_decode_run(handle, args: PaDecodeArgs, stream: int = 0) -> None:
+    _check(load_library().pa_decode_run(handle, ctypes.byref(args), ctypes.c_void_p(stream)),
+           "pa_decode_run")
+
+
+def pa_decode_last_plan(handle) -> PaDecodePlan:
+    plan = PaDecodePlan()
+    _check(load_library().pa_decode_last_plan(handle, ctypes.byref(plan)), "pa_decode_last_plan")
+    return plan
+
+
+def pa_decode_plan_query(desc: PaDecodeDesc, num_cus: int, batch: int, max_context_len: int,
+                         sliding_window: int = 0, partition_size: int = 0) -> PaDecodePlan:
+    plan = PaDecodePlan()
+    _check(load_library().pa_decode_plan_query(ctypes.byref(desc), num_cus, batch,
+                                               max_context_len, sliding_window, partition_size,
+                                               ctypes.byref(plan)),
+           "pa_decode_plan_query")
+    return plan
+
+
+def pa_decode_last_hip_error(handle) -> int:
+    return int(load_library().pa_decode_last_hip_error(handle))
+
+
+def make_desc(num_q_heads, num_kv_heads, head_dim, dtype, max_batch, max_context_len,
+              page_size=16, device=0) -> PaDecodeDesc:
+    code = DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return PaDecodeDesc(num_q_heads, num_kv_heads, head_dim, page_size, code, max_batch,
+                        max_context_len, device)
+
+
+class PagedDecode:
+    """Handle-owning front end for torch tensors on one GPU.
+
+    ``make_args`` builds the C argument block once (a timing loop can reuse it
+    with ``run_args``); ``__call__`` allocates out/lse/workspace with torch.
+    """
+
+    def __init__(self, num_q_heads, num_kv_heads, head_dim, dtype, max_batch,
+                 max_context_len, page_size=16, device=0):
+        self.desc = make_desc(num_q_heads, num_kv_heads, head_dim, dtype, max_batch,
+                              max_context_len, page_size, device)
+        self.dtype = dtype
+        self.device = torch.device("cuda", device)
+        self.handle = pa_decode_create(self.desc)
+        self._workspace = None
+
+    def close(self):
+        if self.handle is not None:
+            pa_decode_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_size(self, batch, max_context_len, sliding_window=0, partition_size=0):
+        return pa_decode_workspace_size(self.handle, batch, max_context_len, sliding_window,
+                                        partition_size)
+
+    def workspace(self, nbytes: int) -> torch.Tensor:
+        """A cached uint8 device buffer of at least nbytes (never shrinks)."""
+        if self._workspace is None or self._workspace.numel() < nbytes:
+            self._workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8,
+                                          device=self.device)
+        return self._workspace
+
+    def make_args(self, q, k_cache, v_cache, page_table, context_lens, scale, out, lse=None,
+                  max_context_len=None, sliding_window=0, partition_size=0,
+                  workspace=None) -> PaDecodeArgs:
+        for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                        ("page_table", page_table), ("context_lens", context_lens),
+                        ("out", out)):
+            if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+                raise TypeError("%s must be a device tensor" % name)
+        if q.dtype != self.dtype or k_cache.dtype != self.dtype or \
+                v_cache.dtype != self.dtype or out.dtype != self.dtype:
+            raise TypeError("q, k/v caches and out must be %s" % self.dtype)
+        if not q.is_contiguous() or not out.is_contiguous():
+            raise ValueError("q and out must be contiguous")
+        if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+            raise ValueError("k_cache and v_cache must share shape and strides")
+        if k_cache.dim() != 4 or k_cache.stride(3) != 1:
+            raise ValueError("caches must be [num_pages, Hkv, page_size, D] with D contiguous")
+        if page_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
+            raise TypeError("page_table and context_lens must be int32")
+        if page_table.dim() != 2 or page_table.stride(1) != 1:
+            raise ValueError("page_table must be [B, pt_stride] with unit inner stride")
+        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+            raise TypeError("lse must be contiguous float32")
+        B = q.shape[0]
+        if max_context_len is None:
+            max_context_len = int(context_lens.max().item()) if B else 0
+        ws_bytes = self.workspace_size(B, max_context_len, sliding_window, partition_size)
+        if workspace is None:
+            workspace = self.workspace(ws_bytes)
+        a = PaDecodeArgs()
+        a.q = q.data_ptr()
+        a.k_cache = k_cache.data_ptr()
+        a.v_cache = v_cache.data_ptr()
+        a.kv_stride_page = k_cache.stride(0)
+        a.kv_stride_head = k_cache.stride(1)
+        a.kv_stride_slot = k_cache.stride(2)
+        a.num_pages = k_cache.shape[0]
+        a.page_table = page_table.data_ptr()
+        a.pt_stride = page_table.stride(0)
+        a.context_lens = context_lens.data_ptr()
+        a.batch = B
+        a.max_context_len = max_context_len
+        a.scale = float(scale)
+        a.sliding_window = int(sliding_window)
+        a.partition_size = int(partition_size)
+        a.out = out.data_ptr()
+        a.lse = lse.data_ptr() if lse is not None else None
+        a.workspace = workspace.data_ptr() if workspace is not None else None
+        a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        a._keep = (q, k_cache, v_cache, page_table, context_lens, out, lse, workspace)
+        return a
+
+    def run_args(self, args: PaDecodeArgs, stream: Optional[int] = None) -> None:
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        pa_decode_run(self.handle, args, stream)
+
+    def __call__(self, q, k_cache, v_cache, page_table, context_lens, scale,
+                 max_context_len=None, sliding_window=0, partition_size=0, out=None,
+                 lse=None):
+        B, Hq, D = q.shape
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=self.dtype, device=q.device)
+        if lse is None:
+            lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        args = self.make_args(q, k_cache, v_cache, page_table, context_lens, scale, out, lse,
+                              max_context_len, sliding_window, partition_size)
+        self.run_args(args)
+        return out, lse
+
+    def last_plan(self) -> PaDecodePlan:
+        return pa_decode_last_plan(self.handle)

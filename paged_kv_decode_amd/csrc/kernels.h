@@ -1,0 +1,53 @@
+// kernels.h -- launch interface of the gfx950 decode-attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace pa {
+
+// Arguments of the partial kernel (one workgroup per (partition, KV head, b)).
+struct PartialParams {
+    const void* q;            // [B, Hq, D]
+    const void* k;            // paged K, element strides below (D contiguous)
+    const void* v;            // paged V, same strides
+    int64_t stride_page, stride_head, stride_slot;
+    const int32_t* page_table;
+    int32_t pt_stride;
+    const int32_t* context_lens;
+    int32_t num_q_heads;
+    int32_t group;            // actual G = Hq / Hkv
+    int32_t partition_size;   // S tokens
+    int32_t num_partitions;   // P (grid x)
+    int32_t window;           // <= 0: none
+    float scale_log2;         // scale * log2(e)
+    int32_t split;            // 1: write partition states; 0: write out/lse
+    float* ws_o;              // [B, Hq, P, D]
+    float* ws_m;              // [B, Hq, P], base-2 running max
+    float* ws_l;              // [B, Hq, P], denominators
+    void* out;                // [B, Hq, D]
+    float* lse;               // [B, Hq] or null
+};
+
+// Arguments of the merge kernel (one workgroup per (query head, b)).
+struct MergeParams {
+    const int32_t* context_lens;
+    int32_t num_q_heads;
+    int32_t partition_size;
+    int32_t num_partitions;
+    int32_t window;
+    const float* ws_o;
+    const float* ws_m;
+    const float* ws_l;
+    void* out;
+    float* lse;
+};
+
+// dtype: PA_DTYPE_*; group_t: an instantiated group size (template_group).
+hipError_t launch_partial(int dtype, int head_dim, int group_t, const PartialParams& p,
+                          dim3 grid, dim3 block, size_t lds_bytes, hipStream_t stream);
+hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, dim3 grid, dim3 block,
+                        hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,227 @@
+// pa_decode_api.cpp -- the C ABI declared in include/pa_decode.h.
+//
+// Host side of one decode step: validate the arguments (no HIP call before
+// that), plan the partitioning for the device's compute units, launch the
+// partial kernel and, when the context is split, the merge kernel, all on the
+// caller's stream.  Nothing here synchronises or allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "kernels.h"
+#include "pa_decode.h"
+#include "planner.h"
+
+struct pa_decode_handle_s {
+    pa_decode_desc desc;
+    int num_cus;
+    pa_decode_plan last_plan;
+    bool has_plan;
+    int last_hip_error;
+};
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_args(const pa_decode_desc& d, const pa_decode_args& a)
+{
+    if (a.batch < 0 || a.batch > d.max_batch || a.max_context_len < 0 ||
+        a.max_context_len > d.max_context_len || a.partition_size < 0)
+        return PA_DECODE_INVALID_ARG;
+    if (a.partition_size > 0 && a.partition_size % d.page_size != 0)
+        return PA_DECODE_INVALID_ARG;
+    if (!std::isfinite(a.scale))
+        return PA_DECODE_INVALID_ARG;
+    if (a.batch == 0)
+        return PA_DECODE_OK;
+    if (!a.q || !a.k_cache || !a.v_cache || !a.page_table || !a.context_lens || !a.out)
+        return PA_DECODE_INVALID_ARG;
+    if (a.num_pages <= 0 || a.pt_stride <= 0)
+        return PA_DECODE_INVALID_ARG;
+    if (int64_t(a.pt_stride) * d.page_size < int64_t(a.max_context_len))
+        return PA_DECODE_INVALID_ARG;
+    const int eb = pa::dtype_bytes(d.dtype);
+    // Strides: non-negative, 16-byte granular (each lane reads 16-byte chunks).
+    const int64_t strides[3] = {a.kv_stride_page, a.kv_stride_head, a.kv_stride_slot};
+    for (int64_t s : strides)
+        if (s < 0 || (s * eb) % 16 != 0)
+            return PA_DECODE_INVALID_ARG;
+    if (a.kv_stride_slot < d.head_dim)
+        return PA_DECODE_INVALID_ARG;
+    if (!aligned16(a.q) || !aligned16(a.k_cache) || !aligned16(a.v_cache) || !aligned16(a.out))
+        return PA_DECODE_INVALID_ARG;
+    return PA_DECODE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_create(const pa_decode_desc* desc, pa_decode_handle* handle)
+{
+    if (!desc || !handle)
+        return PA_DECODE_INVALID_ARG;
+    *handle = nullptr;
+    int st = pa::check_desc(*desc);
+    if (st != PA_DECODE_OK)
+        return st;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || desc->device >= count)
+        return PA_DECODE_HIP_ERROR;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, desc->device) !=
+            hipSuccess ||
+        cus <= 0)
+        return PA_DECODE_HIP_ERROR;
+    auto* h = new (std::nothrow) pa_decode_handle_s();
+    if (!h)
+        return PA_DECODE_HIP_ERROR;
+    h->desc = *desc;
+    h->num_cus = cus;
+    h->has_plan = false;
+    h->last_hip_error = 0;
+    *handle = h;
+    return PA_DECODE_OK;
+}
+
+int pa_decode_destroy(pa_decode_handle handle)
+{
+    delete handle;
+    return PA_DECODE_OK;
+}
+
+int pa_decode_workspace_size(pa_decode_handle handle, int32_t batch, int32_t max_context_len,
+                             int32_t sliding_window, int32_t partition_size, size_t* bytes)
+{
+    if (!handle || !bytes)
+        return PA_DECODE_INVALID_ARG;
+    pa_decode_plan plan;
+    int st = pa::make_plan(handle->desc, handle->num_cus, batch, max_context_len, sliding_window,
+                           partition_size, &plan);
+    if (st != PA_DECODE_OK)
+        return st;
+    *bytes = size_t(plan.workspace_bytes);
+    return PA_DECODE_OK;
+}
+
+int pa_decode_plan_query(const pa_decode_desc* desc, int32_t num_cus, int32_t batch,
+                         int32_t max_context_len, int32_t sliding_window, int32_t partition_size,
+                         pa_decode_plan* plan)
+{
+    if (!desc || !plan)
+        return PA_DECODE_INVALID_ARG;
+    return pa::make_plan(*desc, num_cus, batch, max_context_len, sliding_window, partition_size,
+                         plan);
+}
+
+int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* stream)
+{
+    if (!handle || !args)
+        return PA_DECODE_INVALID_ARG;
+    const pa_decode_desc& d = handle->desc;
+    const pa_decode_args& a = *args;
+    int st = check_args(d, a);
+    if (st != PA_DECODE_OK)
+        return st;
+    pa_decode_plan plan;
+    st = pa::make_plan(d, handle->num_cus, a.batch, a.max_context_len, a.sliding_window,
+                       a.partition_size, &plan);
+    if (st != PA_DECODE_OK)
+        return st;
+    if (plan.split && (!a.workspace || a.workspace_bytes < size_t(plan.workspace_bytes)))
+        return PA_DECODE_WORKSPACE_TOO_SMALL;
+    if (plan.split && !aligned16(a.workspace))
+        return PA_DECODE_INVALID_ARG;
+    handle->last_plan = plan;
+    handle->has_plan = true;
+    if (a.batch == 0)
+        return PA_DECODE_OK;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int G = d.num_q_heads / d.num_kv_heads;
+    const pa::WorkspaceLayout wl = pa::workspace_layout(d, a.batch, plan.num_partitions);
+    char* ws = static_cast<char*>(a.workspace);
+
+    pa::PartialParams pp;
+    pp.q = a.q;
+    pp.k = a.k_cache;
+    pp.v = a.v_cache;
+    pp.stride_page = a.kv_stride_page;
+    pp.stride_head = a.kv_stride_head;
+    pp.stride_slot = a.kv_stride_slot;
+    pp.page_table = a.page_table;
+    pp.pt_stride = a.pt_stride;
+    pp.context_lens = a.context_lens;
+    pp.num_q_heads = d.num_q_heads;
+    pp.group = G;
+    pp.partition_size = plan.partition_size;
+    pp.num_partitions = plan.num_partitions;
+    pp.window = a.sliding_window;
+    pp.scale_log2 = float(double(a.scale) * 1.4426950408889634);
+    pp.split = plan.split;
+    pp.ws_o = plan.split ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
+    pp.ws_m = plan.split ? reinterpret_cast<float*>(ws + wl.m_off) : nullptr;
+    pp.ws_l = plan.split ? reinterpret_cast<float*>(ws + wl.l_off) : nullptr;
+    pp.out = a.out;
+    pp.lse = a.lse;
+
+    const dim3 grid(plan.grid_partial[0], plan.grid_partial[1], plan.grid_partial[2]);
+    const dim3 block(plan.block_partial);
+    hipError_t e = pa::launch_partial(d.dtype, d.head_dim, pa::template_group(G), pp, grid, block,
+                                      pa::partial_lds_bytes(d, plan), s);
+    if (e != hipSuccess) {
+        handle->last_hip_error = int(e);
+        return PA_DECODE_HIP_ERROR;
+    }
+    if (plan.split) {
+        pa::MergeParams mp;
+        mp.context_lens = a.context_lens;
+        mp.num_q_heads = d.num_q_heads;
+        mp.partition_size = plan.partition_size;
+        mp.num_partitions = plan.num_partitions;
+        mp.window = a.sliding_window;
+        mp.ws_o = pp.ws_o;
+        mp.ws_m = pp.ws_m;
+        mp.ws_l = pp.ws_l;
+        mp.out = a.out;
+        mp.lse = a.lse;
+        const dim3 mgrid(plan.grid_merge[0], plan.grid_merge[1], plan.grid_merge[2]);
+        e = pa::launch_merge(d.dtype, d.head_dim, mp, mgrid, dim3(plan.block_merge), s);
+        if (e != hipSuccess) {
+            handle->last_hip_error = int(e);
+            return PA_DECODE_HIP_ERROR;
+        }
+    }
+    return PA_DECODE_OK;
+}
+
+int pa_decode_last_plan(pa_decode_handle handle, pa_decode_plan* plan)
+{
+    if (!handle || !plan || !handle->has_plan)
+        return PA_DECODE_INVALID_ARG;
+    *plan = handle->last_plan;
+    return PA_DECODE_OK;
+}
+
+int pa_decode_last_hip_error(pa_decode_handle handle)
+{
+    return handle ? handle->last_hip_error : 0;
+}
+
+const char* pa_decode_status_string(int status)
+{
+    switch (status) {
+    case PA_DECODE_OK: return "ok";
+    case PA_DECODE_INVALID_ARG: return "invalid argument";
+    case PA_DECODE_UNSUPPORTED: return "unsupported configuration";
+    case PA_DECODE_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PA_DECODE_HIP_ERROR: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

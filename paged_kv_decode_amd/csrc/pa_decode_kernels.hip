@@ -1,0 +1,560 @@
+// pa_decode_kernels.hip -- gfx950 kernels of paged-KV GQA decode attention.
+//
+// Partial kernel: one workgroup of NW wave64s per (partition, KV head,
+// sequence).  The partition's pages are dealt to the waves in blocks of NB
+// pages.  For each block a wave
+//   1. reads the block's page ids from the page table (uniform, scalar loads)
+//      and issues 16-byte loads of every K and V row chunk of those pages;
+//   2. forms the scores of all G query heads of the group against the
+//      block's 16-token pages with one MFMA chain per page: the G query rows
+//      (zero-padded to 16) are the A operand, the page's 16 key rows the B
+//      operand, head_dim the reduction axis, so each K byte is read once per
+//      group and the 16-lane result rows line up with the tokens;
+//   3. updates the per-head online-softmax state (running max, denominator)
+//      with 16-lane DPP reductions, and publishes the block's probabilities
+//      through a small per-wave LDS buffer;
+//   4. accumulates P.V on the vector ALUs: each lane owns one 16-byte chunk
+//      of head_dim for 64/CH token rows and all G heads, so each V byte is
+//      also read once per group and converted to f32 once.
+// The waves' states are then combined in LDS (running max first, then the
+// rescaled denominators and outputs) and the workgroup writes either the
+// partition state (o normalised, max, denominator) for the merge kernel or,
+// when one partition covers the context, out and lse directly.
+//
+// Merge kernel: one workgroup per (query head, sequence): phase 1 takes the
+// maximum of the partition maxima and the rescaled sum of denominators,
+// phase 2 sums the partition outputs weighted by rescale_p / total, then
+// lse = ln(total) + max.  The two phases follow the paged_attention_v2
+// commit page, "Phase 2: Cross-partition reduction" (global max; rescale =
+// exp(m_p - max) * l_p; out = sum rescale_p / sum(rescale) * o_p), and TVM
+// PR #20426, section "Change", third bullet ((max, denom) first, then the
+// weighted outputs).
+//
+// Exponentials are base 2 throughout (scores pre-multiplied by log2(e));
+// lse is converted back to the natural logarithm on output.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+#include "pa_decode.h"
+
+namespace pa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kPage = 16;
+constexpr float kLn2 = 0.693147180559945309f;
+
+template <int DT> struct Elt;
+template <> struct Elt<PA_DTYPE_F32> { static constexpr int bytes = 4; };
+template <> struct Elt<PA_DTYPE_F16> { static constexpr int bytes = 2; };
+template <> struct Elt<PA_DTYPE_BF16> { static constexpr int bytes = 2; };
+
+// ---- cross-lane helpers (wave64, DPP within 16-lane rows) ----
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Max / sum over the 16 lanes of each DPP row (xor 1, xor 2, half mirror, mirror).
+__device__ __forceinline__ float row16_max(float x)
+{
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    x = fmaxf(x, dpp<0x140>(x));
+    return x;
+}
+
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    x += dpp<0x140>(x);
+    return x;
+}
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    // LDS traffic of one wave is ordered; this keeps the compiler from moving
+    // LDS accesses across the exchange point and waits for them to land.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- element conversion of one 16-byte chunk ----
+template <int DT> struct Chunk;
+
+template <> struct Chunk<PA_DTYPE_F16> {
+    __device__ static void to_f32(u32x4 r, float* f)
+    {
+        f16x8 h = __builtin_bit_cast(f16x8, r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = (float)h[e];
+    }
+    __device__ static f32x4 mfma(u32x4 a, u32x4 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+};
+
+template <> struct Chunk<PA_DTYPE_BF16> {
+    __device__ static void to_f32(u32x4 r, float* f)
+    {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[2 * e] = __uint_as_float(r[e] << 16);
+            f[2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
+        }
+    }
+    __device__ static f32x4 mfma(u32x4 a, u32x4 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+
+template <> struct Chunk<PA_DTYPE_F32> {
+    __device__ static void to_f32(u32x4 r, float* f)
+    {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(r[e]);
+    }
+    __device__ static f32x4 mfma(u32x4 a, u32x4 b, f32x4 c)
+    {
+        // Four K=4 steps, one per float of the chunk (same k slot in A and B).
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(b[e]), c,
+                                                     0, 0, 0);
+        return c;
+    }
+};
+
+template <int DT> __device__ __forceinline__ void store_out(void* out, size_t idx, float x);
+template <> __device__ __forceinline__ void store_out<PA_DTYPE_F32>(void* out, size_t idx, float x)
+{
+    static_cast<float*>(out)[idx] = x;
+}
+template <> __device__ __forceinline__ void store_out<PA_DTYPE_F16>(void* out, size_t idx, float x)
+{
+    static_cast<_Float16*>(out)[idx] = (_Float16)x;
+}
+template <> __device__ __forceinline__ void store_out<PA_DTYPE_BF16>(void* out, size_t idx, float x)
+{
+    static_cast<__bf16*>(out)[idx] = (__bf16)x;
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) { return *static_cast<const u32x4*>(p); }
+
+// ---------------------------------------------------------------------------
+// Partial kernel.
+//   DT: element type; D: head_dim; G: instantiated group size (>= actual);
+//   NB: pages per block.
+// Lane maps (lane = 0..63, i16 = lane % 16, grp = lane / 16):
+//   K / MFMA:  lane loads chunk 4*ks + grp of key row i16 of a page,
+//              ks = 0..KS-1; the MFMA result element r of the lane is the score
+//              of query head 4*grp + r against token i16.
+//   V / P.V:   lane owns chunk c = lane % CH of token rows rho = lane / CH,
+//              rho + R, ..., rho + R*(KS-1) of a page.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int G, int NB>
+__global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
+{
+    constexpr int EB = Elt<DT>::bytes;
+    constexpr int CH = D * EB / 16;   // 16-byte chunks per key row
+    constexpr int EPC = 16 / EB;      // elements per chunk
+    constexpr int KS = CH / 4;        // chunks per lane per page (K and V alike)
+    constexpr int R = kWave / CH;     // token rows of the P.V map
+    constexpr int GP4 = (G + 3) / 4 * 4;
+    constexpr int HG = (G + 3) / 4;   // 16-lane groups that carry real heads
+    static_assert(KS * 4 == CH && R * CH == kWave && R * KS == kPage, "lane map");
+
+    extern __shared__ float smem[];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    const int prel = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int Gact = prm.group;
+
+    const int n = prm.context_lens[b];
+    const int lo = (prm.window > 0 && n > prm.window) ? n - prm.window : 0;
+    const int S = prm.partition_size;
+    const int pabs = lo / S + prel;
+    const int t0 = max(pabs * S, lo);
+    const int t1 = min(pabs * S + S, n);
+    if (t0 >= t1) {
+        if (!prm.split && prel == 0) {
+            // Empty context: out = 0, lse = -inf.
+            for (int idx = threadIdx.x; idx < Gact * D; idx += blockDim.x) {
+                const int h = kvh * Gact + idx / D;
+                store_out<DT>(prm.out, (size_t(b) * prm.num_q_heads + h) * D + idx % D, 0.f);
+            }
+            if (prm.lse && threadIdx.x < Gact)
+                prm.lse[size_t(b) * prm.num_q_heads + kvh * Gact + threadIdx.x] = -INFINITY;
+        }
+        return;
+    }
+
+    const int i16 = lane & 15, grp = lane >> 4;
+    const int rho = lane / CH, c = lane % CH;
+
+    // q as the MFMA A operand: row i16 = query head kvh*G + i16 (zero past G).
+    u32x4 qa[KS];
+    {
+        const bool real = i16 < Gact;
+        const char* qrow = static_cast<const char*>(prm.q) +
+                           (size_t(b) * prm.num_q_heads + size_t(kvh) * Gact + (real ? i16 : 0)) * D * EB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 z = {0u, 0u, 0u, 0u};
+            qa[ks] = real ? load16(qrow + (4 * ks + grp) * 16) : z;
+        }
+    }
+
+    const int64_t ss = prm.stride_slot;
+    const int64_t k_lane_off = int64_t(i16) * ss + int64_t(grp) * EPC;
+    const int64_t v_lane_off = int64_t(rho) * ss + int64_t(c) * EPC;
+    const int32_t* pt_row = prm.page_table + size_t(b) * prm.pt_stride;
+    const char* kbase = static_cast<const char*>(prm.k) + int64_t(kvh) * prm.stride_head * EB;
+    const char* vbase = static_cast<const char*>(prm.v) + int64_t(kvh) * prm.stride_head * EB;
+
+    float m_run[4], l_run[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        m_run[r] = -INFINITY;
+        l_run[r] = 0.f;
+    }
+    float acc[G][EPC];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[g][e] = 0.f;
+
+    float* pbuf = smem + wave * (NB * kPage * GP4 + GP4);
+    float* abuf = pbuf + NB * kPage * GP4;
+
+    const int pg0 = t0 / kPage, pg1 = (t1 + kPage - 1) / kPage;
+    const int nblk = (pg1 - pg0 + NB - 1) / NB;
+
+    for (int blk = wave; blk < nblk; blk += nw) {
+        const int pgb = pg0 + blk * NB;
+        const int nbv = min(NB, pg1 - pgb);
+        u32x4 kr[NB][KS], vr[NB][KS];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            if (nb < nbv) {
+                const int64_t page = pt_row[pgb + nb];
+                const char* kp = kbase + page * prm.stride_page * EB;
+                const char* vp = vbase + page * prm.stride_page * EB;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    kr[nb][ks] = load16(kp + (k_lane_off + int64_t(4 * ks) * EPC) * EB);
+#pragma unroll
+                for (int i = 0; i < KS; ++i)
+                    vr[nb][i] = load16(vp + (v_lane_off + int64_t(R * i) * ss) * EB);
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    kr[nb][ks] = u32x4{0u, 0u, 0u, 0u};
+                    vr[nb][ks] = u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+
+        // Scores (base 2) of head 4*grp + r against token i16 of each page.
+        float s[NB][4];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) d = Chunk<DT>::mfma(qa[ks], kr[nb][ks], d);
+            const int tok = (pgb + nb) * kPage + i16;
+            const bool ok = nb < nbv && tok >= t0 && tok < t1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[nb][r] = ok ? d[r] * prm.scale_log2 : -INFINITY;
+        }
+
+        float alpha[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float bm = s[0][r];
+#pragma unroll
+            for (int nb = 1; nb < NB; ++nb) bm = fmaxf(bm, s[nb][r]);
+            bm = row16_max(bm);
+            const float mnew = fmaxf(m_run[r], bm);
+            alpha[r] = fast_exp2(m_run[r] - mnew);
+            float ps = 0.f;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                s[nb][r] = fast_exp2(s[nb][r] - mnew);
+                ps += s[nb][r];
+            }
+            l_run[r] = alpha[r] * l_run[r] + ps;
+            m_run[r] = mnew;
+        }
+
+        // Publish p[page][token][head] and alpha[head] for the P.V lane map.
+        if (grp < HG) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                f32x4 pv = {s[nb][0], s[nb][1], s[nb][2], s[nb][3]};
+                *reinterpret_cast<f32x4*>(pbuf + (nb * kPage + i16) * GP4 + 4 * grp) = pv;
+            }
+            if (i16 == 0) {
+                f32x4 av = {alpha[0], alpha[1], alpha[2], alpha[3]};
+                *reinterpret_cast<f32x4*>(abuf + 4 * grp) = av;
+            }
+        }
+        wave_lds_sync();
+
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float a = abuf[g];
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[g][e] *= a;
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            if (nb < nbv) {
+                const int pgtok = (pgb + nb) * kPage;
+                const bool full = pgtok >= t0 && pgtok + kPage <= t1;
+#pragma unroll
+                for (int i = 0; i < KS; ++i) {
+                    const int t = rho + R * i;
+                    float vf[EPC];
+                    Chunk<DT>::to_f32(vr[nb][i], vf);
+                    if (!full) {
+                        const int tok = pgtok + t;
+                        const bool ok = tok >= t0 && tok < t1;
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e) vf[e] = ok ? vf[e] : 0.f;
+                    }
+                    const float* prow = pbuf + (nb * kPage + t) * GP4;
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const float p = prow[g];
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+                    }
+                }
+            }
+        }
+        wave_lds_sync();
+    }
+
+    // Wave-level reductions: denominators over the 16 token lanes, outputs
+    // over the R token rows.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) l_run[r] = row16_sum(l_run[r]);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+#pragma unroll
+            for (int off = CH; off < kWave; off <<= 1) acc[g][e] += __shfl_xor(acc[g][e], off);
+
+    // Workgroup combine in LDS.
+    __syncthreads();
+    float* cm = smem;               // [nw][GP4]
+    float* cl = cm + nw * GP4;      // [nw][GP4]
+    float* ca = cl + nw * GP4;      // [nw][G][D]
+    if (i16 == 0 && grp < HG) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            cm[wave * GP4 + 4 * grp + r] = m_run[r];
+            cl[wave * GP4 + 4 * grp + r] = l_run[r];
+        }
+    }
+    if (rho == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) ca[(wave * G + g) * D + c * EPC + e] = acc[g][e];
+    }
+    __syncthreads();
+
+    for (int idx = threadIdx.x; idx < Gact * D; idx += blockDim.x) {
+        const int g = idx / D, dd = idx % D;
+        float M = -INFINITY;
+        for (int w = 0; w < nw; ++w) M = fmaxf(M, cm[w * GP4 + g]);
+        float L = 0.f, o = 0.f;
+        for (int w = 0; w < nw; ++w) {
+            const float sc = fast_exp2(cm[w * GP4 + g] - M);
+            L += sc * cl[w * GP4 + g];
+            o += sc * ca[(w * G + g) * D + dd];
+        }
+        o = o / L;
+        const size_t h = size_t(b) * prm.num_q_heads + size_t(kvh) * Gact + g;
+        if (prm.split) {
+            const size_t row = h * prm.num_partitions + prel;
+            prm.ws_o[row * D + dd] = o;
+            if (dd == 0) {
+                prm.ws_m[row] = M;
+                prm.ws_l[row] = L;
+            }
+        } else {
+            store_out<DT>(prm.out, h * D + dd, o);
+            if (dd == 0 && prm.lse) prm.lse[h] = (M + log2f(L)) * kLn2;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Merge kernel: one workgroup (256 threads) per (query head, sequence).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float block_reduce(float x, float* red, bool is_max)
+{
+    // wave reduce with shuffles, then across the 4 waves through LDS
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float y = __shfl_xor(x, off);
+        x = is_max ? fmaxf(x, y) : x + y;
+    }
+    const int wave = threadIdx.x / kWave, nwv = blockDim.x / kWave;
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) red[wave] = x;
+    __syncthreads();
+    x = red[0];
+    for (int w = 1; w < nwv; ++w) x = is_max ? fmaxf(x, red[w]) : x + red[w];
+    return x;
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) void merge_kernel(const MergeParams prm)
+{
+    constexpr int TPR = D / 4;            // threads per partition row (float4 each)
+    __shared__ float red[8];
+    __shared__ f32x4 part[256];
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int n = prm.context_lens[b];
+    const int lo = (prm.window > 0 && n > prm.window) ? n - prm.window : 0;
+    const int S = prm.partition_size;
+    const int np = n > lo ? (n + S - 1) / S - lo / S : 0;
+    const size_t hrow = size_t(b) * prm.num_q_heads + h;
+    if (np == 0) {
+        for (int d = threadIdx.x; d < D; d += blockDim.x) store_out<DT>(prm.out, hrow * D + d, 0.f);
+        if (prm.lse && threadIdx.x == 0) prm.lse[hrow] = -INFINITY;
+        return;
+    }
+    const float* m = prm.ws_m + hrow * prm.num_partitions;
+    const float* l = prm.ws_l + hrow * prm.num_partitions;
+    const f32x4* o = reinterpret_cast<const f32x4*>(prm.ws_o + hrow * prm.num_partitions * D);
+
+    // Phase 1: global max, then the total of the rescaled denominators.
+    float mx = -INFINITY;
+    for (int p = threadIdx.x; p < np; p += blockDim.x) mx = fmaxf(mx, m[p]);
+    const float M = block_reduce(mx, red, true);
+    float tl = 0.f;
+    for (int p = threadIdx.x; p < np; p += blockDim.x) tl += fast_exp2(m[p] - M) * l[p];
+    const float L = block_reduce(tl, red + 4, false);
+
+    // Phase 2: weighted sum of partition outputs.
+    const int rpp = blockDim.x / TPR;     // partition rows per pass
+    const int row0 = threadIdx.x / TPR, c4 = threadIdx.x % TPR;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int p = row0; p < np; p += rpp) {
+        const float w = fast_exp2(m[p] - M) * l[p];
+        const f32x4 v = o[size_t(p) * TPR + c4];
+        a += w * v;
+    }
+    part[threadIdx.x] = a;
+    __syncthreads();
+    if (threadIdx.x < TPR) {
+        f32x4 t = part[threadIdx.x];
+        for (int r = 1; r < rpp; ++r) t += part[r * TPR + threadIdx.x];
+        const float inv = 1.f / L;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_out<DT>(prm.out, hrow * D + 4 * threadIdx.x + e, t[e] * inv);
+    }
+    if (prm.lse && threadIdx.x == 0) prm.lse[hrow] = (M + log2f(L)) * kLn2;
+}
+
+template <int DT, int D, int G>
+hipError_t launch_partial_t(const PartialParams& p, dim3 grid, dim3 block, size_t lds,
+                            hipStream_t stream)
+{
+    constexpr int EB = Elt<DT>::bytes;
+    constexpr int NB = (512 / (D * EB)) < 1 ? 1 : ((512 / (D * EB)) > 4 ? 4 : 512 / (D * EB));
+    hipLaunchKernelGGL((partial_kernel<DT, D, G, NB>), grid, block, lds, stream, p);
+    return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_partial_g(int group_t, const PartialParams& p, dim3 grid, dim3 block, size_t lds,
+                            hipStream_t stream)
+{
+    switch (group_t) {
+    case 1: return launch_partial_t<DT, D, 1>(p, grid, block, lds, stream);
+    case 2: return launch_partial_t<DT, D, 2>(p, grid, block, lds, stream);
+    case 4: return launch_partial_t<DT, D, 4>(p, grid, block, lds, stream);
+    case 6: return launch_partial_t<DT, D, 6>(p, grid, block, lds, stream);
+    case 8: return launch_partial_t<DT, D, 8>(p, grid, block, lds, stream);
+    case 16: return launch_partial_t<DT, D, 16>(p, grid, block, lds, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_partial(int dtype, int head_dim, int group_t, const PartialParams& p, dim3 grid,
+                          dim3 block, size_t lds, hipStream_t stream)
+{
+    if (dtype == PA_DTYPE_F32) {
+        if (head_dim == 64) return launch_partial_g<PA_DTYPE_F32, 64>(group_t, p, grid, block, lds, stream);
+        return hipErrorInvalidValue;
+    }
+    if (dtype == PA_DTYPE_F16) {
+        switch (head_dim) {
+        case 64: return launch_partial_g<PA_DTYPE_F16, 64>(group_t, p, grid, block, lds, stream);
+        case 128: return launch_partial_g<PA_DTYPE_F16, 128>(group_t, p, grid, block, lds, stream);
+        case 256: return launch_partial_g<PA_DTYPE_F16, 256>(group_t, p, grid, block, lds, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (dtype == PA_DTYPE_BF16) {
+        switch (head_dim) {
+        case 64: return launch_partial_g<PA_DTYPE_BF16, 64>(group_t, p, grid, block, lds, stream);
+        case 128: return launch_partial_g<PA_DTYPE_BF16, 128>(group_t, p, grid, block, lds, stream);
+        case 256: return launch_partial_g<PA_DTYPE_BF16, 256>(group_t, p, grid, block, lds, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, dim3 grid, dim3 block,
+                        hipStream_t stream)
+{
+#define PA_MERGE(DT, D) \
+    hipLaunchKernelGGL((merge_kernel<DT, D>), grid, block, 0, stream, p); \
+    return hipGetLastError();
+    if (dtype == PA_DTYPE_F32 && head_dim == 64) { PA_MERGE(PA_DTYPE_F32, 64) }
+    if (dtype == PA_DTYPE_F16) {
+        if (head_dim == 64) { PA_MERGE(PA_DTYPE_F16, 64) }
+        if (head_dim == 128) { PA_MERGE(PA_DTYPE_F16, 128) }
+        if (head_dim == 256) { PA_MERGE(PA_DTYPE_F16, 256) }
+    }
+    if (dtype == PA_DTYPE_BF16) {
+        if (head_dim == 64) { PA_MERGE(PA_DTYPE_BF16, 64) }
+        if (head_dim == 128) { PA_MERGE(PA_DTYPE_BF16, 128) }
+        if (head_dim == 256) { PA_MERGE(PA_DTYPE_BF16, 256) }
+    }
+#undef PA_MERGE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -1,0 +1,165 @@
+// planner.cpp -- see planner.h.
+#include "planner.h"
+
+#include <algorithm>
+#include <cstdlib>
+
+namespace pa {
+
+int dtype_bytes(int dtype)
+{
+    switch (dtype) {
+    case PA_DTYPE_F32: return 4;
+    case PA_DTYPE_F16: return 2;
+    case PA_DTYPE_BF16: return 2;
+    default: return 0;
+    }
+}
+
+int pages_per_block(int head_dim, int dtype)
+{
+    int row = head_dim * dtype_bytes(dtype);
+    return std::max(1, std::min(4, 512 / row));
+}
+
+int template_group(int G)
+{
+    static const int built[] = {1, 2, 4, 6, 8, 16};
+    for (int g : built)
+        if (G <= g) return g;
+    return 0;
+}
+
+int check_desc(const pa_decode_desc& d)
+{
+    if (d.num_q_heads <= 0 || d.num_kv_heads <= 0 || d.head_dim <= 0 || d.page_size <= 0 ||
+        d.max_batch < 0 || d.max_context_len < 0 || d.device < 0)
+        return PA_DECODE_INVALID_ARG;
+    if (d.num_q_heads % d.num_kv_heads != 0)
+        return PA_DECODE_INVALID_ARG;
+    if (d.dtype != PA_DTYPE_F32 && d.dtype != PA_DTYPE_F16 && d.dtype != PA_DTYPE_BF16)
+        return PA_DECODE_UNSUPPORTED;
+    if (d.page_size != kPageSize)
+        return PA_DECODE_UNSUPPORTED;
+    if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256)
+        return PA_DECODE_UNSUPPORTED;
+    if (d.dtype == PA_DTYPE_F32 && d.head_dim != 64)
+        return PA_DECODE_UNSUPPORTED;
+    int G = d.num_q_heads / d.num_kv_heads;
+    if (G > kMaxGroup || template_group(G) == 0)
+        return PA_DECODE_UNSUPPORTED;
+    return PA_DECODE_OK;
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+WorkspaceLayout workspace_layout(const pa_decode_desc& d, int batch, int num_partitions)
+{
+    auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
+    size_t rows = size_t(batch) * size_t(d.num_q_heads) * size_t(num_partitions);
+    WorkspaceLayout w;
+    w.o_off = 0;
+    w.m_off = align(rows * size_t(d.head_dim) * sizeof(float));
+    w.l_off = w.m_off + align(rows * sizeof(float));
+    w.total = w.l_off + align(rows * sizeof(float));
+    return w;
+}
+
+int make_plan(const pa_decode_desc& d, int num_cus, int batch, int max_context_len,
+              int sliding_window, int partition_size, pa_decode_plan* plan)
+{
+    if (!plan)
+        return PA_DECODE_INVALID_ARG;
+    int st = check_desc(d);
+    if (st != PA_DECODE_OK)
+        return st;
+    if (num_cus <= 0 || batch < 0 || batch > d.max_batch || max_context_len < 0 ||
+        max_context_len > d.max_context_len || partition_size < 0)
+        return PA_DECODE_INVALID_ARG;
+    if (partition_size > 0 && partition_size % d.page_size != 0)
+        return PA_DECODE_INVALID_ARG;
+
+    const int ps = d.page_size;
+    const int nb = pages_per_block(d.head_dim, d.dtype);
+    const int units = batch * d.num_kv_heads;
+    const bool windowed = sliding_window > 0 && sliding_window < max_context_len;
+    const int64_t visible = windowed ? sliding_window : max_context_len;
+    // Pages a visible range can touch (one more when the window edge is not
+    // page aligned).
+    const int64_t vis_pages = ceil_div(std::max<int64_t>(visible, 1), ps) + (windowed ? 1 : 0);
+
+    int64_t S;
+    int nw;
+    if (partition_size > 0) {
+        S = partition_size;
+    } else {
+        // Aim for about 8 waves per compute unit over the whole grid, with at
+        // least one page per wave and at most 16 pages per wave.
+        const int64_t target_waves = int64_t(num_cus) * 8;
+        int64_t total_pages = int64_t(std::max(units, 1)) * vis_pages;
+        int64_t ppw = std::max<int64_t>(1, ceil_div(total_pages, target_waves));
+        ppw = std::min<int64_t>(ppw, 16);
+        S = int64_t(kMaxWavesPerGroup) * ppw * ps;
+    }
+    // A partition at least as long as any context: one partition, no merge.
+    int64_t P;
+    if (max_context_len == 0) {
+        P = 1;
+    } else if (windowed) {
+        P = std::min(ceil_div(max_context_len, S), ceil_div(visible, S) + 1);
+    } else {
+        P = ceil_div(max_context_len, S);
+    }
+    P = std::max<int64_t>(P, 1);
+    if (P > 65535)
+        return PA_DECODE_UNSUPPORTED;
+    const bool split = P > 1;
+    if (!split && partition_size == 0 && max_context_len > 0) {
+        // The unsplit path covers the whole context with one workgroup.
+        S = ceil_div(max_context_len, ps) * ps;
+    }
+    // Waves per workgroup: enough blocks of `nb` pages for each wave.
+    int64_t blocks = ceil_div(ceil_div(std::min<int64_t>(S, std::max<int64_t>(visible, 1)), ps) +
+                                  (windowed ? 1 : 0), nb);
+    nw = int(std::max<int64_t>(1, std::min<int64_t>(kMaxWavesPerGroup, blocks)));
+    // Keep the workgroup's combine buffer within 64 KiB of LDS.
+    {
+        const int G = template_group(d.num_q_heads / d.num_kv_heads);
+        const int gp4 = (G + 3) / 4 * 4;
+        const int64_t per_wave = int64_t(2 * gp4 + G * d.head_dim) * 4;
+        while (nw > 1 && nw * per_wave > 65536) --nw;
+    }
+
+    pa_decode_plan p = {};
+    p.split = split ? 1 : 0;
+    p.partition_size = int32_t(S);
+    p.num_partitions = int32_t(P);
+    p.waves_per_group = nw;
+    p.pages_per_block = nb;
+    p.grid_partial[0] = int32_t(P);
+    p.grid_partial[1] = d.num_kv_heads;
+    p.grid_partial[2] = batch;
+    p.block_partial = nw * 64;
+    if (split) {
+        p.grid_merge[0] = d.num_q_heads;
+        p.grid_merge[1] = batch;
+        p.grid_merge[2] = 1;
+        p.block_merge = kMergeThreads;
+        p.workspace_bytes = int64_t(workspace_layout(d, batch, int(P)).total);
+    }
+    p.num_cus = num_cus;
+    *plan = p;
+    return PA_DECODE_OK;
+}
+
+size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan)
+{
+    const int G = template_group(d.num_q_heads / d.num_kv_heads);
+    const int gp4 = (G + 3) / 4 * 4;
+    const int nw = plan.waves_per_group;
+    const size_t loop = size_t(nw) * size_t(plan.pages_per_block * kPageSize * gp4 + gp4);
+    const size_t comb = size_t(nw) * size_t(2 * gp4 + G * d.head_dim);
+    return std::max(loop, comb) * sizeof(float);
+}
+
+}  // namespace pa

@@ -1,0 +1,55 @@
+// planner.h -- host-side dispatch plan for paged-KV decode attention.
+//
+// Pure host C++: no HIP call, so it is unit-testable without a GPU.
+// The plan picks the partition size S (tokens per workgroup), the number of
+// partitions per (sequence, KV head), the waves per workgroup, and whether
+// the merge kernel runs at all.  A single partition per context means the
+// partial kernel writes out/lse directly (the unsplit path for short
+// contexts: TVM PR #20426, section "Change", host-side switch between a
+// single-pass nest and the sharded one); otherwise the context is split and
+// the partition states are merged by log-sum-exp (the paged_attention_v2
+// commit page, "Phase 2").
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "pa_decode.h"
+
+namespace pa {
+
+constexpr int kPageSize = 16;
+constexpr int kMaxGroup = 16;
+constexpr int kMaxWavesPerGroup = 4;
+constexpr int kMergeThreads = 256;
+
+// Bytes per element of a PA_DTYPE_* code (0 when unknown).
+int dtype_bytes(int dtype);
+
+// Pages of K (and of V) one wave holds in flight per step: 8 KiB of K and
+// 8 KiB of V per wave, i.e. 512 bytes of one token row times 16 rows.
+int pages_per_block(int head_dim, int dtype);
+
+// The instantiated group size that serves an actual GQA group size G
+// (the smallest built one >= G); 0 when G is not supported.
+int template_group(int G);
+
+// Checks the static description; returns a PA_DECODE_* status.
+int check_desc(const pa_decode_desc& d);
+
+// Fills `plan` for the given call sizes; returns a PA_DECODE_* status.
+int make_plan(const pa_decode_desc& d, int num_cus, int batch, int max_context_len,
+              int sliding_window, int partition_size, pa_decode_plan* plan);
+
+// Dynamic LDS bytes of the partial kernel for a plan.
+size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan);
+
+// Workspace layout of a split plan: partition outputs o[B][Hq][P][D] (f32),
+// then maxima m[B][Hq][P] and denominators l[B][Hq][P] (f32), each region
+// 256-byte aligned.
+struct WorkspaceLayout {
+    size_t o_off, m_off, l_off, total;
+};
+WorkspaceLayout workspace_layout(const pa_decode_desc& d, int batch, int num_partitions);
+
+}  // namespace pa

@@ -1,0 +1,144 @@
+"""Host-side checks of libpa_decode.so (CPU only, no kernel launch).
+
+* the library loads and exports every function include/pa_decode.h declares;
+* the status strings;
+* pa_decode_create rejects invalid descriptions before touching HIP;
+* the planner (pa_decode_plan_query, pure host) covers every context with its
+  partitions, keeps the partition size a multiple of the page size, picks the
+  unsplit path exactly when one partition covers every context, keeps the
+  grid and LDS within limits, and honours a forced partition size (the
+  5-th workload's 512-token partitions give 196 of them at 100,000 tokens).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from paged_kv_decode_amd import binding as B
+from paged_kv_decode_amd import workloads as W
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "pa_decode.h")
+
+
+def lib():
+    return B.load_library()
+
+
+def test_library_exports_every_declared_symbol():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:int|const char\*)\s+(pa_decode_\w+)\s*\(", text, re.M))
+    assert declared == set(B.EXPORTED), declared ^ set(B.EXPORTED)
+    L = lib()
+    for name in declared:
+        assert hasattr(L, name) and getattr(L, name) is not None
+
+
+def test_status_strings():
+    assert B.pa_decode_status_string(0) == "ok"
+    assert B.pa_decode_status_string(-3) == "workspace too small"
+    assert B.pa_decode_status_string(123) == "unknown status"
+
+
+@pytest.mark.parametrize("fields,status", [
+    (dict(num_q_heads=0), B.PA_DECODE_INVALID_ARG),
+    (dict(num_q_heads=6, num_kv_heads=4), B.PA_DECODE_INVALID_ARG),
+    (dict(head_dim=96), B.PA_DECODE_UNSUPPORTED),
+    (dict(page_size=32), B.PA_DECODE_UNSUPPORTED),
+    (dict(dtype=7), B.PA_DECODE_UNSUPPORTED),
+    (dict(dtype=B.PA_DTYPE_F32, head_dim=128), B.PA_DECODE_UNSUPPORTED),
+    (dict(num_q_heads=32, num_kv_heads=1), B.PA_DECODE_UNSUPPORTED),
+    (dict(max_batch=-1), B.PA_DECODE_INVALID_ARG),
+])
+def test_create_rejects_invalid_descriptions(fields, status):
+    base = dict(num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=16,
+                dtype=B.PA_DTYPE_F16, max_batch=4, max_context_len=4096, device=0)
+    base.update(fields)
+    d = B.PaDecodeDesc(**base)
+    h = ctypes.c_void_p()
+    assert lib().pa_decode_create(ctypes.byref(d), ctypes.byref(h)) == status
+    assert not h.value
+
+
+def test_null_arguments_are_rejected():
+    assert lib().pa_decode_create(None, None) == B.PA_DECODE_INVALID_ARG
+    assert lib().pa_decode_run(None, None, None) == B.PA_DECODE_INVALID_ARG
+    assert lib().pa_decode_last_plan(None, None) == B.PA_DECODE_INVALID_ARG
+    assert lib().pa_decode_destroy(None) == B.PA_DECODE_OK
+
+
+def plan(w: W.Workload, num_cus=256, batch=None, max_ctx=None, S=None, window=None):
+    d = B.make_desc(w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype, max_batch=4096,
+                    max_context_len=1 << 20)
+    lens = w.context_lens or [4096]
+    return B.pa_decode_plan_query(d, num_cus, batch or w.batch, max_ctx or max(lens),
+                                  w.window if window is None else window,
+                                  w.partition_size if S is None else S)
+
+
+def covered(p, n, window):
+    """Partitions [lo/S + i for i < P] cover [lo, n) with the plan's S."""
+    lo = n - window if (window > 0 and n > window) else 0
+    if n == lo:
+        return True
+    S = p.partition_size
+    first = lo // S
+    last = (n + S - 1) // S - 1
+    return last - first + 1 <= p.num_partitions
+
+
+@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+def test_plan_covers_every_context(name):
+    w = W.CONFIGS[name]
+    for max_ctx in (1, 15, 16, 17, 300, 3060, 4096, 8192, 100000):
+        for S in (0, 16, 48, 512):
+            p = plan(w, max_ctx=max_ctx, S=S)
+            assert p.partition_size % 16 == 0 and p.partition_size > 0
+            if S:
+                assert p.partition_size == S
+            for n in {0, 1, max_ctx // 2, max_ctx - 1, max_ctx}:
+                if 0 <= n <= max_ctx:
+                    assert covered(p, n, w.window), (name, max_ctx, S, n)
+            assert p.split == (1 if p.num_partitions > 1 else 0)
+            assert p.grid_partial[0] == p.num_partitions
+            assert p.grid_partial[1] == w.num_kv_heads
+            assert 64 <= p.block_partial <= 256 and p.block_partial % 64 == 0
+            if p.split:
+                assert p.grid_merge[:2] == [w.num_q_heads, w.batch]
+                rows = w.batch * w.num_q_heads * p.num_partitions
+                assert p.workspace_bytes >= rows * (w.head_dim + 2) * 4
+            else:
+                assert p.workspace_bytes == 0
+
+
+def test_forced_512_partitions_at_100k_give_196():
+    p = plan(W.CONFIGS["ctx100k_gqa6_f16"])
+    assert p.partition_size == 512 and p.num_partitions == 196 and p.split == 1
+
+
+def test_unsplit_when_one_partition_covers_the_context():
+    w = W.custom(batch=512, num_q_heads=32, num_kv_heads=8, head_dim=128, context_lens=[200] * 512)
+    p = plan(w)
+    assert p.split == 0 and p.num_partitions == 1 and p.partition_size >= 200
+    # long context, small batch: split
+    p = plan(W.CONFIGS["llama1b_ctx3060_f16"])
+    assert p.split == 1 and p.num_partitions > 1
+
+
+def test_plan_fills_the_device():
+    # at least about one wave per compute unit when the work allows it
+    for name in ("llama1b_ctx3060_f16", "llama8b_b16_ragged_f16", "d256_window4096_bf16"):
+        w = W.CONFIGS[name]
+        p = plan(w)
+        waves = p.grid_partial[0] * p.grid_partial[1] * p.grid_partial[2] * p.block_partial // 64
+        assert waves >= 256, (name, p.as_dict())
+
+
+def test_plan_rejects_bad_partition_sizes():
+    w = W.CONFIGS["llama1b_ctx3060_f16"]
+    with pytest.raises(B.PaDecodeError):
+        plan(w, S=24)
+    with pytest.raises(B.PaDecodeError):
+        plan(w, num_cus=0)

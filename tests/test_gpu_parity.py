@@ -1,0 +1,163 @@
+"""GPU parity: the HIP path against the float64 oracle (needs an MI355X).
+
+Every case draws seeded inputs, runs pa_decode_run through the C ABI and
+compares out (relative L2 against the oracle rounded to the output dtype) and
+lse (absolute error) with the tolerances in helpers.py.  Covered:
+  * the five workloads at full size (tiny GQA-4 fp32; Llama-3.2-1B-shaped
+    batch-1 at 3060 tokens; Llama-3.1-8B-shaped batch 16 with ragged lengths
+    including 1, 17 and 4096; head_dim 256 bf16 with a 4096-token sliding
+    window; 100,000 tokens GQA-6 cut into 196 partitions of 512) in the
+    launch configuration the benchmark times;
+  * nine context lengths from 1 to 3060 with a shuffled page table, for
+    head_dim 64 / 128 / 256 (TVM PR #20426, section "Correctness", checks
+    nine lengths in that range with a shuffled table);
+  * forced partition sizes (16 ... 1024 tokens) and the unsplit path;
+  * every built group size G in 1..16;
+  * NaN in every slot the method must not read (tail slots, keys before the
+    window, unused pages, page-table padding);
+  * an empty context in a batch (out = 0, lse = -inf) and batch 0;
+  * a token-major cache layout [num_pages, page_size, Hkv, D];
+  * bitwise invariants: physical page shuffling, run-to-run repeatability,
+    n = 1 giving exactly v0.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_decode_amd import binding as B
+from paged_kv_decode_amd import workloads as W
+
+from helpers import compare, engine, run_gpu, run_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(p, S=None, what=""):
+    ref_out, ref_lse = run_oracle(p)
+    out, lse, plan = run_gpu(p, partition_size=S)
+    rel, lerr = compare(out, lse, ref_out, ref_lse, p.workload.dtype,
+                        what="%s S=%s plan=%s" % (what, S, plan))
+    print("%s S=%s plan(S=%d,P=%d,nw=%d,split=%d) rel_l2=%.3g lse_err=%.3g" %
+          (what, S, plan["partition_size"], plan["num_partitions"], plan["waves_per_group"],
+           plan["split"], rel, lerr), flush=True)
+    return out, lse
+
+
+@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+def test_workload_full_size(name):
+    p = W.generate(W.CONFIGS[name])
+    _check(p, what=name)
+
+
+@pytest.mark.parametrize("D,dtype", [(64, torch.float16), (128, torch.float16),
+                                     (256, torch.bfloat16), (64, torch.float32)])
+def test_nine_context_lengths_shuffled_pages(D, dtype):
+    lens = [1, 2, 15, 16, 17, 255, 257, 1000, 3060]
+    G = 4
+    w = W.custom(batch=len(lens), num_q_heads=8, num_kv_heads=8 // G, head_dim=D, dtype=dtype,
+                 context_lens=lens, seed=100 + D, num_pages=600)
+    _check(W.generate(w), what="nine-lengths D=%d %s" % (D, dtype))
+
+
+@pytest.mark.parametrize("S", [16, 32, 48, 64, 128, 512, 1024, 4096])
+def test_forced_partition_sizes(S):
+    w = W.custom(batch=3, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype=torch.float16,
+                 context_lens=[1, 3060, 777], seed=200)
+    _check(W.generate(w), S=S, what="forced")
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16])
+def test_every_group_size(G):
+    Hkv = 2
+    for D, dtype in ((64, torch.float16), (256, torch.bfloat16)):
+        w = W.custom(batch=2, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D, dtype=dtype,
+                     context_lens=[333, 1200], seed=300 + G)
+        _check(W.generate(w), what="G=%d D=%d" % (G, D))
+
+
+@pytest.mark.parametrize("name", W.CONFIG_ORDER[:4])
+def test_poisoned_unread_slots(name):
+    w = W.CONFIGS[name]
+    if name == "d256_window4096_bf16":
+        w = dataclasses.replace(w, context_lens=[8192, 5000, 4097, 333], window=4096,
+                                num_pages=2048)
+    p = W.generate(w, poison=True, extra_pages=3)
+    for S in (0, 16, 64):
+        _check(p, S=S, what="poison " + name)
+
+
+def test_window_edges():
+    for Wn in (1, 15, 16, 17, 100, 4095):
+        w = W.custom(batch=3, num_q_heads=8, num_kv_heads=4, head_dim=256, dtype=torch.bfloat16,
+                     context_lens=[5000, Wn, Wn + 1], seed=400, window=Wn)
+        p = W.generate(w, poison=True)
+        for S in (0, 32, 512):
+            _check(p, S=S, what="window %d" % Wn)
+
+
+def test_empty_context_and_empty_batch():
+    w = W.custom(batch=4, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype=torch.float16,
+                 context_lens=[0, 5, 0, 2000], seed=500)
+    p = W.generate(w)
+    for S in (0, 16, 4096):
+        out, lse = _check(p, S=S, what="empty")
+        assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    # batch 0: nothing to do, but still a valid call
+    eng = engine(p)
+    d = to_device(p)
+    out = torch.empty((0, 8, 128), dtype=torch.float16, device="cuda")
+    args = eng.make_args(d.q[:0], d.k_cache, d.v_cache, d.page_table[:0], d.context_lens[:0],
+                         p.scale, out, None, max_context_len=0)
+    eng.run_args(args)
+    torch.cuda.synchronize()
+
+
+def test_token_major_cache_layout():
+    w = W.custom(batch=2, num_q_heads=16, num_kv_heads=4, head_dim=128, dtype=torch.float16,
+                 context_lens=[999, 1500], seed=600)
+    p = W.generate(w)
+    # [num_pages, ps, Hkv, D] storage viewed as [num_pages, Hkv, ps, D]
+    k = p.k_cache.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    v = p.v_cache.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    assert k.stride(2) == 4 * 128
+    p2 = dataclasses.replace(p, k_cache=k, v_cache=v)
+    ref = run_oracle(p)
+    for S in (0, 64):
+        out, lse, _ = run_gpu(p2, partition_size=S)
+        compare(out, lse, ref[0], ref[1], torch.float16, "token-major")
+
+
+def test_bitwise_page_shuffle_and_repeatability():
+    p = W.generate(W.CONFIGS["llama1b_ctx3060_f16"])
+    a = run_gpu(p)
+    b = run_gpu(p)
+    c = run_gpu(W.permute_pages(p, seed=77))
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
+
+
+def test_single_key_is_exactly_v0():
+    w = W.custom(batch=3, num_q_heads=24, num_kv_heads=4, head_dim=256, dtype=torch.float16,
+                 context_lens=[1, 1, 1], seed=700)
+    p = W.generate(w, keep_logical=True)
+    for S in (0, 16):
+        out, lse, _ = run_gpu(p, partition_size=S)
+        for h in range(24):
+            assert torch.equal(out[:, h], p.logical_v[:, 0, h // 6])
+        ref = run_oracle(p)
+        assert np.abs(lse.double().numpy() - ref[1]).max() <= 1e-5
+
+
+def test_workspace_too_small_is_reported():
+    p = W.generate(W.CONFIGS["llama1b_ctx3060_f16"])
+    d = to_device(p)
+    eng = engine(p)
+    out = torch.empty_like(d.q)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    args = eng.make_args(d.q, d.k_cache, d.v_cache, d.page_table, d.context_lens, p.scale, out,
+                         None, max_context_len=3060, partition_size=16, workspace=small)
+    with pytest.raises(B.PaDecodeError) as e:
+        eng.run_args(args)
+    assert e.value.status == B.PA_DECODE_WORKSPACE_TOO_SMALL
