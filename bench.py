@@ -1,0 +1,338 @@
+"""Benchmark of paged-KV GQA decode attention on one MI355X.
+
+A step is one pa_decode_run (partial kernel + merge kernel) over one batch of
+synthetic decode inputs.  Default workload: Llama-3.2-1B-shaped decode,
+batch 1, Hq 32 / Hkv 8, head_dim 64, fp16, 3060 tokens of context in a
+shuffled 4096-page pool.
+
+Timed region: W eager warm-up steps, then exactly K steps replayed from one
+HIP graph, bracketed by synchronisations, timed with events on the launch
+stream.  The K steps cycle over R replicas of the workload whose page pools
+are independent random permutations of the same pages (every replica computes
+the same result); R is large enough that the KV the rotation touches exceeds
+the GPU's last-level caches, so each step reads its KV from HBM rather than
+from cache.  Inputs are resident in HBM before the timed region starts.
+
+value = algorithmic KV bytes per step / seconds per step (GB/s), where the
+algorithmic bytes are the K and V bytes of the visible keys only.
+
+roofline: the dominant kernel is the partial kernel; its average duration
+comes from start/stop HIP events the library records around each of its
+launches (pa_decode_profile_begin/end) in a second pass of K steps run
+eagerly on the same stream.  achieved = algorithmic KV bytes per launch /
+average partial-kernel duration; peak = 8 TB/s HBM.  traffic (HBM bytes per
+launch measured with rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by the same
+counters on a plain copy) is read from profiles/traffic.json and reported
+only while the kernel sources hash to the value recorded there.
+
+cpu_baseline: the float64 CPU oracle timed on this host on the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from paged_kv_decode_amd import binding  # noqa: E402
+from paged_kv_decode_amd import workloads as W  # noqa: E402
+
+METRIC = "decode-attention µs/step + achieved KV HBM GB/s (% of peak) at ctx 3k / 100k"
+PEAK_GBPS = 8000.0
+CACHE_BYTES = 288 << 20          # 256 MiB MALL + 8 x 4 MiB L2
+KERNEL_SOURCES = ["paged_kv_decode_amd/csrc/pa_decode_kernels.hip",
+                  "paged_kv_decode_amd/csrc/planner.cpp"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+class Replicas:
+    """R page-permuted copies of one problem, resident on the GPU."""
+
+    def __init__(self, p: W.Problem, R: int, eng: binding.PagedDecode, partition_size: int):
+        self.p = p
+        dev = torch.device("cuda", 0)
+        k0 = p.k_cache.to(dev)
+        v0 = p.v_cache.to(dev)
+        pt0 = p.page_table.to(dev)
+        self.q = p.q.to(dev)
+        self.lens = p.context_lens.to(dev)
+        B, Hq, D = p.q.shape
+        self.out = torch.empty((B, Hq, D), dtype=p.q.dtype, device=dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        ws_bytes = eng.workspace_size(B, p.max_context_len, p.window, partition_size)
+        self.ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.caches = []
+        self.args = []
+        gen = torch.Generator(device="cpu")
+        gen.manual_seed(1234)
+        num_pages = k0.shape[0]
+        for r in range(R):
+            if r == 0:
+                k, v, pt = k0, v0, pt0
+            else:
+                perm = torch.randperm(num_pages, generator=gen).to(dev)
+                k = torch.empty_like(k0)
+                v = torch.empty_like(v0)
+                k[perm] = k0
+                v[perm] = v0
+                pt = perm.to(torch.int32)[pt0.long()]
+            self.caches.append((k, v, pt))
+            self.args.append(eng.make_args(self.q, k, v, pt, self.lens, p.scale, self.out,
+                                           self.lse, max_context_len=p.max_context_len,
+                                           sliding_window=p.window,
+                                           partition_size=partition_size, workspace=self.ws))
+
+
+def run_oracle_baseline(p: W.Problem, budget_s: float):
+    import oracle
+    threads = oracle.max_threads()
+    reps = 0
+    t0 = time.perf_counter()
+    out = lse = None
+    while True:
+        out, lse = oracle.decode(p.q, p.k_cache, p.v_cache, p.page_table, p.context_lens,
+                                 p.scale, window=p.window)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return out, lse, reps, el, threads
+
+
+def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cache):
+    w = W.CONFIGS[name]
+    S = w.partition_size if partition_size is None else partition_size
+    t0 = time.perf_counter()
+    p = W.generate(w)
+    log("%s: generated in %.1fs" % (name, time.perf_counter() - t0))
+    key = (w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype)
+    eng = eng_cache.get(key)
+    if eng is None:
+        eng = binding.PagedDecode(w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype,
+                                  max_batch=max(w.batch, 64), max_context_len=1 << 20)
+        eng_cache[key] = eng
+    kv_bytes = p.kv_bytes()
+    if replicas is None:
+        pool_bytes = 2 * p.k_cache.numel() * p.k_cache.element_size()
+        R = max(2, math.ceil(4 * CACHE_BYTES / kv_bytes))
+        R = min(R, max(2, int((64 << 30) // pool_bytes)))
+    else:
+        R = replicas
+    reps = Replicas(p, R, eng, S)
+    log("%s: %d replicas, %.1f MB KV per step" % (name, R, kv_bytes / 1e6))
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    # Every replica must produce the same bits (page-shuffle invariance).
+    outs = []
+    for r in (0, R - 1):
+        eng.run_args(reps.args[r], sp)
+        torch.cuda.synchronize()
+        outs.append((reps.out.clone(), reps.lse.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1]), \
+        "replicas disagree"
+    plan = eng.last_plan().as_dict()
+
+    for i in range(warmup):
+        eng.run_args(reps.args[i % R], sp)
+    torch.cuda.synchronize()
+
+    if mode == "graph":
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                cs = torch.cuda.current_stream().cuda_stream
+                for i in range(steps):
+                    eng.run_args(reps.args[i % R], cs)
+        stream.wait_stream(cap)
+        g.replay()  # upload / first replay, untimed
+        torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    if mode == "graph":
+        g.replay()
+    else:
+        for i in range(steps):
+            eng.run_args(reps.args[i % R], sp)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_per_step = ms_total / steps
+
+    # Kernel durations: start/stop events recorded around each launch.
+    nprof = min(steps, 2000)
+    binding.pa_decode_profile_begin(eng.handle, nprof)
+    for i in range(nprof):
+        eng.run_args(reps.args[i % R], sp)
+    pm, pn, mm, mn = binding.pa_decode_profile_end(eng.handle)
+    partial_us = 1e3 * pm / max(pn, 1)
+    merge_us = 1e3 * mm / max(mn, 1) if mn else 0.0
+
+    res = {
+        "workload": name, "p": p, "plan": plan, "kv_bytes": kv_bytes, "replicas": R,
+        "ms_per_step": ms_per_step, "us_per_step": 1e3 * ms_per_step,
+        "gbps": kv_bytes / (ms_per_step * 1e-3) / 1e9,
+        "partial_us": partial_us, "merge_us": merge_us,
+        "partial_gbps": kv_bytes / (partial_us * 1e-6) / 1e9,
+        "gpu_out": outs[0][0].cpu(), "gpu_lse": outs[0][1].cpu(),
+    }
+    del reps
+    torch.cuda.empty_cache()
+    return res
+
+
+def parity(res):
+    import oracle
+    p = res["p"]
+    ref_out, ref_lse = oracle.decode(p.q, p.k_cache, p.v_cache, p.page_table, p.context_lens,
+                                     p.scale, window=p.window)
+    ref = torch.from_numpy(ref_out).to(p.q.dtype).double()
+    rel = ((res["gpu_out"].double() - ref).norm() / ref.norm()).item()
+    fin = np.isfinite(ref_lse)
+    lerr = float(np.abs(res["gpu_lse"].double().numpy()[fin] - ref_lse[fin]).max())
+    return rel, lerr
+
+
+def traffic_for(name, plan):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    e = t.get("workloads", {}).get(name)
+    if not e:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="llama1b_ctx3060_f16", choices=W.CONFIG_ORDER)
+    ap.add_argument("--also", default="ctx100k_gqa6_f16,llama8b_b16_ragged_f16,d256_window4096_bf16",
+                    help="comma-separated extra workloads reported under 'also' ('' for none)")
+    ap.add_argument("--also-steps", type=int, default=300)
+    ap.add_argument("--replicas", type=int, default=None)
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work for the CPU baseline (0: skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this decode-attention path runs on a single "
+              "MI355X and has no multi-GPU mode (requested --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    binding.load_library()
+
+    engines = {}
+    main_res = bench_workload(args.workload, args.steps, args.warmup, args.replicas,
+                              args.partition_size, args.mode, engines)
+    log("%s: %.2f us/step, %.0f GB/s; partial %.2f us (%.0f GB/s), merge %.2f us" % (
+        args.workload, main_res["us_per_step"], main_res["gbps"], main_res["partial_us"],
+        main_res["partial_gbps"], main_res["merge_us"]))
+    also = {}
+    for name in [s for s in args.also.split(",") if s and s != args.workload]:
+        r = bench_workload(name, args.also_steps, 20, None, None, args.mode, engines)
+        rel, lerr = parity(r)
+        also[name] = {
+            "us_per_step": round(r["us_per_step"], 3), "GBps": round(r["gbps"], 1),
+            "frac_of_peak": round(r["gbps"] / PEAK_GBPS, 4),
+            "partial_us": round(r["partial_us"], 3), "merge_us": round(r["merge_us"], 3),
+            "partial_GBps": round(r["partial_gbps"], 1),
+            "partial_frac": round(r["partial_gbps"] / PEAK_GBPS, 4),
+            "kv_bytes": r["kv_bytes"], "replicas": r["replicas"],
+            "plan": {k: r["plan"][k] for k in ("partition_size", "num_partitions",
+                                               "waves_per_group", "split")},
+            "parity": {"out_rel_l2": rel, "lse_max_abs_err": lerr},
+        }
+        log("%s: %.2f us/step, %.0f GB/s; partial %.2f us (%.0f GB/s), merge %.2f us; "
+            "rel_l2 %.2g" % (name, r["us_per_step"], r["gbps"], r["partial_us"],
+                             r["partial_gbps"], r["merge_us"], rel))
+
+    rel, lerr = parity(main_res)
+    cpu = None
+    if args.cpu_budget > 0:
+        p = main_res["p"]
+        _, _, reps, el, threads = run_oracle_baseline(p, args.cpu_budget)
+        cpu = {"value": round(main_res["kv_bytes"] * reps / el / 1e9, 4), "unit": "GB/s",
+               "cores": threads, "kind": "oracle",
+               "sample": "%d full steps of the %s workload (float64 C oracle, OpenMP), %.1f s"
+                         % (reps, args.workload, el),
+               "us_per_step": round(1e6 * el / reps, 1)}
+    dtype_name = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}
+    w = W.CONFIGS[args.workload]
+    traffic = traffic_for(args.workload, main_res["plan"])
+    achieved = main_res["partial_gbps"]
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["gbps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 6),
+        "us_per_step": round(main_res["us_per_step"], 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype_name[w.dtype] + " in, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": w.batch, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "context_lens": p_lens(main_res["p"]), "page_size": w.page_size,
+                   "sliding_window": w.window, "kv_bytes_per_step": main_res["kv_bytes"],
+                   "replicas": main_res["replicas"], "mode": args.mode,
+                   "plan": main_res["plan"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "partial_kernel", "kernel_us": round(main_res["partial_us"], 3),
+                     "merge_us": round(main_res["merge_us"], 3)},
+        "cpu_baseline": cpu,
+        "parity": {"out_rel_l2": rel, "lse_max_abs_err": lerr},
+        "also": also,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def p_lens(p):
+    lens = p.context_lens.tolist()
+    return lens if len(lens) <= 4 else {"n": len(lens), "sum": sum(lens), "max": max(lens)}
+
+
+if __name__ == "__main__":
+    main()

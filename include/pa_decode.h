@@ -106,7 +106,8 @@ typedef struct pa_decode_args {
     float* lse;                 /* device, float32 [batch, Hq], may be NULL */
     void* workspace;            /* device scratch of >= workspace_bytes needed by the */
     size_t workspace_bytes;     /*   plan (pa_decode_workspace_size); may be NULL/0   */
-                                /*   when that size is 0                              */
+                                /*   when that size is 0.  Calls that share a         */
+                                /*   workspace must not run concurrently.             */
 } pa_decode_args;
 
 /* The plan pa_decode_run derives from (batch, max_context_len, window,
@@ -119,7 +120,8 @@ typedef struct pa_decode_plan {
     int32_t pages_per_block;    /* pages each wave holds in flight per step */
     int32_t grid_partial[3];    /* partial kernel grid (x = partition, y = KV head, z = b) */
     int32_t block_partial;      /* threads per workgroup of the partial kernel */
-    int32_t grid_merge[3];      /* merge kernel grid (0s when split == 0) */
+    int32_t grid_merge[3];      /* merge kernel grid (x = query head, y = b, z = 64-dim */
+                                /*   slice of head_dim; 0s when split == 0)           */
     int32_t block_merge;
     int32_t num_cus;            /* compute units the plan was made for */
     int64_t workspace_bytes;    /* bytes of workspace the plan needs */
@@ -145,8 +147,10 @@ int pa_decode_workspace_size(pa_decode_handle handle, int32_t batch, int32_t max
  * HIP_ERROR when a launch fails.  Page ids, context lengths and page-table
  * rows live in device memory and are the caller's contract: every page id
  * read (rows b, entries [lo_b/ps, ceil(n_b/ps))) must be < num_pages and
- * n_b <= max_context_len.  Entries past ceil(n_b/ps), keys before lo_b and
- * slots past n_b are never read, so they may hold anything. */
+ * n_b <= max_context_len.  Keys before lo_b and slots past n_b never reach
+ * the result, so they may hold anything (NaN included); page-table entries
+ * past ceil(n_b/ps) (within the row's pt_stride entries) may be read but are
+ * never used to address K/V. */
 int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* stream);
 
 /* The plan of the last successful pa_decode_run on this handle. */
@@ -157,6 +161,19 @@ int pa_decode_last_plan(pa_decode_handle handle, pa_decode_plan* plan);
 int pa_decode_plan_query(const pa_decode_desc* desc, int32_t num_cus, int32_t batch,
                          int32_t max_context_len, int32_t sliding_window,
                          int32_t partition_size, pa_decode_plan* plan);
+
+/* Kernel timing for measurement tools.  After pa_decode_profile_begin, the
+ * next `max_launches` launches of each kernel (partial, merge) made by
+ * pa_decode_run on this handle carry start/stop HIP events recorded on the
+ * launch stream around the kernel itself.  pa_decode_profile_end waits for
+ * those events, returns the summed kernel durations in milliseconds and the
+ * launch counts (either output pointer may be NULL), and stops timing.
+ * The events are created in pa_decode_profile_begin (host set-up, not in the
+ * decode step).  Errors: INVALID_ARG (null handle, max_launches < 1),
+ * HIP_ERROR (event creation or query failed). */
+int pa_decode_profile_begin(pa_decode_handle handle, int32_t max_launches);
+int pa_decode_profile_end(pa_decode_handle handle, double* partial_ms, int32_t* partial_launches,
+                          double* merge_ms, int32_t* merge_launches);
 
 /* Last hipError_t recorded on the handle (0 when none). */
 int pa_decode_last_hip_error(pa_decode_handle handle);

@@ -34,6 +34,7 @@ DTYPE_CODE = {torch.float32: PA_DTYPE_F32, torch.float16: PA_DTYPE_F16,
 # Symbols include/pa_decode.h declares.
 EXPORTED = ["pa_decode_create", "pa_decode_destroy", "pa_decode_workspace_size",
             "pa_decode_run", "pa_decode_last_plan", "pa_decode_plan_query",
+            "pa_decode_profile_begin", "pa_decode_profile_end",
             "pa_decode_last_hip_error", "pa_decode_status_string"]
 
 
@@ -104,6 +105,10 @@ def load_library(path: Optional[str] = None):
         lib.pa_decode_last_plan.argtypes = [vp, ctypes.POINTER(PaDecodePlan)]
         lib.pa_decode_plan_query.argtypes = [ctypes.POINTER(PaDecodeDesc), i32, i32, i32, i32,
                                              i32, ctypes.POINTER(PaDecodePlan)]
+        lib.pa_decode_profile_begin.argtypes = [vp, i32]
+        lib.pa_decode_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
+                                              ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double),
+                                              ctypes.POINTER(i32)]
         lib.pa_decode_last_hip_error.argtypes = [vp]
         lib.pa_decode_status_string.argtypes = [ctypes.c_int]
         lib.pa_decode_status_string.restype = ctypes.c_char_p
@@ -166,6 +171,20 @@ def pa_decode_plan_query(desc: PaDecodeDesc, num_cus: int, batch: int, max_conte
     return plan
 
 
+def pa_decode_profile_begin(handle, max_launches: int) -> None:
+    _check(load_library().pa_decode_profile_begin(handle, max_launches), "pa_decode_profile_begin")
+
+
+def pa_decode_profile_end(handle):
+    """Returns (partial_ms_total, partial_launches, merge_ms_total, merge_launches)."""
+    pm, mm = ctypes.c_double(), ctypes.c_double()
+    pn, mn = ctypes.c_int32(), ctypes.c_int32()
+    _check(load_library().pa_decode_profile_end(handle, ctypes.byref(pm), ctypes.byref(pn),
+                                                ctypes.byref(mm), ctypes.byref(mn)),
+           "pa_decode_profile_end")
+    return pm.value, pn.value, mm.value, mn.value
+
+
 def pa_decode_last_hip_error(handle) -> int:
     return int(load_library().pa_decode_last_hip_error(handle))
 
@@ -211,7 +230,7 @@ class PagedDecode:
     def workspace(self, nbytes: int) -> torch.Tensor:
         """A cached uint8 device buffer of at least nbytes (never shrinks)."""
         if self._workspace is None or self._workspace.numel() < nbytes:
-            self._workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8,
+            self._workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8,
                                           device=self.device)
         return self._workspace
 

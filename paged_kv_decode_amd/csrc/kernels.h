@@ -44,10 +44,17 @@ struct MergeParams {
     float* lse;
 };
 
+// Optional start/stop events recorded around one launch (both null: none).
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
 // dtype: PA_DTYPE_*; group_t: an instantiated group size (template_group).
 hipError_t launch_partial(int dtype, int head_dim, int group_t, const PartialParams& p,
-                          dim3 grid, dim3 block, size_t lds_bytes, hipStream_t stream);
+                          dim3 grid, dim3 block, size_t lds_bytes, hipStream_t stream,
+                          LaunchEvents ev);
 hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, dim3 grid, dim3 block,
-                        hipStream_t stream);
+                        hipStream_t stream, LaunchEvents ev);
 
 }  // namespace pa

@@ -10,10 +10,35 @@
 #include <cstdint>
 #include <cstring>
 #include <new>
+#include <vector>
 
 #include "kernels.h"
 #include "pa_decode.h"
 #include "planner.h"
+
+// Start/stop event pairs for kernel timing (see pa_decode_profile_begin).
+struct EventRing {
+    std::vector<hipEvent_t> start, stop;
+    int used = 0;
+    pa::LaunchEvents next()
+    {
+        pa::LaunchEvents ev;
+        if (used < int(start.size())) {
+            ev.start = start[used];
+            ev.stop = stop[used];
+            ++used;
+        }
+        return ev;
+    }
+    void release()
+    {
+        for (hipEvent_t e : start) hipEventDestroy(e);
+        for (hipEvent_t e : stop) hipEventDestroy(e);
+        start.clear();
+        stop.clear();
+        used = 0;
+    }
+};
 
 struct pa_decode_handle_s {
     pa_decode_desc desc;
@@ -21,6 +46,8 @@ struct pa_decode_handle_s {
     pa_decode_plan last_plan;
     bool has_plan;
     int last_hip_error;
+    bool profiling;
+    EventRing prof_partial, prof_merge;
 };
 
 namespace {
@@ -84,13 +111,75 @@ int pa_decode_create(const pa_decode_desc* desc, pa_decode_handle* handle)
     h->num_cus = cus;
     h->has_plan = false;
     h->last_hip_error = 0;
+    h->profiling = false;
     *handle = h;
     return PA_DECODE_OK;
 }
 
 int pa_decode_destroy(pa_decode_handle handle)
 {
+    if (handle) {
+        handle->prof_partial.release();
+        handle->prof_merge.release();
+    }
     delete handle;
+    return PA_DECODE_OK;
+}
+
+int pa_decode_profile_begin(pa_decode_handle handle, int32_t max_launches)
+{
+    if (!handle || max_launches < 1)
+        return PA_DECODE_INVALID_ARG;
+    handle->prof_partial.release();
+    handle->prof_merge.release();
+    for (EventRing* r : {&handle->prof_partial, &handle->prof_merge}) {
+        for (int i = 0; i < max_launches; ++i) {
+            hipEvent_t a = nullptr, b = nullptr;
+            hipError_t e = hipEventCreate(&a);
+            if (e == hipSuccess) e = hipEventCreate(&b);
+            if (e != hipSuccess) {
+                if (a) hipEventDestroy(a);
+                r->release();
+                handle->last_hip_error = int(e);
+                return PA_DECODE_HIP_ERROR;
+            }
+            r->start.push_back(a);
+            r->stop.push_back(b);
+        }
+    }
+    handle->profiling = true;
+    return PA_DECODE_OK;
+}
+
+int pa_decode_profile_end(pa_decode_handle handle, double* partial_ms, int32_t* partial_launches,
+                          double* merge_ms, int32_t* merge_launches)
+{
+    if (!handle)
+        return PA_DECODE_INVALID_ARG;
+    handle->profiling = false;
+    double sums[2] = {0.0, 0.0};
+    int counts[2] = {handle->prof_partial.used, handle->prof_merge.used};
+    EventRing* rings[2] = {&handle->prof_partial, &handle->prof_merge};
+    for (int k = 0; k < 2; ++k) {
+        for (int i = 0; i < counts[k]; ++i) {
+            hipError_t e = hipEventSynchronize(rings[k]->stop[i]);
+            float ms = 0.f;
+            if (e == hipSuccess) e = hipEventElapsedTime(&ms, rings[k]->start[i], rings[k]->stop[i]);
+            if (e != hipSuccess) {
+                handle->last_hip_error = int(e);
+                rings[0]->release();
+                rings[1]->release();
+                return PA_DECODE_HIP_ERROR;
+            }
+            sums[k] += ms;
+        }
+    }
+    rings[0]->release();
+    rings[1]->release();
+    if (partial_ms) *partial_ms = sums[0];
+    if (partial_launches) *partial_launches = counts[0];
+    if (merge_ms) *merge_ms = sums[1];
+    if (merge_launches) *merge_launches = counts[1];
     return PA_DECODE_OK;
 }
 
@@ -171,8 +260,10 @@ int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* str
 
     const dim3 grid(plan.grid_partial[0], plan.grid_partial[1], plan.grid_partial[2]);
     const dim3 block(plan.block_partial);
+    const pa::LaunchEvents ev_partial =
+        handle->profiling ? handle->prof_partial.next() : pa::LaunchEvents();
     hipError_t e = pa::launch_partial(d.dtype, d.head_dim, pa::template_group(G), pp, grid, block,
-                                      pa::partial_lds_bytes(d, plan), s);
+                                      pa::partial_lds_bytes(d, plan), s, ev_partial);
     if (e != hipSuccess) {
         handle->last_hip_error = int(e);
         return PA_DECODE_HIP_ERROR;
@@ -190,7 +281,9 @@ int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* str
         mp.out = a.out;
         mp.lse = a.lse;
         const dim3 mgrid(plan.grid_merge[0], plan.grid_merge[1], plan.grid_merge[2]);
-        e = pa::launch_merge(d.dtype, d.head_dim, mp, mgrid, dim3(plan.block_merge), s);
+        const pa::LaunchEvents ev_merge =
+            handle->profiling ? handle->prof_merge.next() : pa::LaunchEvents();
+        e = pa::launch_merge(d.dtype, d.head_dim, mp, mgrid, dim3(plan.block_merge), s, ev_merge);
         if (e != hipSuccess) {
             handle->last_hip_error = int(e);
             return PA_DECODE_HIP_ERROR;

@@ -32,6 +32,7 @@
 //
 // Exponentials are base 2 throughout (scores pre-multiplied by log2(e));
 // lse is converted back to the natural logarithm on output.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -80,6 +81,19 @@ __device__ __forceinline__ float row16_sum(float x)
     x += dpp<0x4E>(x);
     x += dpp<0x141>(x);
     x += dpp<0x140>(x);
+    return x;
+}
+
+// Sum of x over the lanes that share lane % CH (CH = 8, 16, 32 or 64):
+// xor 8 by a DPP rotate within 16-lane rows, xor 16 by ds_swizzle within
+// 32-lane halves, xor 32 by ds_bpermute.
+template <int CH>
+__device__ __forceinline__ float sum_rows(float x)
+{
+    if constexpr (CH <= 8) x += dpp<0x128>(x);
+    if constexpr (CH <= 16)
+        x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+    if constexpr (CH <= 32) x += __shfl_xor(x, 32);
     return x;
 }
 
@@ -160,6 +174,7 @@ template <> __device__ __forceinline__ void store_out<PA_DTYPE_BF16>(void* out, 
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *static_cast<const u32x4*>(p); }
 
+
 // ---------------------------------------------------------------------------
 // Partial kernel.
 //   DT: element type; D: head_dim; G: instantiated group size (>= actual);
@@ -181,36 +196,37 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     constexpr int R = kWave / CH;     // token rows of the P.V map
     constexpr int GP4 = (G + 3) / 4 * 4;
     constexpr int HG = (G + 3) / 4;   // 16-lane groups that carry real heads
+    constexpr int IPV = kWave / NB;   // loop iterations one page-id vector covers
     static_assert(KS * 4 == CH && R * CH == kWave && R * KS == kPage, "lane map");
 
     extern __shared__ float smem[];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    // Wave index and count are wave-uniform: keep them in scalar registers so
+    // that page ids and loop bounds are scalar too.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nw = blockDim.x / kWave;
     const int prel = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int Gact = prm.group;
-
-    const int n = prm.context_lens[b];
-    const int lo = (prm.window > 0 && n > prm.window) ? n - prm.window : 0;
     const int S = prm.partition_size;
-    const int pabs = lo / S + prel;
-    const int t0 = max(pabs * S, lo);
-    const int t1 = min(pabs * S + S, n);
-    if (t0 >= t1) {
-        if (!prm.split && prel == 0) {
-            // Empty context: out = 0, lse = -inf.
-            for (int idx = threadIdx.x; idx < Gact * D; idx += blockDim.x) {
-                const int h = kvh * Gact + idx / D;
-                store_out<DT>(prm.out, (size_t(b) * prm.num_q_heads + h) * D + idx % D, 0.f);
-            }
-            if (prm.lse && threadIdx.x < Gact)
-                prm.lse[size_t(b) * prm.num_q_heads + kvh * Gact + threadIdx.x] = -INFINITY;
-        }
-        return;
-    }
-
+    const int32_t* pt_row = prm.page_table + size_t(b) * prm.pt_stride;
     const int i16 = lane & 15, grp = lane >> 4;
     const int rho = lane / CH, c = lane % CH;
+
+    // Page ids of this wave's pages, one per lane: lane j holds the page of
+    // block (wave + nw * (it0 + j / NB)), page j % NB of the partition that
+    // starts at page pg_first; entries at or past pg_end are not read.
+    auto load_ids = [&](int pg_first, int pg_end, int it0) {
+        const int it = it0 + lane / NB;
+        const int pg = pg_first + (wave + nw * it) * NB + lane % NB;
+        return pg < pg_end ? pt_row[pg] : 0;
+    };
+    // Without a window the partition's first page does not depend on the
+    // context length: fetch the page ids together with the length and q.
+    int ids = 0;
+    if (prm.window <= 0) {
+        const int pgs = prel * (S / kPage);
+        ids = load_ids(pgs, min(pgs + S / kPage, prm.pt_stride), 0);
+    }
 
     // q as the MFMA A operand: row i16 = query head kvh*G + i16 (zero past G).
     u32x4 qa[KS];
@@ -225,10 +241,37 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         }
     }
 
+    const int n = prm.context_lens[b];
+    const int lo = (prm.window > 0 && n > prm.window) ? n - prm.window : 0;
+    const int pabs = lo / S + prel;
+    const int t0 = max(pabs * S, lo);
+    const int t1 = min(pabs * S + S, n);
+    if (t0 >= t1) {
+        if (prm.split) {
+            // Empty partition: a state the merge gives zero weight.
+            if (threadIdx.x < Gact) {
+                const size_t row = (size_t(b) * prm.num_q_heads + size_t(kvh) * Gact + threadIdx.x) *
+                                       prm.num_partitions + prel;
+                prm.ws_m[row] = -INFINITY;
+                prm.ws_l[row] = 0.f;
+            }
+        } else if (prel == 0) {
+            // Empty context: out = 0, lse = -inf.
+            for (int idx = threadIdx.x; idx < Gact * D; idx += blockDim.x) {
+                const int h = kvh * Gact + idx / D;
+                store_out<DT>(prm.out, (size_t(b) * prm.num_q_heads + h) * D + idx % D, 0.f);
+            }
+            if (prm.lse && threadIdx.x < Gact)
+                prm.lse[size_t(b) * prm.num_q_heads + kvh * Gact + threadIdx.x] = -INFINITY;
+        }
+    } else {
+    const int pg0 = t0 / kPage, pg1 = (t1 + kPage - 1) / kPage;
+    if (prm.window > 0)
+        ids = load_ids(pg0, pg1, 0);
+
     const int64_t ss = prm.stride_slot;
     const int64_t k_lane_off = int64_t(i16) * ss + int64_t(grp) * EPC;
     const int64_t v_lane_off = int64_t(rho) * ss + int64_t(c) * EPC;
-    const int32_t* pt_row = prm.page_table + size_t(b) * prm.pt_stride;
     const char* kbase = static_cast<const char*>(prm.k) + int64_t(kvh) * prm.stride_head * EB;
     const char* vbase = static_cast<const char*>(prm.v) + int64_t(kvh) * prm.stride_head * EB;
 
@@ -247,19 +290,24 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     float* pbuf = smem + wave * (NB * kPage * GP4 + GP4);
     float* abuf = pbuf + NB * kPage * GP4;
 
-    const int pg0 = t0 / kPage, pg1 = (t1 + kPage - 1) / kPage;
     const int nblk = (pg1 - pg0 + NB - 1) / NB;
+    const int nit = nblk > wave ? (nblk - wave + nw - 1) / nw : 0;
 
-    for (int blk = wave; blk < nblk; blk += nw) {
-        const int pgb = pg0 + blk * NB;
+    for (int it = 0; it < nit; ++it) {
+        if (it > 0 && it % IPV == 0)
+            ids = load_ids(pg0, pg1, it);
+        const int pgb = pg0 + (wave + nw * it) * NB;
         const int nbv = min(NB, pg1 - pgb);
+        // All page ids of the block into scalar registers before any load.
+        int64_t page[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) page[nb] = __builtin_amdgcn_readlane(ids, (it % IPV) * NB + nb);
         u32x4 kr[NB][KS], vr[NB][KS];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             if (nb < nbv) {
-                const int64_t page = pt_row[pgb + nb];
-                const char* kp = kbase + page * prm.stride_page * EB;
-                const char* vp = vbase + page * prm.stride_page * EB;
+                const char* kp = kbase + page[nb] * prm.stride_page * EB;
+                const char* vp = vbase + page[nb] * prm.stride_page * EB;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
                     kr[nb][ks] = load16(kp + (k_lane_off + int64_t(4 * ks) * EPC) * EB);
@@ -357,15 +405,13 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     }
 
     // Wave-level reductions: denominators over the 16 token lanes, outputs
-    // over the R token rows.
+    // over the R token rows (lanes c, c + CH, ...).
 #pragma unroll
     for (int r = 0; r < 4; ++r) l_run[r] = row16_sum(l_run[r]);
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e)
-#pragma unroll
-            for (int off = CH; off < kWave; off <<= 1) acc[g][e] += __shfl_xor(acc[g][e], off);
+        for (int e = 0; e < EPC; ++e) acc[g][e] = sum_rows<CH>(acc[g][e]);
 
     // Workgroup combine in LDS.
     __syncthreads();
@@ -411,6 +457,8 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
             if (dd == 0 && prm.lse) prm.lse[h] = (M + log2f(L)) * kLn2;
         }
     }
+    }  // non-empty partition
+
 }
 
 // ---------------------------------------------------------------------------
@@ -418,14 +466,13 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float block_reduce(float x, float* red, bool is_max)
 {
-    // wave reduce with shuffles, then across the 4 waves through LDS
+    // wave reduce with shuffles, then across the waves through LDS
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         const float y = __shfl_xor(x, off);
         x = is_max ? fmaxf(x, y) : x + y;
     }
     const int wave = threadIdx.x / kWave, nwv = blockDim.x / kWave;
-    __syncthreads();
     if ((threadIdx.x & (kWave - 1)) == 0) red[wave] = x;
     __syncthreads();
     x = red[0];
@@ -433,77 +480,119 @@ __device__ __forceinline__ float block_reduce(float x, float* red, bool is_max)
     return x;
 }
 
+// Merge kernel: one 256-thread workgroup per (query head, sequence, 64-dim
+// slice of head_dim).  16 threads read one partition row slice as float4s,
+// 16 row groups cover 16 partitions per pass; every load of the first 256
+// partitions is issued before the first reduction.  Empty partitions carry
+// max = -inf and denominator 0 and get weight 0.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams prm)
 {
-    constexpr int TPR = D / 4;            // threads per partition row (float4 each)
-    __shared__ float red[8];
+    constexpr int TPR = 16;               // threads per row slice (64 floats)
+    constexpr int RG = 256 / TPR;         // row groups
+    constexpr int RPT = 16;               // rows per thread held in registers
+    __shared__ float red[2][4];
     __shared__ f32x4 part[256];
-    const int h = blockIdx.x, b = blockIdx.y;
-    const int n = prm.context_lens[b];
-    const int lo = (prm.window > 0 && n > prm.window) ? n - prm.window : 0;
-    const int S = prm.partition_size;
-    const int np = n > lo ? (n + S - 1) / S - lo / S : 0;
+    const int h = blockIdx.x, b = blockIdx.y, dsl = blockIdx.z;
+    const int rg = threadIdx.x / TPR, c4 = threadIdx.x % TPR;
+    const int P = prm.num_partitions;
     const size_t hrow = size_t(b) * prm.num_q_heads + h;
-    if (np == 0) {
-        for (int d = threadIdx.x; d < D; d += blockDim.x) store_out<DT>(prm.out, hrow * D + d, 0.f);
-        if (prm.lse && threadIdx.x == 0) prm.lse[hrow] = -INFINITY;
+    const float* m = prm.ws_m + hrow * P;
+    const float* l = prm.ws_l + hrow * P;
+    const f32x4* o = reinterpret_cast<const f32x4*>(prm.ws_o + hrow * P * D) + dsl * TPR + c4;
+
+    // Rows rg, rg + RG, ... of the first pass, all loads in flight together.
+    float mr[RPT], lr[RPT];
+    f32x4 orow[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int p = rg + RG * i;
+        const bool ok = p < P;
+        mr[i] = ok ? m[p] : -INFINITY;
+        lr[i] = ok ? l[p] : 0.f;
+        orow[i] = ok ? o[size_t(p) * (D / 4)] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Phase 1: global max of the partition maxima.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) mx = fmaxf(mx, mr[i]);
+    for (int p = threadIdx.x + RG * RPT; p < P; p += blockDim.x) mx = fmaxf(mx, m[p]);
+    const float M = block_reduce(mx, red[0], true);
+    if (M == -INFINITY) {
+        // Every partition empty: out = 0, lse = -inf.
+        if (rg == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) store_out<DT>(prm.out, hrow * D + dsl * 64 + 4 * c4 + e, 0.f);
+        }
+        if (prm.lse && dsl == 0 && threadIdx.x == 0) prm.lse[hrow] = -INFINITY;
         return;
     }
-    const float* m = prm.ws_m + hrow * prm.num_partitions;
-    const float* l = prm.ws_l + hrow * prm.num_partitions;
-    const f32x4* o = reinterpret_cast<const f32x4*>(prm.ws_o + hrow * prm.num_partitions * D);
 
-    // Phase 1: global max, then the total of the rescaled denominators.
-    float mx = -INFINITY;
-    for (int p = threadIdx.x; p < np; p += blockDim.x) mx = fmaxf(mx, m[p]);
-    const float M = block_reduce(mx, red, true);
+    // Phase 2: rescale each partition's denominator and sum the weighted
+    // outputs (rescale_p = 2^(m_p - M) * l_p).
     float tl = 0.f;
-    for (int p = threadIdx.x; p < np; p += blockDim.x) tl += fast_exp2(m[p] - M) * l[p];
-    const float L = block_reduce(tl, red + 4, false);
-
-    // Phase 2: weighted sum of partition outputs.
-    const int rpp = blockDim.x / TPR;     // partition rows per pass
-    const int row0 = threadIdx.x / TPR, c4 = threadIdx.x % TPR;
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    for (int p = row0; p < np; p += rpp) {
-        const float w = fast_exp2(m[p] - M) * l[p];
-        const f32x4 v = o[size_t(p) * TPR + c4];
-        a += w * v;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const float w = lr[i] > 0.f ? fast_exp2(mr[i] - M) * lr[i] : 0.f;
+        tl += w;
+        if (w > 0.f) a += w * orow[i];
     }
+    for (int p = rg + RG * RPT; p < P; p += RG) {
+        const float lp = l[p];
+        const float w = lp > 0.f ? fast_exp2(m[p] - M) * lp : 0.f;
+        tl += w;
+        if (w > 0.f) a += w * o[size_t(p) * (D / 4)];
+    }
+    // Each row's weight is held by all TPR threads of its row group: count it once.
+    const float L = block_reduce(c4 == 0 ? tl : 0.f, red[1], false);
     part[threadIdx.x] = a;
     __syncthreads();
     if (threadIdx.x < TPR) {
         f32x4 t = part[threadIdx.x];
-        for (int r = 1; r < rpp; ++r) t += part[r * TPR + threadIdx.x];
+        for (int r = 1; r < RG; ++r) t += part[r * TPR + threadIdx.x];
         const float inv = 1.f / L;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) store_out<DT>(prm.out, hrow * D + 4 * threadIdx.x + e, t[e] * inv);
+        for (int e = 0; e < 4; ++e)
+            store_out<DT>(prm.out, hrow * D + dsl * 64 + 4 * threadIdx.x + e, t[e] * inv);
     }
-    if (prm.lse && threadIdx.x == 0) prm.lse[hrow] = (M + log2f(L)) * kLn2;
+    if (prm.lse && dsl == 0 && threadIdx.x == 0) prm.lse[hrow] = (M + log2f(L)) * kLn2;
+}
+
+// Launch through hipExtLaunchKernelGGL so optional start/stop events bracket
+// the kernel itself.
+template <typename K, typename P>
+hipError_t launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                  LaunchEvents ev, const P& p)
+{
+    if (ev.start || ev.stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, uint32_t(lds), stream, ev.start, ev.stop, 0, p);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, stream, p);
+    return hipGetLastError();
 }
 
 template <int DT, int D, int G>
 hipError_t launch_partial_t(const PartialParams& p, dim3 grid, dim3 block, size_t lds,
-                            hipStream_t stream)
+                            hipStream_t stream, LaunchEvents ev)
 {
     constexpr int EB = Elt<DT>::bytes;
     constexpr int NB = (512 / (D * EB)) < 1 ? 1 : ((512 / (D * EB)) > 4 ? 4 : 512 / (D * EB));
-    hipLaunchKernelGGL((partial_kernel<DT, D, G, NB>), grid, block, lds, stream, p);
-    return hipGetLastError();
+    return launch(partial_kernel<DT, D, G, NB>, grid, block, lds, stream, ev, p);
 }
 
 template <int DT, int D>
 hipError_t launch_partial_g(int group_t, const PartialParams& p, dim3 grid, dim3 block, size_t lds,
-                            hipStream_t stream)
+                            hipStream_t stream, LaunchEvents ev)
 {
     switch (group_t) {
-    case 1: return launch_partial_t<DT, D, 1>(p, grid, block, lds, stream);
-    case 2: return launch_partial_t<DT, D, 2>(p, grid, block, lds, stream);
-    case 4: return launch_partial_t<DT, D, 4>(p, grid, block, lds, stream);
-    case 6: return launch_partial_t<DT, D, 6>(p, grid, block, lds, stream);
-    case 8: return launch_partial_t<DT, D, 8>(p, grid, block, lds, stream);
-    case 16: return launch_partial_t<DT, D, 16>(p, grid, block, lds, stream);
+    case 1: return launch_partial_t<DT, D, 1>(p, grid, block, lds, stream, ev);
+    case 2: return launch_partial_t<DT, D, 2>(p, grid, block, lds, stream, ev);
+    case 4: return launch_partial_t<DT, D, 4>(p, grid, block, lds, stream, ev);
+    case 6: return launch_partial_t<DT, D, 6>(p, grid, block, lds, stream, ev);
+    case 8: return launch_partial_t<DT, D, 8>(p, grid, block, lds, stream, ev);
+    case 16: return launch_partial_t<DT, D, 16>(p, grid, block, lds, stream, ev);
     default: return hipErrorInvalidValue;
     }
 }
@@ -511,37 +600,28 @@ hipError_t launch_partial_g(int group_t, const PartialParams& p, dim3 grid, dim3
 }  // namespace
 
 hipError_t launch_partial(int dtype, int head_dim, int group_t, const PartialParams& p, dim3 grid,
-                          dim3 block, size_t lds, hipStream_t stream)
+                          dim3 block, size_t lds, hipStream_t stream, LaunchEvents ev)
 {
-    if (dtype == PA_DTYPE_F32) {
-        if (head_dim == 64) return launch_partial_g<PA_DTYPE_F32, 64>(group_t, p, grid, block, lds, stream);
-        return hipErrorInvalidValue;
-    }
+#define PA_PARTIAL(DT, D) return launch_partial_g<DT, D>(group_t, p, grid, block, lds, stream, ev);
+    if (dtype == PA_DTYPE_F32 && head_dim == 64) { PA_PARTIAL(PA_DTYPE_F32, 64) }
     if (dtype == PA_DTYPE_F16) {
-        switch (head_dim) {
-        case 64: return launch_partial_g<PA_DTYPE_F16, 64>(group_t, p, grid, block, lds, stream);
-        case 128: return launch_partial_g<PA_DTYPE_F16, 128>(group_t, p, grid, block, lds, stream);
-        case 256: return launch_partial_g<PA_DTYPE_F16, 256>(group_t, p, grid, block, lds, stream);
-        default: return hipErrorInvalidValue;
-        }
+        if (head_dim == 64) { PA_PARTIAL(PA_DTYPE_F16, 64) }
+        if (head_dim == 128) { PA_PARTIAL(PA_DTYPE_F16, 128) }
+        if (head_dim == 256) { PA_PARTIAL(PA_DTYPE_F16, 256) }
     }
     if (dtype == PA_DTYPE_BF16) {
-        switch (head_dim) {
-        case 64: return launch_partial_g<PA_DTYPE_BF16, 64>(group_t, p, grid, block, lds, stream);
-        case 128: return launch_partial_g<PA_DTYPE_BF16, 128>(group_t, p, grid, block, lds, stream);
-        case 256: return launch_partial_g<PA_DTYPE_BF16, 256>(group_t, p, grid, block, lds, stream);
-        default: return hipErrorInvalidValue;
-        }
+        if (head_dim == 64) { PA_PARTIAL(PA_DTYPE_BF16, 64) }
+        if (head_dim == 128) { PA_PARTIAL(PA_DTYPE_BF16, 128) }
+        if (head_dim == 256) { PA_PARTIAL(PA_DTYPE_BF16, 256) }
     }
+#undef PA_PARTIAL
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, dim3 grid, dim3 block,
-                        hipStream_t stream)
+                        hipStream_t stream, LaunchEvents ev)
 {
-#define PA_MERGE(DT, D) \
-    hipLaunchKernelGGL((merge_kernel<DT, D>), grid, block, 0, stream, p); \
-    return hipGetLastError();
+#define PA_MERGE(DT, D) return launch(merge_kernel<DT, D>, grid, block, 0, stream, ev, p);
     if (dtype == PA_DTYPE_F32 && head_dim == 64) { PA_MERGE(PA_DTYPE_F32, 64) }
     if (dtype == PA_DTYPE_F16) {
         if (head_dim == 64) { PA_MERGE(PA_DTYPE_F16, 64) }

@@ -59,7 +59,7 @@ WorkspaceLayout workspace_layout(const pa_decode_desc& d, int batch, int num_par
     size_t rows = size_t(batch) * size_t(d.num_q_heads) * size_t(num_partitions);
     WorkspaceLayout w;
     w.o_off = 0;
-    w.m_off = align(rows * size_t(d.head_dim) * sizeof(float));
+    w.m_off = w.o_off + align(rows * size_t(d.head_dim) * sizeof(float));
     w.l_off = w.m_off + align(rows * sizeof(float));
     w.total = w.l_off + align(rows * sizeof(float));
     return w;
@@ -122,6 +122,11 @@ int make_plan(const pa_decode_desc& d, int num_cus, int batch, int max_context_l
     int64_t blocks = ceil_div(ceil_div(std::min<int64_t>(S, std::max<int64_t>(visible, 1)), ps) +
                                   (windowed ? 1 : 0), nb);
     nw = int(std::max<int64_t>(1, std::min<int64_t>(kMaxWavesPerGroup, blocks)));
+    // Experiments only: PA_DECODE_WAVES overrides the waves per workgroup.
+    if (const char* env = std::getenv("PA_DECODE_WAVES")) {
+        const int v = std::atoi(env);
+        if (v >= 1 && v <= kMaxWavesPerGroup) nw = v;
+    }
     // Keep the workgroup's combine buffer within 64 KiB of LDS.
     {
         const int G = template_group(d.num_q_heads / d.num_kv_heads);
@@ -143,7 +148,7 @@ int make_plan(const pa_decode_desc& d, int num_cus, int batch, int max_context_l
     if (split) {
         p.grid_merge[0] = d.num_q_heads;
         p.grid_merge[1] = batch;
-        p.grid_merge[2] = 1;
+        p.grid_merge[2] = d.head_dim / 64;
         p.block_merge = kMergeThreads;
         p.workspace_bytes = int64_t(workspace_layout(d, batch, int(P)).total);
     }

@@ -45,7 +45,7 @@ int make_plan(const pa_decode_desc& d, int num_cus, int batch, int max_context_l
 size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan);
 
 // Workspace layout of a split plan: partition outputs o[B][Hq][P][D] (f32),
-// then maxima m[B][Hq][P] and denominators l[B][Hq][P] (f32), each region
+// maxima m[B][Hq][P] and denominators l[B][Hq][P] (f32), each region
 // 256-byte aligned.
 struct WorkspaceLayout {
     size_t o_off, m_off, l_off, total;

@@ -106,7 +106,7 @@ def test_plan_covers_every_context(name):
             assert p.grid_partial[1] == w.num_kv_heads
             assert 64 <= p.block_partial <= 256 and p.block_partial % 64 == 0
             if p.split:
-                assert p.grid_merge[:2] == [w.num_q_heads, w.batch]
+                assert list(p.grid_merge) == [w.num_q_heads, w.batch, w.head_dim // 64]
                 rows = w.batch * w.num_q_heads * p.num_partitions
                 assert p.workspace_bytes >= rows * (w.head_dim + 2) * 4
             else:

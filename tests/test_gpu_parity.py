@@ -161,3 +161,62 @@ def test_workspace_too_small_is_reported():
     with pytest.raises(B.PaDecodeError) as e:
         eng.run_args(args)
     assert e.value.status == B.PA_DECODE_WORKSPACE_TOO_SMALL
+
+
+def test_repeated_calls_reuse_the_workspace():
+    """Many calls with different plans on one workspace: each is right, and a
+    repeated plan gives identical bits."""
+    w = W.CONFIGS["llama8b_b16_ragged_f16"]
+    p = W.generate(w)
+    d = to_device(p)
+    eng = engine(p)
+    out = torch.empty_like(d.q)
+    lse = torch.empty(d.q.shape[:2], dtype=torch.float32, device="cuda")
+    results = []
+    for S in (0, 64, 0, 1024, 16, 0):
+        args = eng.make_args(d.q, d.k_cache, d.v_cache, d.page_table, d.context_lens, p.scale,
+                             out, lse, max_context_len=p.max_context_len, partition_size=S)
+        for _ in range(3):
+            eng.run_args(args)
+        torch.cuda.synchronize()
+        results.append((S, out.cpu(), lse.cpu()))
+    ref = run_oracle(p)
+    for S, o, l in results:
+        compare(o, l, ref[0], ref[1], w.dtype, "repeat S=%d" % S)
+    base = [r for r in results if r[0] == 0]
+    for _, o, l in base[1:]:
+        assert torch.equal(o, base[0][1]) and torch.equal(l, base[0][2])
+
+
+@pytest.mark.parametrize("name", ["llama1b_ctx3060_f16", "ctx100k_gqa6_f16"])
+def test_graph_replays_match_eager(name):
+    """Captured steps replayed several times, with eager work and syncs between
+    replays, give the eager result every time."""
+    p = W.generate(W.CONFIGS[name])
+    d = to_device(p)
+    eng = engine(p)
+    out = torch.empty_like(d.q)
+    lse = torch.empty(d.q.shape[:2], dtype=torch.float32, device="cuda")
+    args = eng.make_args(d.q, d.k_cache, d.v_cache, d.page_table, d.context_lens, p.scale, out,
+                         lse, max_context_len=p.max_context_len,
+                         partition_size=p.workload.partition_size)
+    eng.run_args(args)
+    torch.cuda.synchronize()
+    eager = (out.clone(), lse.clone())
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            eng.run_args(args, torch.cuda.current_stream().cuda_stream)
+            eng.run_args(args, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(4):
+        out.zero_()
+        lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[0]) and torch.equal(lse, eager[1]), "replay %d" % i
+        eng.run_args(args)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[0])
