@@ -115,15 +115,20 @@ typedef struct pa_decode_args {
 typedef struct pa_decode_plan {
     int32_t split;              /* 1: partial kernel + merge kernel; 0: partial only */
     int32_t partition_size;     /* S, tokens per partition */
-    int32_t num_partitions;     /* partitions per (sequence, KV head) in the grid */
+    int32_t num_partitions;     /* partitions per (sequence, KV head) */
     int32_t waves_per_group;    /* waves per workgroup of the partial kernel */
+    int32_t waves_per_partition;/* waves of a workgroup sharing one partition; a   */
+                                /*   workgroup covers waves_per_group /            */
+                                /*   waves_per_partition consecutive partitions    */
     int32_t pages_per_block;    /* pages each wave holds in flight per step */
-    int32_t grid_partial[3];    /* partial kernel grid (x = partition, y = KV head, z = b) */
+    int32_t grid_partial[3];    /* partial kernel grid (x = group of partitions,    */
+                                /*   y = KV head, z = b)                            */
     int32_t block_partial;      /* threads per workgroup of the partial kernel */
     int32_t grid_merge[3];      /* merge kernel grid (x = query head, y = b, z = 64-dim */
                                 /*   slice of head_dim; 0s when split == 0)           */
     int32_t block_merge;
     int32_t num_cus;            /* compute units the plan was made for */
+    int32_t waves_per_cu;       /* partial-kernel waves one compute unit holds     */
     int64_t workspace_bytes;    /* bytes of workspace the plan needs */
 } pa_decode_plan;
 
@@ -157,9 +162,11 @@ int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* str
 int pa_decode_last_plan(pa_decode_handle handle, pa_decode_plan* plan);
 
 /* Plan without a handle or device (pure host): the same planner that
- * pa_decode_run uses, for a given compute-unit count. */
-int pa_decode_plan_query(const pa_decode_desc* desc, int32_t num_cus, int32_t batch,
-                         int32_t max_context_len, int32_t sliding_window,
+ * pa_decode_run uses, for a given compute-unit count and number of
+ * partial-kernel waves a compute unit holds at once (pa_decode_run uses the
+ * device's values; the plan of a run reports them). */
+int pa_decode_plan_query(const pa_decode_desc* desc, int32_t num_cus, int32_t waves_per_cu,
+                         int32_t batch, int32_t max_context_len, int32_t sliding_window,
                          int32_t partition_size, pa_decode_plan* plan);
 
 /* Kernel timing for measurement tools.  After pa_decode_profile_begin, the

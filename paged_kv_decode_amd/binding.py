@@ -61,18 +61,21 @@ class PaDecodeArgs(ctypes.Structure):
 class PaDecodePlan(ctypes.Structure):
     _fields_ = [("split", ctypes.c_int32), ("partition_size", ctypes.c_int32),
                 ("num_partitions", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
-                ("pages_per_block", ctypes.c_int32), ("grid_partial", ctypes.c_int32 * 3),
+                ("waves_per_partition", ctypes.c_int32), ("pages_per_block", ctypes.c_int32), ("grid_partial", ctypes.c_int32 * 3),
                 ("block_partial", ctypes.c_int32), ("grid_merge", ctypes.c_int32 * 3),
                 ("block_merge", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+                ("waves_per_cu", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self):
         return {"split": self.split, "partition_size": self.partition_size,
                 "num_partitions": self.num_partitions, "waves_per_group": self.waves_per_group,
+                "waves_per_partition": self.waves_per_partition,
                 "pages_per_block": self.pages_per_block,
                 "grid_partial": list(self.grid_partial), "block_partial": self.block_partial,
                 "grid_merge": list(self.grid_merge), "block_merge": self.block_merge,
-                "num_cus": self.num_cus, "workspace_bytes": self.workspace_bytes}
+                "num_cus": self.num_cus, "waves_per_cu": self.waves_per_cu,
+                "workspace_bytes": self.workspace_bytes}
 
 
 class PaDecodeError(RuntimeError):
@@ -104,7 +107,7 @@ def load_library(path: Optional[str] = None):
         lib.pa_decode_run.argtypes = [vp, ctypes.POINTER(PaDecodeArgs), vp]
         lib.pa_decode_last_plan.argtypes = [vp, ctypes.POINTER(PaDecodePlan)]
         lib.pa_decode_plan_query.argtypes = [ctypes.POINTER(PaDecodeDesc), i32, i32, i32, i32,
-                                             i32, ctypes.POINTER(PaDecodePlan)]
+                                             i32, i32, ctypes.POINTER(PaDecodePlan)]
         lib.pa_decode_profile_begin.argtypes = [vp, i32]
         lib.pa_decode_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                               ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double),
@@ -161,10 +164,11 @@ def pa_decode_last_plan(handle) -> PaDecodePlan:
     return plan
 
 
-def pa_decode_plan_query(desc: PaDecodeDesc, num_cus: int, batch: int, max_context_len: int,
-                         sliding_window: int = 0, partition_size: int = 0) -> PaDecodePlan:
+def pa_decode_plan_query(desc: PaDecodeDesc, num_cus: int, waves_per_cu: int, batch: int,
+                         max_context_len: int, sliding_window: int = 0,
+                         partition_size: int = 0) -> PaDecodePlan:
     plan = PaDecodePlan()
-    _check(load_library().pa_decode_plan_query(ctypes.byref(desc), num_cus, batch,
+    _check(load_library().pa_decode_plan_query(ctypes.byref(desc), num_cus, waves_per_cu, batch,
                                                max_context_len, sliding_window, partition_size,
                                                ctypes.byref(plan)),
            "pa_decode_plan_query")

@@ -19,7 +19,8 @@ struct PartialParams {
     int32_t num_q_heads;
     int32_t group;            // actual G = Hq / Hkv
     int32_t partition_size;   // S tokens
-    int32_t num_partitions;   // P (grid x)
+    int32_t num_partitions;   // P: partitions per (sequence, KV head)
+    int32_t waves_per_partition;  // waves of a workgroup that share one partition
     int32_t window;           // <= 0: none
     float scale_log2;         // scale * log2(e)
     int32_t split;            // 1: write partition states; 0: write out/lse
@@ -56,5 +57,9 @@ hipError_t launch_partial(int dtype, int head_dim, int group_t, const PartialPar
                           LaunchEvents ev);
 hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, dim3 grid, dim3 block,
                         hipStream_t stream, LaunchEvents ev);
+
+// Waves of the partial kernel (256-thread workgroups with `lds_bytes` of
+// dynamic LDS) that one compute unit holds at once; 0 when unknown.
+int partial_waves_per_cu(int dtype, int head_dim, int group_t, size_t lds_bytes);
 
 }  // namespace pa

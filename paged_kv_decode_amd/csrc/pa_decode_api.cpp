@@ -43,6 +43,7 @@ struct EventRing {
 struct pa_decode_handle_s {
     pa_decode_desc desc;
     int num_cus;
+    int waves_per_cu;  // partial-kernel waves one compute unit holds at once
     pa_decode_plan last_plan;
     bool has_plan;
     int last_hip_error;
@@ -109,6 +110,17 @@ int pa_decode_create(const pa_decode_desc* desc, pa_decode_handle* handle)
         return PA_DECODE_HIP_ERROR;
     h->desc = *desc;
     h->num_cus = cus;
+    {
+        // Occupancy of the partial kernel this description uses, for a
+        // four-wave workgroup.
+        pa_decode_plan probe = {};
+        probe.waves_per_group = pa::kMaxWavesPerGroup;
+        probe.pages_per_block = pa::pages_per_block(desc->head_dim, desc->dtype);
+        const int G = desc->num_q_heads / desc->num_kv_heads;
+        int w = pa::partial_waves_per_cu(desc->dtype, desc->head_dim, pa::template_group(G),
+                                         pa::partial_lds_bytes(*desc, probe));
+        h->waves_per_cu = w > 0 ? w : 8;
+    }
     h->has_plan = false;
     h->last_hip_error = 0;
     h->profiling = false;
@@ -189,7 +201,8 @@ int pa_decode_workspace_size(pa_decode_handle handle, int32_t batch, int32_t max
     if (!handle || !bytes)
         return PA_DECODE_INVALID_ARG;
     pa_decode_plan plan;
-    int st = pa::make_plan(handle->desc, handle->num_cus, batch, max_context_len, sliding_window,
+    int st = pa::make_plan(handle->desc, handle->num_cus, handle->waves_per_cu, batch,
+                           max_context_len, sliding_window,
                            partition_size, &plan);
     if (st != PA_DECODE_OK)
         return st;
@@ -197,14 +210,14 @@ int pa_decode_workspace_size(pa_decode_handle handle, int32_t batch, int32_t max
     return PA_DECODE_OK;
 }
 
-int pa_decode_plan_query(const pa_decode_desc* desc, int32_t num_cus, int32_t batch,
-                         int32_t max_context_len, int32_t sliding_window, int32_t partition_size,
-                         pa_decode_plan* plan)
+int pa_decode_plan_query(const pa_decode_desc* desc, int32_t num_cus, int32_t waves_per_cu,
+                         int32_t batch, int32_t max_context_len, int32_t sliding_window,
+                         int32_t partition_size, pa_decode_plan* plan)
 {
     if (!desc || !plan)
         return PA_DECODE_INVALID_ARG;
-    return pa::make_plan(*desc, num_cus, batch, max_context_len, sliding_window, partition_size,
-                         plan);
+    return pa::make_plan(*desc, num_cus, waves_per_cu, batch, max_context_len, sliding_window,
+                         partition_size, plan);
 }
 
 int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* stream)
@@ -217,7 +230,8 @@ int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* str
     if (st != PA_DECODE_OK)
         return st;
     pa_decode_plan plan;
-    st = pa::make_plan(d, handle->num_cus, a.batch, a.max_context_len, a.sliding_window,
+    st = pa::make_plan(d, handle->num_cus, handle->waves_per_cu, a.batch, a.max_context_len,
+                       a.sliding_window,
                        a.partition_size, &plan);
     if (st != PA_DECODE_OK)
         return st;
@@ -249,6 +263,7 @@ int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* str
     pp.group = G;
     pp.partition_size = plan.partition_size;
     pp.num_partitions = plan.num_partitions;
+    pp.waves_per_partition = plan.waves_per_partition;
     pp.window = a.sliding_window;
     pp.scale_log2 = float(double(a.scale) * 1.4426950408889634);
     pp.split = plan.split;

@@ -108,6 +108,11 @@ __device__ __forceinline__ void wave_lds_sync()
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Compiler-only memory barrier: keeps prefetch loads where they are written
+// (otherwise they are sunk next to their first use, which undoes the
+// software pipeline); emits no instruction.
+__device__ __forceinline__ void pin_loads() { asm volatile("" ::: "memory"); }
+
 // ---- element conversion of one 16-byte chunk ----
 template <int DT> struct Chunk;
 
@@ -179,12 +184,17 @@ __device__ __forceinline__ u32x4 load16(const void* p) { return *static_cast<con
 // Partial kernel.
 //   DT: element type; D: head_dim; G: instantiated group size (>= actual);
 //   NB: pages per block.
+// Workgroup: blockDim.x / 64 waves split into partition slots of
+// prm.waves_per_partition waves; slot j of workgroup x handles partition
+// x * slots + j of KV head blockIdx.y of sequence blockIdx.z.
 // Lane maps (lane = 0..63, i16 = lane % 16, grp = lane / 16):
 //   K / MFMA:  lane loads chunk 4*ks + grp of key row i16 of a page,
 //              ks = 0..KS-1; the MFMA result element r of the lane is the score
 //              of query head 4*grp + r against token i16.
 //   V / P.V:   lane owns chunk c = lane % CH of token rows rho = lane / CH,
 //              rho + R, ..., rho + R*(KS-1) of a page.
+// LDS: [q tile (head_dim 256 only)][per-wave p / alpha buffers]; after the
+// main loop the whole area is reused for the combine of the slot's waves.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int G, int NB>
 __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
@@ -197,6 +207,8 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     constexpr int GP4 = (G + 3) / 4 * 4;
     constexpr int HG = (G + 3) / 4;   // 16-lane groups that carry real heads
     constexpr int IPV = kWave / NB;   // loop iterations one page-id vector covers
+    constexpr bool QLDS = KS >= 8;    // q operand read from LDS (saves 4*KS VGPRs)
+    constexpr int QTILE = QLDS ? KS * kWave * 4 : 0;  // floats
     static_assert(KS * 4 == CH && R * CH == kWave && R * KS == kPage, "lane map");
 
     extern __shared__ float smem[];
@@ -205,7 +217,10 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     // that page ids and loop bounds are scalar too.
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nw = blockDim.x / kWave;
-    const int prel = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int wpp = prm.waves_per_partition;
+    const int slot = wave / wpp, wi = wave % wpp;
+    const int prel = blockIdx.x * (nw / wpp) + slot;
+    const int kvh = blockIdx.y, b = blockIdx.z;
     const int Gact = prm.group;
     const int S = prm.partition_size;
     const int32_t* pt_row = prm.page_table + size_t(b) * prm.pt_stride;
@@ -213,60 +228,57 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     const int rho = lane / CH, c = lane % CH;
 
     // Page ids of this wave's pages, one per lane: lane j holds the page of
-    // block (wave + nw * (it0 + j / NB)), page j % NB of the partition that
+    // block (wi + wpp * (it0 + j / NB)), page j % NB of the partition that
     // starts at page pg_first; entries at or past pg_end are not read.
     auto load_ids = [&](int pg_first, int pg_end, int it0) {
         const int it = it0 + lane / NB;
-        const int pg = pg_first + (wave + nw * it) * NB + lane % NB;
+        const int pg = pg_first + (wi + wpp * it) * NB + lane % NB;
         return pg < pg_end ? pt_row[pg] : 0;
     };
     // Without a window the partition's first page does not depend on the
     // context length: fetch the page ids together with the length and q.
     int ids = 0;
-    if (prm.window <= 0) {
+    if (prm.window <= 0 && prel < prm.num_partitions) {
         const int pgs = prel * (S / kPage);
         ids = load_ids(pgs, min(pgs + S / kPage, prm.pt_stride), 0);
     }
 
     // q as the MFMA A operand: row i16 = query head kvh*G + i16 (zero past G).
-    u32x4 qa[KS];
+    u32x4 qa[QLDS ? 1 : KS];
     {
         const bool real = i16 < Gact;
         const char* qrow = static_cast<const char*>(prm.q) +
                            (size_t(b) * prm.num_q_heads + size_t(kvh) * Gact + (real ? i16 : 0)) * D * EB;
+        if constexpr (QLDS) {
+            // One copy per workgroup: [ks][lane] 16-byte chunks.
+            u32x4* qt = reinterpret_cast<u32x4*>(smem);
+            for (int ks = wave; ks < KS; ks += nw) {
+                u32x4 z = {0u, 0u, 0u, 0u};
+                qt[ks * kWave + lane] = real ? load16(qrow + (4 * ks + grp) * 16) : z;
+            }
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 z = {0u, 0u, 0u, 0u};
-            qa[ks] = real ? load16(qrow + (4 * ks + grp) * 16) : z;
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 z = {0u, 0u, 0u, 0u};
+                qa[ks] = real ? load16(qrow + (4 * ks + grp) * 16) : z;
+            }
         }
     }
+    auto q_operand = [&](int ks) -> u32x4 {
+        if constexpr (QLDS)
+            return reinterpret_cast<const u32x4*>(smem)[ks * kWave + lane];
+        else
+            return qa[ks];
+    };
 
     const int n = prm.context_lens[b];
     const int lo = (prm.window > 0 && n > prm.window) ? n - prm.window : 0;
     const int pabs = lo / S + prel;
     const int t0 = max(pabs * S, lo);
     const int t1 = min(pabs * S + S, n);
-    if (t0 >= t1) {
-        if (prm.split) {
-            // Empty partition: a state the merge gives zero weight.
-            if (threadIdx.x < Gact) {
-                const size_t row = (size_t(b) * prm.num_q_heads + size_t(kvh) * Gact + threadIdx.x) *
-                                       prm.num_partitions + prel;
-                prm.ws_m[row] = -INFINITY;
-                prm.ws_l[row] = 0.f;
-            }
-        } else if (prel == 0) {
-            // Empty context: out = 0, lse = -inf.
-            for (int idx = threadIdx.x; idx < Gact * D; idx += blockDim.x) {
-                const int h = kvh * Gact + idx / D;
-                store_out<DT>(prm.out, (size_t(b) * prm.num_q_heads + h) * D + idx % D, 0.f);
-            }
-            if (prm.lse && threadIdx.x < Gact)
-                prm.lse[size_t(b) * prm.num_q_heads + kvh * Gact + threadIdx.x] = -INFINITY;
-        }
-    } else {
+    const bool active = prel < prm.num_partitions && t0 < t1;
     const int pg0 = t0 / kPage, pg1 = (t1 + kPage - 1) / kPage;
-    if (prm.window > 0)
+    if (prm.window > 0 && active)
         ids = load_ids(pg0, pg1, 0);
 
     const int64_t ss = prm.stride_slot;
@@ -287,41 +299,63 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[g][e] = 0.f;
 
-    float* pbuf = smem + wave * (NB * kPage * GP4 + GP4);
+    float* pbuf = smem + QTILE + wave * (NB * kPage * GP4 + GP4);
     float* abuf = pbuf + NB * kPage * GP4;
 
-    const int nblk = (pg1 - pg0 + NB - 1) / NB;
-    const int nit = nblk > wave ? (nblk - wave + nw - 1) / nw : 0;
+    const int nblk = active ? (pg1 - pg0 + NB - 1) / NB : 0;
+    const int nit = nblk > wi ? (nblk - wi + wpp - 1) / wpp : 0;
+    if constexpr (QLDS) __syncthreads();   // q tile written
 
-    for (int it = 0; it < nit; ++it) {
-        if (it > 0 && it % IPV == 0)
-            ids = load_ids(pg0, pg1, it);
-        const int pgb = pg0 + (wave + nw * it) * NB;
-        const int nbv = min(NB, pg1 - pgb);
-        // All page ids of the block into scalar registers before any load.
-        int64_t page[NB];
+    // Software pipeline over the wave's blocks: block it+1's K is requested as
+    // soon as block it's scores are formed (the K registers are free again),
+    // and block it+1's V as soon as block it's P.V is done, so one of the two
+    // is always in flight while the other is used.  Every phase issues exactly
+    // NB*KS loads (pages missing from a short block re-read the block's last
+    // page; the last iteration re-reads its own block) so that the wait for K
+    // can leave V in flight and vice versa.
+    u32x4 kr[NB][KS], vr[NB][KS];
+    int64_t page[NB];
+    auto fetch_ids = [&](int it, int it0) {
+        // Page ids of block `it` into scalar registers (ids holds the blocks
+        // it0 .. it0 + IPV - 1).
+        const int nbv_ = min(NB, pg1 - (pg0 + (wi + wpp * it) * NB));
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) page[nb] = __builtin_amdgcn_readlane(ids, (it % IPV) * NB + nb);
-        u32x4 kr[NB][KS], vr[NB][KS];
+        for (int nb = 0; nb < NB; ++nb)
+            page[nb] = __builtin_amdgcn_readlane(ids, (it - it0) * NB + min(nb, nbv_ - 1));
+    };
+    auto issue_k = [&]() {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            if (nb < nbv) {
-                const char* kp = kbase + page[nb] * prm.stride_page * EB;
-                const char* vp = vbase + page[nb] * prm.stride_page * EB;
+            const char* kp = kbase + page[nb] * prm.stride_page * EB;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    kr[nb][ks] = load16(kp + (k_lane_off + int64_t(4 * ks) * EPC) * EB);
-#pragma unroll
-                for (int i = 0; i < KS; ++i)
-                    vr[nb][i] = load16(vp + (v_lane_off + int64_t(R * i) * ss) * EB);
-            } else {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    kr[nb][ks] = u32x4{0u, 0u, 0u, 0u};
-                    vr[nb][ks] = u32x4{0u, 0u, 0u, 0u};
-                }
-            }
+            for (int ks = 0; ks < KS; ++ks)
+                kr[nb][ks] = load16(kp + (k_lane_off + int64_t(4 * ks) * EPC) * EB);
         }
+    };
+    auto issue_v = [&]() {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const char* vp = vbase + page[nb] * prm.stride_page * EB;
+#pragma unroll
+            for (int i = 0; i < KS; ++i)
+                vr[nb][i] = load16(vp + (v_lane_off + int64_t(R * i) * ss) * EB);
+        }
+    };
+
+    // Outer loop over chunks of IPV blocks (one page-id vector each); the
+    // pipelined inner loop itself issues no load but K/V.
+    for (int it0 = 0; it0 < nit; it0 += IPV) {
+    const int it1 = min(nit, it0 + IPV);
+    if (it0 > 0)
+        ids = load_ids(pg0, pg1, it0);
+    fetch_ids(it0, it0);
+    issue_k();
+    issue_v();
+    pin_loads();
+
+    for (int it = it0; it < it1; ++it) {
+        const int pgb = pg0 + (wi + wpp * it) * NB;
+        const int nbv = min(NB, pg1 - pgb);
 
         // Scores (base 2) of head 4*grp + r against token i16 of each page.
         float s[NB][4];
@@ -329,12 +363,15 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         for (int nb = 0; nb < NB; ++nb) {
             f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) d = Chunk<DT>::mfma(qa[ks], kr[nb][ks], d);
+            for (int ks = 0; ks < KS; ++ks) d = Chunk<DT>::mfma(q_operand(ks), kr[nb][ks], d);
             const int tok = (pgb + nb) * kPage + i16;
             const bool ok = nb < nbv && tok >= t0 && tok < t1;
 #pragma unroll
             for (int r = 0; r < 4; ++r) s[nb][r] = ok ? d[r] * prm.scale_log2 : -INFINITY;
         }
+        fetch_ids(min(it + 1, it1 - 1), it0);
+        issue_k();
+        pin_loads();
 
         float alpha[4];
 #pragma unroll
@@ -402,7 +439,10 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
             }
         }
         wave_lds_sync();
+        issue_v();
+        pin_loads();
     }
+    }  // chunks of IPV blocks
 
     // Wave-level reductions: denominators over the 16 token lanes, outputs
     // over the R token rows (lanes c, c + CH, ...).
@@ -413,7 +453,10 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[g][e] = sum_rows<CH>(acc[g][e]);
 
-    // Workgroup combine in LDS.
+    // Combine the waves of each partition slot in LDS: maximum first, then
+    // the rescaled denominators and outputs.  A wave without blocks holds
+    // max = -inf, denominator 0 and contributes nothing; a slot whose
+    // partition is empty ends with max = -inf.
     __syncthreads();
     float* cm = smem;               // [nw][GP4]
     float* cl = cm + nw * GP4;      // [nw][GP4]
@@ -433,32 +476,37 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     }
     __syncthreads();
 
-    for (int idx = threadIdx.x; idx < Gact * D; idx += blockDim.x) {
-        const int g = idx / D, dd = idx % D;
+    const int nslots = nw / wpp;
+    for (int idx = threadIdx.x; idx < nslots * Gact * D; idx += blockDim.x) {
+        const int sl = idx / (Gact * D), g = (idx / D) % Gact, dd = idx % D;
+        const int p_rel = blockIdx.x * nslots + sl;
+        if (p_rel >= prm.num_partitions) continue;
         float M = -INFINITY;
-        for (int w = 0; w < nw; ++w) M = fmaxf(M, cm[w * GP4 + g]);
+        for (int w = sl * wpp; w < sl * wpp + wpp; ++w) M = fmaxf(M, cm[w * GP4 + g]);
         float L = 0.f, o = 0.f;
-        for (int w = 0; w < nw; ++w) {
-            const float sc = fast_exp2(cm[w * GP4 + g] - M);
-            L += sc * cl[w * GP4 + g];
-            o += sc * ca[(w * G + g) * D + dd];
+        if (M != -INFINITY) {
+            for (int w = sl * wpp; w < sl * wpp + wpp; ++w) {
+                const float sc = fast_exp2(cm[w * GP4 + g] - M);
+                L += sc * cl[w * GP4 + g];
+                o += sc * ca[(w * G + g) * D + dd];
+            }
+            o = o / L;
         }
-        o = o / L;
         const size_t h = size_t(b) * prm.num_q_heads + size_t(kvh) * Gact + g;
         if (prm.split) {
-            const size_t row = h * prm.num_partitions + prel;
+            const size_t row = h * prm.num_partitions + p_rel;
             prm.ws_o[row * D + dd] = o;
             if (dd == 0) {
                 prm.ws_m[row] = M;
                 prm.ws_l[row] = L;
             }
         } else {
+            // One partition covers the context: write the result (an empty
+            // context gives out = 0, lse = -inf).
             store_out<DT>(prm.out, h * D + dd, o);
-            if (dd == 0 && prm.lse) prm.lse[h] = (M + log2f(L)) * kLn2;
+            if (dd == 0 && prm.lse) prm.lse[h] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
         }
     }
-    }  // non-empty partition
-
 }
 
 // ---------------------------------------------------------------------------
@@ -573,13 +621,44 @@ hipError_t launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t strea
     return hipGetLastError();
 }
 
+template <int DT, int D>
+constexpr int pages_per_block_t()
+{
+    constexpr int EB = Elt<DT>::bytes;
+    return (512 / (D * EB)) < 1 ? 1 : ((512 / (D * EB)) > 4 ? 4 : 512 / (D * EB));
+}
+
 template <int DT, int D, int G>
 hipError_t launch_partial_t(const PartialParams& p, dim3 grid, dim3 block, size_t lds,
                             hipStream_t stream, LaunchEvents ev)
 {
-    constexpr int EB = Elt<DT>::bytes;
-    constexpr int NB = (512 / (D * EB)) < 1 ? 1 : ((512 / (D * EB)) > 4 ? 4 : 512 / (D * EB));
-    return launch(partial_kernel<DT, D, G, NB>, grid, block, lds, stream, ev, p);
+    return launch(partial_kernel<DT, D, G, pages_per_block_t<DT, D>()>, grid, block, lds, stream, ev,
+                  p);
+}
+
+template <int DT, int D, int G>
+int waves_per_cu_t(size_t lds)
+{
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &blocks, reinterpret_cast<const void*>(partial_kernel<DT, D, G, pages_per_block_t<DT, D>()>),
+            256, lds) != hipSuccess)
+        return 0;
+    return blocks * 4;
+}
+
+template <int DT, int D>
+int waves_per_cu_g(int group_t, size_t lds)
+{
+    switch (group_t) {
+    case 1: return waves_per_cu_t<DT, D, 1>(lds);
+    case 2: return waves_per_cu_t<DT, D, 2>(lds);
+    case 4: return waves_per_cu_t<DT, D, 4>(lds);
+    case 6: return waves_per_cu_t<DT, D, 6>(lds);
+    case 8: return waves_per_cu_t<DT, D, 8>(lds);
+    case 16: return waves_per_cu_t<DT, D, 16>(lds);
+    default: return 0;
+    }
 }
 
 template <int DT, int D>
@@ -616,6 +695,24 @@ hipError_t launch_partial(int dtype, int head_dim, int group_t, const PartialPar
     }
 #undef PA_PARTIAL
     return hipErrorInvalidValue;
+}
+
+int partial_waves_per_cu(int dtype, int head_dim, int group_t, size_t lds)
+{
+#define PA_OCC(DT, D) return waves_per_cu_g<DT, D>(group_t, lds);
+    if (dtype == PA_DTYPE_F32 && head_dim == 64) { PA_OCC(PA_DTYPE_F32, 64) }
+    if (dtype == PA_DTYPE_F16) {
+        if (head_dim == 64) { PA_OCC(PA_DTYPE_F16, 64) }
+        if (head_dim == 128) { PA_OCC(PA_DTYPE_F16, 128) }
+        if (head_dim == 256) { PA_OCC(PA_DTYPE_F16, 256) }
+    }
+    if (dtype == PA_DTYPE_BF16) {
+        if (head_dim == 64) { PA_OCC(PA_DTYPE_BF16, 64) }
+        if (head_dim == 128) { PA_OCC(PA_DTYPE_BF16, 128) }
+        if (head_dim == 256) { PA_OCC(PA_DTYPE_BF16, 256) }
+    }
+#undef PA_OCC
+    return 0;
 }
 
 hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, dim3 grid, dim3 block,

@@ -65,43 +65,46 @@ WorkspaceLayout workspace_layout(const pa_decode_desc& d, int batch, int num_par
     return w;
 }
 
-int make_plan(const pa_decode_desc& d, int num_cus, int batch, int max_context_len,
-              int sliding_window, int partition_size, pa_decode_plan* plan)
+int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
+              int max_context_len, int sliding_window, int partition_size,
+              pa_decode_plan* plan)
 {
     if (!plan)
         return PA_DECODE_INVALID_ARG;
     int st = check_desc(d);
     if (st != PA_DECODE_OK)
         return st;
-    if (num_cus <= 0 || batch < 0 || batch > d.max_batch || max_context_len < 0 ||
-        max_context_len > d.max_context_len || partition_size < 0)
+    if (num_cus <= 0 || waves_per_cu <= 0 || batch < 0 || batch > d.max_batch ||
+        max_context_len < 0 || max_context_len > d.max_context_len || partition_size < 0)
         return PA_DECODE_INVALID_ARG;
     if (partition_size > 0 && partition_size % d.page_size != 0)
         return PA_DECODE_INVALID_ARG;
 
     const int ps = d.page_size;
     const int nb = pages_per_block(d.head_dim, d.dtype);
-    const int units = batch * d.num_kv_heads;
+    const int G = d.num_q_heads / d.num_kv_heads;
+    const int64_t units = int64_t(std::max(batch, 1)) * d.num_kv_heads;
     const bool windowed = sliding_window > 0 && sliding_window < max_context_len;
     const int64_t visible = windowed ? sliding_window : max_context_len;
     // Pages a visible range can touch (one more when the window edge is not
     // page aligned).
     const int64_t vis_pages = ceil_div(std::max<int64_t>(visible, 1), ps) + (windowed ? 1 : 0);
+    // Waves the grid aims for: about four per compute unit (one per SIMD),
+    // never more than the device holds at once.  Measured on MI355X, fewer
+    // waves with more pages each stream KV faster than more, shorter waves.
+    const int64_t capacity = int64_t(num_cus) * waves_per_cu;
+    const int64_t target = std::min<int64_t>(capacity, int64_t(num_cus) * 4);
 
     int64_t S;
-    int nw;
     if (partition_size > 0) {
         S = partition_size;
     } else {
-        // Aim for about 8 waves per compute unit over the whole grid, with at
-        // least one page per wave and at most 16 pages per wave.
-        const int64_t target_waves = int64_t(num_cus) * 8;
-        int64_t total_pages = int64_t(std::max(units, 1)) * vis_pages;
-        int64_t ppw = std::max<int64_t>(1, ceil_div(total_pages, target_waves));
-        ppw = std::min<int64_t>(ppw, 16);
+        // Pages per wave so that `target` waves cover the work, four waves
+        // sharing a partition; at least one page per wave and at most 64.
+        int64_t ppw = std::max<int64_t>(1, ceil_div(units * vis_pages, target));
+        ppw = std::min<int64_t>(ppw, 64);
         S = int64_t(kMaxWavesPerGroup) * ppw * ps;
     }
-    // A partition at least as long as any context: one partition, no merge.
     int64_t P;
     if (max_context_len == 0) {
         P = 1;
@@ -111,37 +114,65 @@ int make_plan(const pa_decode_desc& d, int num_cus, int batch, int max_context_l
         P = ceil_div(max_context_len, S);
     }
     P = std::max<int64_t>(P, 1);
-    if (P > 65535)
+    if (P > 65535 * int64_t(kMaxWavesPerGroup))
         return PA_DECODE_UNSUPPORTED;
     const bool split = P > 1;
     if (!split && partition_size == 0 && max_context_len > 0) {
         // The unsplit path covers the whole context with one workgroup.
         S = ceil_div(max_context_len, ps) * ps;
     }
-    // Waves per workgroup: enough blocks of `nb` pages for each wave.
-    int64_t blocks = ceil_div(ceil_div(std::min<int64_t>(S, std::max<int64_t>(visible, 1)), ps) +
-                                  (windowed ? 1 : 0), nb);
-    nw = int(std::max<int64_t>(1, std::min<int64_t>(kMaxWavesPerGroup, blocks)));
-    // Experiments only: PA_DECODE_WAVES overrides the waves per workgroup.
-    if (const char* env = std::getenv("PA_DECODE_WAVES")) {
-        const int v = std::atoi(env);
-        if (v >= 1 && v <= kMaxWavesPerGroup) nw = v;
-    }
-    // Keep the workgroup's combine buffer within 64 KiB of LDS.
+
+    // Waves per workgroup: four, fewer when the combine buffer would pass
+    // 64 KiB of LDS.
+    int nw = kMaxWavesPerGroup;
     {
-        const int G = template_group(d.num_q_heads / d.num_kv_heads);
-        const int gp4 = (G + 3) / 4 * 4;
-        const int64_t per_wave = int64_t(2 * gp4 + G * d.head_dim) * 4;
-        while (nw > 1 && nw * per_wave > 65536) --nw;
+        const int Gt = template_group(G);
+        const int gp4 = (Gt + 3) / 4 * 4;
+        const int64_t per_wave = int64_t(2 * gp4 + Gt * d.head_dim) * 4;
+        while (nw > 1 && nw * per_wave > 65536) nw /= 2;
     }
+    // Waves sharing one partition: the count (1, 2 or 4, at most one per
+    // block of the partition) whose grid total is closest to `target` and
+    // fits in one round of resident waves.
+    const int64_t blocks =
+        ceil_div(ceil_div(std::min<int64_t>(S, std::max<int64_t>(visible, 1)), ps) + (windowed ? 1 : 0), nb);
+    int wpp = 1;
+    {
+        int64_t best = -1;
+        for (int cand = 1; cand <= nw; cand *= 2) {
+            if (cand > 1 && (cand > blocks || units * P * cand > capacity)) break;
+            const int64_t dist = std::abs(units * P * cand - target);
+            if (best < 0 || dist < best) {
+                best = dist;
+                wpp = cand;
+            }
+        }
+    }
+    if (!split)
+        wpp = int(std::min<int64_t>(nw, std::max<int64_t>(1, blocks)));  // one partition: all waves on it
+    // Experiments only: PA_DECODE_WAVES_PER_PARTITION overrides the choice.
+    if (const char* env = std::getenv("PA_DECODE_WAVES_PER_PARTITION")) {
+        const int v = std::atoi(env);
+        if (v == 1 || v == 2 || v == 4) wpp = std::min(v, nw);
+    }
+    // A grid with fewer partitions than two per compute unit gets one
+    // partition per workgroup, so that its workgroups spread over the
+    // compute units instead of sharing a few.
+    if (!split || units * P < int64_t(num_cus) * 2)
+        nw = wpp;
+    const int slots = nw / wpp;
+    const int64_t gx = ceil_div(P, slots);
+    if (gx > 65535)
+        return PA_DECODE_UNSUPPORTED;
 
     pa_decode_plan p = {};
     p.split = split ? 1 : 0;
     p.partition_size = int32_t(S);
     p.num_partitions = int32_t(P);
     p.waves_per_group = nw;
+    p.waves_per_partition = wpp;
     p.pages_per_block = nb;
-    p.grid_partial[0] = int32_t(P);
+    p.grid_partial[0] = int32_t(gx);
     p.grid_partial[1] = d.num_kv_heads;
     p.grid_partial[2] = batch;
     p.block_partial = nw * 64;
@@ -153,6 +184,7 @@ int make_plan(const pa_decode_desc& d, int num_cus, int batch, int max_context_l
         p.workspace_bytes = int64_t(workspace_layout(d, batch, int(P)).total);
     }
     p.num_cus = num_cus;
+    p.waves_per_cu = waves_per_cu;
     *plan = p;
     return PA_DECODE_OK;
 }
@@ -162,7 +194,11 @@ size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan)
     const int G = template_group(d.num_q_heads / d.num_kv_heads);
     const int gp4 = (G + 3) / 4 * 4;
     const int nw = plan.waves_per_group;
-    const size_t loop = size_t(nw) * size_t(plan.pages_per_block * kPageSize * gp4 + gp4);
+    // q tile of the 16-bit head_dim-256 kernels: 8 chunks x 64 lanes x 16 B.
+    const int ks = d.head_dim * dtype_bytes(d.dtype) / 64;
+    const size_t qtile = ks >= 8 ? size_t(ks) * 64 * 4 : 0;
+    const size_t loop =
+        qtile + size_t(nw) * size_t(plan.pages_per_block * kPageSize * gp4 + gp4);
     const size_t comb = size_t(nw) * size_t(2 * gp4 + G * d.head_dim);
     return std::max(loop, comb) * sizeof(float);
 }

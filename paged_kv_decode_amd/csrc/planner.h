@@ -38,8 +38,11 @@ int template_group(int G);
 int check_desc(const pa_decode_desc& d);
 
 // Fills `plan` for the given call sizes; returns a PA_DECODE_* status.
-int make_plan(const pa_decode_desc& d, int num_cus, int batch, int max_context_len,
-              int sliding_window, int partition_size, pa_decode_plan* plan);
+// waves_per_cu: how many waves of the partial kernel one compute unit holds
+// at once (from the kernel's register and LDS use).
+int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
+              int max_context_len, int sliding_window, int partition_size,
+              pa_decode_plan* plan);
 
 // Dynamic LDS bytes of the partial kernel for a plan.
 size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan);

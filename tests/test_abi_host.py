@@ -69,12 +69,13 @@ def test_null_arguments_are_rejected():
     assert lib().pa_decode_destroy(None) == B.PA_DECODE_OK
 
 
-def plan(w: W.Workload, num_cus=256, batch=None, max_ctx=None, S=None, window=None):
+def plan(w: W.Workload, num_cus=256, batch=None, max_ctx=None, S=None, window=None,
+         waves_per_cu=8):
     d = B.make_desc(w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype, max_batch=4096,
                     max_context_len=1 << 20)
     lens = w.context_lens or [4096]
-    return B.pa_decode_plan_query(d, num_cus, batch or w.batch, max_ctx or max(lens),
-                                  w.window if window is None else window,
+    return B.pa_decode_plan_query(d, num_cus, waves_per_cu, batch or w.batch,
+                                  max_ctx or max(lens), w.window if window is None else window,
                                   w.partition_size if S is None else S)
 
 
@@ -102,9 +103,12 @@ def test_plan_covers_every_context(name):
                 if 0 <= n <= max_ctx:
                     assert covered(p, n, w.window), (name, max_ctx, S, n)
             assert p.split == (1 if p.num_partitions > 1 else 0)
-            assert p.grid_partial[0] == p.num_partitions
+            assert p.waves_per_partition in (1, 2, 4)
+            assert p.waves_per_group % p.waves_per_partition == 0
+            slots = p.waves_per_group // p.waves_per_partition
+            assert p.grid_partial[0] == -(-p.num_partitions // slots)
             assert p.grid_partial[1] == w.num_kv_heads
-            assert 64 <= p.block_partial <= 256 and p.block_partial % 64 == 0
+            assert 64 <= p.block_partial <= 256 and p.block_partial == 64 * p.waves_per_group
             if p.split:
                 assert list(p.grid_merge) == [w.num_q_heads, w.batch, w.head_dim // 64]
                 rows = w.batch * w.num_q_heads * p.num_partitions
@@ -116,6 +120,31 @@ def test_plan_covers_every_context(name):
 def test_forced_512_partitions_at_100k_give_196():
     p = plan(W.CONFIGS["ctx100k_gqa6_f16"])
     assert p.partition_size == 512 and p.num_partitions == 196 and p.split == 1
+
+
+@pytest.mark.parametrize("waves_per_cu", [4, 8, 12, 16])
+@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+def test_waves_per_partition_target_one_round(name, waves_per_cu):
+    """The waves sharing a partition bring the grid's wave count closest to
+    four per compute unit without exceeding what the device holds at once."""
+    w = W.CONFIGS[name]
+    p = plan(w, waves_per_cu=waves_per_cu)
+    if not p.split:
+        return
+    units = w.batch * w.num_kv_heads * p.num_partitions
+    capacity, target = 256 * waves_per_cu, min(256 * waves_per_cu, 256 * 4)
+    blocks = -(-(p.partition_size // 16 + (1 if w.window else 0)) // p.pages_per_block)
+    cands = [c for c in (1, 2, 4) if c == 1 or (c <= blocks and units * c <= capacity
+                                                and c <= p.waves_per_group)]
+    best = min(cands, key=lambda c: abs(units * c - target))
+    assert p.waves_per_partition == best
+    assert units * p.waves_per_partition <= max(capacity, units)
+
+
+def test_long_context_with_512_token_partitions_uses_one_wave_each():
+    p = plan(W.CONFIGS["ctx100k_gqa6_f16"], waves_per_cu=8)
+    assert p.waves_per_partition == 1 and p.waves_per_group == 4
+    assert p.grid_partial[0] == 49  # 196 partitions, 4 per workgroup
 
 
 def test_unsplit_when_one_partition_covers_the_context():
