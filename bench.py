@@ -245,6 +245,10 @@ def main():
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
+    ap.add_argument("--probe", choices=["copy"], default=None,
+                    help="calibration only: time a plain device copy of --probe-bytes "
+                         "(the reference kernel for the HBM traffic counters)")
+    ap.add_argument("--probe-bytes", type=int, default=256 << 20)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -256,6 +260,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.probe == "copy":
+        copy_probe(args.probe_bytes, args.steps, args.warmup)
+        return
     binding.load_library()
 
     engines = {}
@@ -327,6 +334,27 @@ def main():
         "also": also,
     }
     print(json.dumps(line), flush=True)
+
+
+def copy_probe(nbytes, steps, warmup):
+    """A plain copy of nbytes (read nbytes, write nbytes) repeated `steps` times."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    print(json.dumps({"probe": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                      "launches": steps + warmup, "us_per_copy": round(ms * 1e3, 2),
+                      "GBps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}),
+          flush=True)
 
 
 def p_lens(p):
