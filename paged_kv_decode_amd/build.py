@@ -29,6 +29,10 @@ FLAGS = [
     "-Wall",
     # Packed fp32 VALU ops stay off: the compiler emits plain fp32 ops.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the decode loop rescales them on the
+    # vector ALUs, which cannot touch AGPRs (AGPR accumulators cost two moves
+    # per element per rescale).
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"),
     "-I" + os.path.join(HERE, "csrc"),
 ]

@@ -2,20 +2,23 @@
 //
 // Partial kernel: one workgroup of NW wave64s per (partition, KV head,
 // sequence).  The partition's pages are dealt to the waves in blocks of NB
-// pages.  For each block a wave
-//   1. reads the block's page ids from the page table (uniform, scalar loads)
-//      and issues 16-byte loads of every K and V row chunk of those pages;
-//   2. forms the scores of all G query heads of the group against the
-//      block's 16-token pages with one MFMA chain per page: the G query rows
-//      (zero-padded to 16) are the A operand, the page's 16 key rows the B
+// pages (8 KiB of K and 8 KiB of V per block).  For each block a wave
+//   1. reads the block's page ids from a page-id vector (one scalar readlane
+//      per page) and issues 16-byte loads of whole 128-byte lines of every K
+//      and V row of those pages;
+//   2. copies the rows into per-wave LDS tiles (row-swizzled) as soon as they
+//      land, and requests the next block's rows into the freed registers;
+//   3. forms the scores of all G query heads of the group against each
+//      16-token page with one MFMA chain: the page's key rows (from the K
+//      tile) are the A operand, the G query rows (zero-padded to 16) the B
 //      operand, head_dim the reduction axis, so each K byte is read once per
-//      group and the 16-lane result rows line up with the tokens;
-//   3. updates the per-head online-softmax state (running max, denominator)
-//      with 16-lane DPP reductions, and publishes the block's probabilities
-//      through a small per-wave LDS buffer;
-//   4. accumulates P.V on the vector ALUs: each lane owns one 16-byte chunk
-//      of head_dim for 64/CH token rows and all G heads, so each V byte is
-//      also read once per group and converted to f32 once.
+//      group;
+//   4. updates the per-head online-softmax state (running max, denominator):
+//      each lane holds one head and four tokens, so the block maximum is an
+//      in-lane max plus two cross-lane steps;
+//   5. accumulates P.V on the matrix cores: the probabilities are already in
+//      the A-operand layout, V comes from the V tile through the LDS
+//      transpose read, and the output block sits in VGPRs.
 // The waves' states are then combined in LDS (running max first, then the
 // rescaled denominators and outputs) and the workgroup writes either the
 // partition state (o normalised, max, denominator) for the merge kernel or,
@@ -48,6 +51,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kPage = 16;
@@ -113,23 +119,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // software pipeline); emits no instruction.
 __device__ __forceinline__ void pin_loads() { asm volatile("" ::: "memory"); }
 
-// ---- element conversion of one 16-byte chunk ----
+// ---- score MFMA over one 16-byte chunk of head_dim ----
 template <int DT> struct Chunk;
 
 template <> struct Chunk<PA_DTYPE_F16> {
-    __device__ static void to_f32(u32x4 r, float* f)
-    {
-        f16x8 h = __builtin_bit_cast(f16x8, r);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = (float)h[e];
-    }
-    // acc[e] += p * x[e]; the f16 -> f32 widening folds into v_fma_mix_f32.
-    __device__ static void fma_into(float p, u32x4 r, float* acc)
-    {
-        f16x8 h = __builtin_bit_cast(f16x8, r);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(p, (float)h[e], acc[e]);
-    }
     __device__ static f32x4 mfma(u32x4 a, u32x4 b, f32x4 c)
     {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
@@ -138,40 +131,14 @@ template <> struct Chunk<PA_DTYPE_F16> {
 };
 
 template <> struct Chunk<PA_DTYPE_BF16> {
-    __device__ static void to_f32(u32x4 r, float* f)
-    {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            f[2 * e] = __uint_as_float(r[e] << 16);
-            f[2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
-        }
-    }
     __device__ static f32x4 mfma(u32x4 a, u32x4 b, f32x4 c)
     {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     }
-    __device__ static void fma_into(float p, u32x4 r, float* acc)
-    {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc[2 * e] = __builtin_fmaf(p, __uint_as_float(r[e] << 16), acc[2 * e]);
-            acc[2 * e + 1] = __builtin_fmaf(p, __uint_as_float(r[e] & 0xffff0000u), acc[2 * e + 1]);
-        }
-    }
 };
 
 template <> struct Chunk<PA_DTYPE_F32> {
-    __device__ static void to_f32(u32x4 r, float* f)
-    {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(r[e]);
-    }
-    __device__ static void fma_into(float p, u32x4 r, float* acc)
-    {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(p, __uint_as_float(r[e]), acc[e]);
-    }
     __device__ static f32x4 mfma(u32x4 a, u32x4 b, f32x4 c)
     {
         // Four K=4 steps, one per float of the chunk (same k slot in A and B).
@@ -208,6 +175,35 @@ __device__ __forceinline__ u32x4 load16_stream(const void* p)
 }
 
 
+// ---- P.V on the matrix cores ----
+// One 16x16 output block (16 query-head rows x 16 head_dim columns) gains
+// p[head][token] * V[token][column] over the 16 tokens of a page.  Lane l
+// holds p of head l % 16 for tokens 4*(l/16) + j (the score MFMA leaves them
+// there) and reads V[tokens 4*(l/16) + j][column l % 16] from the LDS tile.
+template <int DT> struct PV;
+
+template <> struct PV<PA_DTYPE_F16> {
+    __device__ static f32x4 mma(const float p[4], s16x4 v, f32x4 c)
+    {
+        const f16x4 a = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, __builtin_bit_cast(f16x4, v), c, 0, 0, 0);
+    }
+};
+
+template <> struct PV<PA_DTYPE_BF16> {
+    // p = hi + lo in two bf16 parts (16 significant bits): one bf16 part alone
+    // would leave a relative error near 2^-9 in every probability.
+    __device__ static f32x4 mma(const float p[4], s16x4 v, f32x4 c)
+    {
+        const bf16x4 hi = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+        const bf16x4 lo = {(__bf16)(p[0] - (float)hi[0]), (__bf16)(p[1] - (float)hi[1]),
+                           (__bf16)(p[2] - (float)hi[2]), (__bf16)(p[3] - (float)hi[3])};
+        const bf16x4 vb = __builtin_bit_cast(bf16x4, v);
+        c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hi, vb, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lo, vb, c, 0, 0, 0);
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Partial kernel.
 //   DT: element type; D: head_dim; G: instantiated group size (>= actual);
@@ -216,13 +212,24 @@ __device__ __forceinline__ u32x4 load16_stream(const void* p)
 // prm.waves_per_partition waves; slot j of workgroup x handles partition
 // x * slots + j of KV head blockIdx.y of sequence blockIdx.z.
 // Lane maps (lane = 0..63, i16 = lane % 16, grp = lane / 16):
-//   K / MFMA:  lane loads chunk 4*ks + grp of key row i16 of a page,
-//              ks = 0..KS-1; the MFMA result element r of the lane is the score
-//              of query head 4*grp + r against token i16.
-//   V / P.V:   lane owns chunk c = lane % CH of token rows rho = lane / CH,
-//              rho + R, ..., rho + R*(KS-1) of a page.
-// LDS: [q tile (head_dim 256 only)][per-wave p / alpha buffers]; after the
-// main loop the whole area is reused for the combine of the slot's waves.
+//   loads:   K and V alike: lane loads chunk c = lane % CH of token rows
+//            rho = lane / CH, rho + R, ..., rho + R*(KS-1) of a page, so each
+//            load instruction reads whole 128-byte lines; the rows go to
+//            per-wave LDS tiles (16-byte chunks XOR-swizzled by row so that
+//            the reads below are bank-conflict free);
+//   scores:  MFMA with the page's 16 key rows as A and the G query rows
+//            (zero-padded to 16) as B, head_dim the reduction axis: lane reads
+//            chunk 4*ks + grp of key row i16 and of query row i16; result
+//            element r of the lane is the score of query head i16 against
+//            token 4*grp + r, so each K byte is read once per group;
+//   P.V:     MFMA with those probabilities as A (no data movement) and V as
+//            B, read from the V tile with the LDS transpose read; output
+//            element r of the lane is head 4*grp + r, column 16*db + i16.
+// The MFMA operand layout read straight from memory would fetch 16 rows x 64
+// bytes per instruction: twice the L1 tag lookups of whole lines, and with
+// non-temporal loads two L2 requests per line.
+// LDS: [q tile (head_dim 256 only)][per wave: K tile, V tile]; after the main
+// loop the whole area is reused for the combine of the slot's waves.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int G, int NB>
 __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
@@ -231,13 +238,16 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     constexpr int CH = D * EB / 16;   // 16-byte chunks per key row
     constexpr int EPC = 16 / EB;      // elements per chunk
     constexpr int KS = CH / 4;        // chunks per lane per page (K and V alike)
-    constexpr int R = kWave / CH;     // token rows of the P.V map
+    constexpr int R = kWave / CH;     // token rows per load instruction
+    constexpr int NDB = D / 16;       // 16-column blocks of the output
     constexpr int GP4 = (G + 3) / 4 * 4;
-    constexpr int HG = (G + 3) / 4;   // 16-lane groups that carry real heads
     constexpr int IPV = kWave / NB;   // loop iterations one page-id vector covers
     constexpr bool QLDS = KS >= 8;    // q operand read from LDS (saves 4*KS VGPRs)
     constexpr int QTILE = QLDS ? KS * kWave * 4 : 0;  // floats
+    constexpr int KT = NB * kPage * CH;  // 16-byte chunks of one block's K (or V) tile
     static_assert(KS * 4 == CH && R * CH == kWave && R * KS == kPage, "lane map");
+    static_assert(KT == 8 * kWave && (CH == 8 || CH == 16 || CH == 32), "tiles");
+    static_assert(G <= 16, "one 16-row MFMA block of query heads");
 
     extern __shared__ __attribute__((aligned(16))) float smem[];
     const int lane = threadIdx.x & (kWave - 1);
@@ -271,7 +281,7 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         ids = load_ids(pgs, min(pgs + S / kPage, prm.pt_stride), 0);
     }
 
-    // q as the MFMA A operand: row i16 = query head kvh*G + i16 (zero past G).
+    // q as the MFMA B operand: column i16 = query head kvh*G + i16 (zero past G).
     u32x4 qa[QLDS ? 1 : KS];
     {
         const bool real = i16 < Gact;
@@ -310,184 +320,205 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         ids = load_ids(pg0, pg1, 0);
 
     const int64_t ss = prm.stride_slot;
-    const int64_t k_lane_off = int64_t(i16) * ss + int64_t(grp) * EPC;
-    const int64_t v_lane_off = int64_t(rho) * ss + int64_t(c) * EPC;
+    const int64_t lane_off = int64_t(rho) * ss + int64_t(c) * EPC;
     const char* kbase = static_cast<const char*>(prm.k) + int64_t(kvh) * prm.stride_head * EB;
     const char* vbase = static_cast<const char*>(prm.v) + int64_t(kvh) * prm.stride_head * EB;
 
-    float m_run[4], l_run[4];
+    // Online-softmax state of head i16 (the same in the four lane groups;
+    // the denominator holds the lane's own tokens until the end).
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[NDB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        m_run[r] = -INFINITY;
-        l_run[r] = 0.f;
-    }
-    float acc[G][EPC];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[g][e] = 0.f;
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    float* pbuf = smem + QTILE + wave * (NB * kPage * GP4 + GP4);
-    float* abuf = pbuf + NB * kPage * GP4;
+    u32x4* ktile = reinterpret_cast<u32x4*>(smem + QTILE + wave * 8 * KT);
+    u32x4* vtile = ktile + KT;
+    // Tile layout (K and V alike): chunk j of tile row r (page r / 16, token
+    // r % 16) sits at r * CH + (j ^ swz(r)); swz permutes within aligned
+    // groups of 8 chunks, so a 128-byte line still lands whole, and the 16
+    // rows one read touches fall in distinct 16-byte bank groups.
+    auto swz = [](int r) { return CH >= 16 ? (r & 15) : ((r >> 1) & 7); };
+    const int kswz = swz(i16);
 
     const int nblk = active ? (pg1 - pg0 + NB - 1) / NB : 0;
     const int nit = nblk > wi ? (nblk - wi + wpp - 1) / wpp : 0;
     if constexpr (QLDS) __syncthreads();   // q tile written
 
-    // Software pipeline over the wave's blocks: block it+1's K is requested as
-    // soon as block it's scores are formed (the K registers are free again),
-    // and block it+1's V as soon as block it's P.V is done, so one of the two
-    // is always in flight while the other is used.  Every phase issues exactly
-    // NB*KS loads (pages missing from a short block re-read the block's last
-    // page; the last iteration re-reads its own block) so that the wait for K
-    // can leave V in flight and vice versa.
+    // Software pipeline over the wave's blocks: as soon as block it's K and V
+    // rows are in the LDS tiles, the registers take block it+1's loads, so the
+    // loads of one block are in flight while the previous block is computed.
+    // Every phase issues exactly 2*NB*KS loads, with no branch around them, so
+    // that each wait leaves the younger loads in flight: a page past the
+    // wave's last block (or past the end of a short block) gets a zero lane
+    // offset, i.e. all lanes read one 16-byte piece of a page.
     u32x4 kr[NB][KS], vr[NB][KS];
     int64_t page[NB];
-    auto fetch_ids = [&](int it, int it0) {
-        // Page ids of block `it` into scalar registers (ids holds the blocks
+    uint32_t pmask[NB];
+    const uint32_t lane_off32 = uint32_t(lane_off * EB);
+    auto fetch_ids = [&](int itn, int it0, int it1) {
+        // Page ids of block `itn` into scalar registers (ids holds the blocks
         // it0 .. it0 + IPV - 1).
-        const int nbv_ = min(NB, pg1 - (pg0 + (wi + wpp * it) * NB));
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            page[nb] = __builtin_amdgcn_readlane(ids, (it - it0) * NB + min(nb, nbv_ - 1));
-    };
-    auto issue_k = [&]() {
+        const int itc = min(itn, it1 - 1);
+        const int nbv_ = itn < it1 ? min(NB, pg1 - (pg0 + (wi + wpp * itn) * NB)) : 0;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const char* kp = kbase + page[nb] * prm.stride_page * EB;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kr[nb][ks] = load16_stream(kp + (k_lane_off + int64_t(4 * ks) * EPC) * EB);
+            page[nb] = __builtin_amdgcn_readlane(ids, (itc - it0) * NB + nb);
+            uint32_t m = __builtin_amdgcn_readfirstlane(nb < nbv_ ? ~0u : 0u);
+            asm volatile("" : "+s"(m));  // an opaque mask, not a branch condition
+            pmask[nb] = m;
         }
     };
-    auto issue_v = [&]() {
+    auto issue = [&](const char* base, u32x4 (&r)[NB][KS]) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const char* vp = vbase + page[nb] * prm.stride_page * EB;
+            const char* pb = base + page[nb] * prm.stride_page * EB;
 #pragma unroll
             for (int i = 0; i < KS; ++i)
-                vr[nb][i] = load16_stream(vp + (v_lane_off + int64_t(R * i) * ss) * EB);
+                r[nb][i] = load16_stream(pb + ((lane_off32 + uint32_t(R * i * ss * EB)) & pmask[nb]));
         }
+    };
+    // Registers -> swizzled tile; V rows of tokens outside [t0, t1) (or of
+    // pages past the block's end) become zero, so that slots the method must
+    // not read never reach the output (their probabilities are already 0).
+    auto stage = [&](u32x4* tile, const u32x4 (&r)[NB][KS], bool zero_invalid, int pgb, int nbv) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < KS; ++i) {
+                const int row = nb * kPage + R * i + rho;
+                u32x4 x = r[nb][i];
+                if (zero_invalid) {
+                    const int tok = (pgb + nb) * kPage + R * i + rho;
+                    const u32x4 z = {0u, 0u, 0u, 0u};
+                    x = (nb < nbv && tok >= t0 && tok < t1) ? x : z;
+                }
+                tile[row * CH + (c ^ swz(row))] = x;
+            }
     };
 
     // Outer loop over chunks of IPV blocks (one page-id vector each); the
     // pipelined inner loop itself issues no load but K/V.
     for (int it0 = 0; it0 < nit; it0 += IPV) {
-    const int it1 = min(nit, it0 + IPV);
-    if (it0 > 0)
-        ids = load_ids(pg0, pg1, it0);
-    fetch_ids(it0, it0);
-    issue_k();
-    issue_v();
-    pin_loads();
-
-    for (int it = it0; it < it1; ++it) {
-        const int pgb = pg0 + (wi + wpp * it) * NB;
-        const int nbv = min(NB, pg1 - pgb);
-
-        // Scores (base 2) of head 4*grp + r against token i16 of each page.
-        float s[NB][4];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) d = Chunk<DT>::mfma(q_operand(ks), kr[nb][ks], d);
-            const int tok = (pgb + nb) * kPage + i16;
-            const bool ok = nb < nbv && tok >= t0 && tok < t1;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s[nb][r] = ok ? d[r] * prm.scale_log2 : -INFINITY;
-        }
-        fetch_ids(min(it + 1, it1 - 1), it0);
-        issue_k();
+        const int it1 = min(nit, it0 + IPV);
+        if (it0 > 0)
+            ids = load_ids(pg0, pg1, it0);
+        fetch_ids(it0, it0, it1);
+        issue(kbase, kr);
+        pin_loads();
+        issue(vbase, vr);
         pin_loads();
 
-        float alpha[4];
-        bool rescale = false;
+        for (int it = it0; it < it1; ++it) {
+            const int pgb = pg0 + (wi + wpp * it) * NB;
+            const int nbv = min(NB, pg1 - pgb);
+            // Edge blocks only (partition or window ends, short blocks) need
+            // the V mask (wave-uniform).
+            const bool edge = nbv < NB || pgb * kPage < t0 || (pgb + NB) * kPage > t1;
+
+            stage(ktile, kr, false, pgb, nbv);
+            if (edge)
+                stage(vtile, vr, true, pgb, nbv);
+            else
+                stage(vtile, vr, false, pgb, nbv);
+            wave_lds_sync();
+            fetch_ids(it + 1, it0, it1);
+            issue(kbase, kr);
+            pin_loads();
+            issue(vbase, vr);
+            pin_loads();
+
+            // Scores (base 2) of head i16 against token 4*grp + r of each page.
+            float s[NB][4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float bm = s[0][r];
+            for (int nb = 0; nb < NB; ++nb) {
+                f32x4 d = {0.f, 0.f, 0.f, 0.f};
+                const u32x4* krow = ktile + (nb * kPage + i16) * CH;
 #pragma unroll
-            for (int nb = 1; nb < NB; ++nb) bm = fmaxf(bm, s[nb][r]);
-            bm = row16_max(bm);
-            const float mnew = fmaxf(m_run[r], bm);
-            alpha[r] = fast_exp2(m_run[r] - mnew);
-            rescale |= mnew != m_run[r];
+                for (int ks = 0; ks < KS; ++ks)
+                    d = Chunk<DT>::mfma(krow[(4 * ks + grp) ^ kswz], q_operand(ks), d);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tok = (pgb + nb) * kPage + 4 * grp + r;
+                    const bool ok = nb < nbv && tok >= t0 && tok < t1;
+                    s[nb][r] = ok ? d[r] * prm.scale_log2 : -INFINITY;
+                }
+            }
+
+            // Block maximum of head i16: the lane's own 4*NB scores, then the
+            // four lane groups (xor 16 by ds_swizzle, xor 32 by ds_bpermute).
+            float bm = s[0][0];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bm = fmaxf(bm, s[nb][r]);
+            bm = fmaxf(bm, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(bm), 0x401F)));
+            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            const float mnew = fmaxf(m_run, bm);
+            const float alpha = fast_exp2(m_run - mnew);
+            // The output accumulators need rescaling only when some head's
+            // running maximum moved (wave-uniform decision).
+            const bool any_rescale = __any(mnew != m_run && i16 < G);
             float ps = 0.f;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                s[nb][r] = fast_exp2(s[nb][r] - mnew);
-                ps += s[nb][r];
-            }
-            l_run[r] = alpha[r] * l_run[r] + ps;
-            m_run[r] = mnew;
-        }
-        // The output accumulators need rescaling only when some head's
-        // running maximum moved (wave-uniform decision).
-        const bool any_rescale = __any(rescale && grp < HG);
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    s[nb][r] = fast_exp2(s[nb][r] - mnew);
+                    ps += s[nb][r];
+                }
+            l_run = alpha * l_run + ps;
+            m_run = mnew;
 
-        // Publish p[page][token][head] and alpha[head] for the P.V lane map.
-        if (grp < HG) {
+            if (any_rescale) {
+                // Row 4*grp + r of the output blocks is head 4*grp + r, whose
+                // alpha sits in lane 4*grp + r.
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float a = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) acc[db][r] *= a;
+                }
+            }
+
+            // P.V: V rows 4*grp + i16/4 of each page, columns 16*db +
+            // 4*(i16%4) .. +3 for the transpose read.
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                f32x4 pv = {s[nb][0], s[nb][1], s[nb][2], s[nb][3]};
-                *reinterpret_cast<f32x4*>(pbuf + (nb * kPage + i16) * GP4 + 4 * grp) = pv;
-            }
-            if (i16 == 0 && any_rescale) {
-                f32x4 av = {alpha[0], alpha[1], alpha[2], alpha[3]};
-                *reinterpret_cast<f32x4*>(abuf + 4 * grp) = av;
-            }
-        }
-        wave_lds_sync();
-
-        if (any_rescale) {
+                const int vrow = nb * kPage + 4 * grp + (i16 >> 2);
+                const char* vrow_p = reinterpret_cast<const char*>(vtile + vrow * CH);
+                const int vsw = swz(vrow);
+                if constexpr (DT == PA_DTYPE_F32) {
+                    // 16x16x4 f32 steps: step r takes token 4*grp + r of
+                    // every lane group (k index grp).
 #pragma unroll
-            for (int g4 = 0; g4 < GP4; g4 += 4) {
-                const f32x4 a4 = *reinterpret_cast<const f32x4*>(abuf + g4);
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = nb * kPage + 4 * grp + r;
+                        const float* vr_p = reinterpret_cast<const float*>(vtile + row * CH);
+                        const int rsw = swz(row);
 #pragma unroll
-                for (int g = g4; g < g4 + 4 && g < G; ++g)
+                        for (int db = 0; db < NDB; ++db) {
+                            const int col = 16 * db + i16;
+                            const float v = vr_p[((col >> 2) ^ rsw) * 4 + (col & 3)];
+                            acc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(s[nb][r], v, acc[db], 0, 0, 0);
+                        }
+                    }
+                } else {
 #pragma unroll
-                    for (int e = 0; e < EPC; ++e) acc[g][e] *= a4[g - g4];
-            }
-        }
-        // P.V: every lane adds p[head][token] * V[token][its chunk] for its
-        // token rows; a token outside [t0, t1) (edge pages only) gets a
-        // zeroed V chunk (its p is already 0), so unread slots never reach acc.
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            if (nb < nbv) {
-                const int pgtok = (pgb + nb) * kPage;
-#pragma unroll
-                for (int i = 0; i < KS; ++i) {
-                    const int t = rho + R * i;
-                    const int tok = pgtok + t;
-                    u32x4 raw = vr[nb][i];
-                    u32x4 z = {0u, 0u, 0u, 0u};
-                    raw = (tok >= t0 && tok < t1) ? raw : z;
-                    const float* prow = pbuf + (nb * kPage + t) * GP4;
-#pragma unroll
-                    for (int g4 = 0; g4 < GP4; g4 += 4) {
-                        const f32x4 p4 = *reinterpret_cast<const f32x4*>(prow + g4);
-#pragma unroll
-                        for (int g = g4; g < g4 + 4 && g < G; ++g)
-                            Chunk<DT>::fma_into(p4[g - g4], raw, acc[g]);
+                    for (int db = 0; db < NDB; ++db) {
+                        const int j = 2 * db + ((i16 & 3) >> 1);
+                        const char* addr = vrow_p + (j ^ vsw) * 16 + (i16 & 1) * 8;
+                        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4*)(addr));
+                        acc[db] = PV<DT>::mma(s[nb], v, acc[db]);
                     }
                 }
             }
         }
-        wave_lds_sync();
-        issue_v();
-        pin_loads();
-    }
     }  // chunks of IPV blocks
 
-    // Wave-level reductions: denominators over the 16 token lanes, outputs
-    // over the R token rows (lanes c, c + CH, ...).
-#pragma unroll
-    for (int r = 0; r < 4; ++r) l_run[r] = row16_sum(l_run[r]);
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[g][e] = sum_rows<CH>(acc[g][e]);
+    // Denominator of head i16 over the four lane groups.
+    l_run += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(l_run), 0x401F));
+    l_run += __shfl_xor(l_run, 32);
 
     // Combine the waves of each partition slot in LDS: maximum first, then
     // the rescaled denominators and outputs.  A wave without blocks holds
@@ -497,18 +528,17 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     float* cm = smem;               // [nw][GP4]
     float* cl = cm + nw * GP4;      // [nw][GP4]
     float* ca = cl + nw * GP4;      // [nw][G][D]
-    if (i16 == 0 && grp < HG) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            cm[wave * GP4 + 4 * grp + r] = m_run[r];
-            cl[wave * GP4 + 4 * grp + r] = l_run[r];
-        }
+    if (grp == 0 && i16 < G) {
+        cm[wave * GP4 + i16] = m_run;
+        cl[wave * GP4 + i16] = l_run;
     }
-    if (rho == 0) {
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+    for (int r = 0; r < 4; ++r) {
+        const int g = 4 * grp + r;
+        if (g < G) {
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) ca[(wave * G + g) * D + c * EPC + e] = acc[g][e];
+            for (int db = 0; db < NDB; ++db) ca[(wave * G + g) * D + 16 * db + i16] = acc[db][r];
+        }
     }
     __syncthreads();
 

@@ -160,6 +160,11 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
     // compute units instead of sharing a few.
     if (!split || units * P < int64_t(num_cus) * 2)
         nw = wpp;
+    // Experiments only: PA_DECODE_WAVES_PER_GROUP overrides the workgroup size.
+    if (const char* env = std::getenv("PA_DECODE_WAVES_PER_GROUP")) {
+        const int v = std::atoi(env);
+        if ((v == 1 || v == 2 || v == 4) && v >= wpp) nw = v;
+    }
     const int slots = nw / wpp;
     const int64_t gx = ceil_div(P, slots);
     if (gx > 65535)
@@ -197,8 +202,10 @@ size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan)
     // q tile of the 16-bit head_dim-256 kernels: 8 chunks x 64 lanes x 16 B.
     const int ks = d.head_dim * dtype_bytes(d.dtype) / 64;
     const size_t qtile = ks >= 8 ? size_t(ks) * 64 * 4 : 0;
-    const size_t loop =
-        qtile + size_t(nw) * size_t(plan.pages_per_block * kPageSize * gp4 + gp4);
+    // per wave: the block's K and V tiles (8 KiB each)
+    const size_t ktile = size_t(plan.pages_per_block) * kPageSize * d.head_dim *
+                         dtype_bytes(d.dtype) / sizeof(float);
+    const size_t loop = qtile + size_t(nw) * 2 * ktile;
     const size_t comb = size_t(nw) * size_t(2 * gp4 + G * d.head_dim);
     return std::max(loop, comb) * sizeof(float);
 }
