@@ -249,7 +249,18 @@ def main():
                     help="calibration only: time a plain device copy of --probe-bytes "
                          "(the reference kernel for the HBM traffic counters)")
     ap.add_argument("--probe-bytes", type=int, default=256 << 20)
+    ap.add_argument("--profile-commands", metavar="DIR", default=None,
+                    help="print the rocprofv3 commands whose output --summarize-profiles reads")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="write profiles/*.md and profiles/traffic.json from that output")
     args = ap.parse_args()
+
+    if args.profile_commands:
+        print("\n".join("%s\t%s" % nc for nc in profile_commands(args.profile_commands)))
+        return
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this decode-attention path runs on a single "
@@ -355,6 +366,151 @@ def copy_probe(nbytes, steps, warmup):
                       "launches": steps + warmup, "us_per_copy": round(ms * 1e3, 2),
                       "GBps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}),
           flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Profiling evidence: the rocprofv3 runs behind profiles/ and their summary.
+# ---------------------------------------------------------------------------
+PROFILED = ["llama1b_ctx3060_f16", "llama8b_b16_ragged_f16", "d256_window4096_bf16",
+            "ctx100k_gqa6_f16"]
+COPY_BYTES = 256 << 20
+
+
+def profile_commands(outdir):
+    """(name, command) of every run behind profiles/: per workload a plain
+    benchmark run (its stdout goes to <outdir>/<name>.log) and a kernel trace,
+    then the FETCH_SIZE and WRITE_SIZE passes and their copy calibration.
+    The rocprofv3 commands run from /tmp with TMPDIR=/tmp."""
+    b = "/root/repo/bench.py"
+    cmds = []
+    for w in PROFILED:
+        steps = 2000 if w == "llama1b_ctx3060_f16" else 300
+        run = "python3 %s --workload %s --also '' --cpu-budget 0 --steps %d --warmup 20" % (b, w, steps)
+        cmds.append(("bench_%s" % w, run))
+        cmds.append(("trace_%s" % w, "rocprofv3 --kernel-trace --stats --output-format csv -d %s/trace_%s "
+                                     "-o %s -- %s" % (outdir, w, w, run)))
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        for w in PROFILED:
+            cmds.append(("pmc_%s_%s" % (w, c),
+                         "rocprofv3 --pmc %s --output-format csv -d %s/pmc_%s_%s -o %s -- python3 %s "
+                         "--workload %s --also '' --cpu-budget 0 --steps 20 --warmup 2 --mode eager"
+                         % (c, outdir, w, c, w, b, w)))
+        cmds.append(("pmc_copy_%s" % c,
+                     "rocprofv3 --pmc %s --output-format csv -d %s/pmc_copy_%s -o copy -- python3 %s "
+                     "--probe copy --probe-bytes %d --steps 10 --warmup 2" % (c, outdir, c, b, COPY_BYTES)))
+    return cmds
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name):
+    for k in ("partial_kernel", "merge_kernel", "copyBuffer"):
+        if k in name:
+            return k
+    return None
+
+
+def summarize_profiles(indir):
+    """Writes profiles/<kernel>_<workload>.md and profiles/traffic.json from the
+    output of profile_commands(indir)."""
+    import statistics
+    prof = os.path.join(ROOT, "profiles")
+    counters = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = _csv_rows(os.path.join(indir, "pmc_copy_%s" % c, "copy_counter_collection.csv"))
+        vals = [float(r["Counter_Value"]) for r in rows if _short(r["Kernel_Name"]) == "copyBuffer"
+                and r["Counter_Name"] == c]
+        counters[c] = statistics.median(vals)
+    fetch_scale = COPY_BYTES / 1024.0 / counters["FETCH_SIZE"]
+    write_scale = COPY_BYTES / 1024.0 / counters["WRITE_SIZE"]
+    named = dict(profile_commands(indir))
+    traffic = {"kernel_hash": kernel_hash(), "kernel_sources": KERNEL_SOURCES,
+               "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+               "calibration": "plain %d KiB device copy (__amd_rocclr_copyBuffer): FETCH_SIZE "
+                              "%.1f KiB, WRITE_SIZE %.1f KiB per dispatch for %d KiB read and written"
+                              % (COPY_BYTES >> 10, counters["FETCH_SIZE"], counters["WRITE_SIZE"],
+                                 COPY_BYTES >> 10),
+               "commands": [c for n, c in named.items() if n.startswith("pmc_")],
+               "workloads": {}}
+    for w in PROFILED:
+        p = W.generate(W.CONFIGS[w])
+        kv = p.kv_bytes()
+        stats = {_short(r["Name"]): r for r in
+                 _csv_rows(os.path.join(indir, "trace_%s" % w, "%s_kernel_stats.csv" % w))}
+        line = None
+        logp = os.path.join(indir, "bench_%s.log" % w)
+        if os.path.exists(logp):
+            for ln in open(logp):
+                if ln.startswith("{"):
+                    line = json.loads(ln)
+        pmc = {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            rows = _csv_rows(os.path.join(indir, "pmc_%s_%s" % (w, c), "%s_counter_collection.csv" % w))
+            for k in ("partial_kernel", "merge_kernel"):
+                v = [float(r["Counter_Value"]) for r in rows
+                     if _short(r["Kernel_Name"]) == k and r["Counter_Name"] == c]
+                if v:
+                    pmc[(k, c)] = statistics.median(v)
+        fb = int(round(pmc[("partial_kernel", "FETCH_SIZE")] * 1024 * fetch_scale))
+        wb = int(round(pmc[("partial_kernel", "WRITE_SIZE")] * 1024 * write_scale))
+        e = {"kernel": "partial_kernel", "fetch_bytes": fb, "write_bytes": wb,
+             "bytes_per_launch": fb + wb, "algorithmic_kv_bytes": kv,
+             "fetch_over_algorithmic": round(fb / kv, 4)}
+        if ("merge_kernel", "FETCH_SIZE") in pmc:
+            e["merge_kernel_fetch_bytes"] = int(round(pmc[("merge_kernel", "FETCH_SIZE")] * 1024 * fetch_scale))
+            e["merge_kernel_write_bytes"] = int(round(pmc[("merge_kernel", "WRITE_SIZE")] * 1024 * write_scale))
+        traffic["workloads"][w] = e
+
+        part = stats["partial_kernel"]
+        avg_us = float(part["AverageNs"]) / 1e3
+        out = ["# %s -- partial and merge kernels on MI355X (gfx950)" % w, "",
+               "Kernel trace (rocprofv3 --kernel-trace --stats), run from /tmp with TMPDIR=/tmp:",
+               "  " + named["trace_%s" % w], "",
+               "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for k in ("partial_kernel", "merge_kernel"):
+            if k in stats:
+                r = stats[k]
+                out.append("| %s | %s | %.3f | %.3f | %.3f |" % (
+                    r["Name"].replace("void pa::(anonymous namespace)::", ""), r["Calls"],
+                    float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+        out += ["", "Algorithmic KV bytes per launch: %d; at the trace's average partial-kernel "
+                    "duration that is %.1f GB/s (%.1f%% of 8 TB/s)." % (kv, kv / avg_us / 1e3,
+                                                                        kv / avg_us / 1e3 / PEAK_GBPS * 100)]
+        if line:
+            ro = line["roofline"]
+            out += ["", "The same benchmark without the profiler (HIP events around each launch):",
+                    "  " + named["bench_%s" % w],
+                    "gives partial %.3f us (%.1f GB/s, %.1f%% of peak), merge %.3f us, %.2f us per "
+                    "graph-replayed step, %.1f GB/s per step." % (
+                        ro["kernel_us"], ro["achieved"], 100 * ro["frac"], ro["merge_us"],
+                        line["us_per_step"], line["value"])]
+        out += ["", "HBM traffic per dispatch (rocprofv3 --pmc, one counter per run, median over "
+                    "dispatches), C = FETCH_SIZE, then WRITE_SIZE:",
+                "  " + named["pmc_%s_FETCH_SIZE" % w].replace("FETCH_SIZE", "{C}"),
+                "calibration:",
+                "  " + named["pmc_copy_FETCH_SIZE"].replace("FETCH_SIZE", "{C}"),
+                "  copy of %d KiB: FETCH_SIZE reads %.1f KiB (scale %.4f), WRITE_SIZE reads %.1f KiB "
+                "(scale %.4f)" % (COPY_BYTES >> 10, counters["FETCH_SIZE"], fetch_scale,
+                                   counters["WRITE_SIZE"], write_scale), "",
+                "| kernel | FETCH_SIZE KiB (raw) | fetched bytes (scaled) | WRITE_SIZE KiB | written bytes |",
+                "|---|---|---|---|---|"]
+        for k in ("partial_kernel", "merge_kernel"):
+            if (k, "FETCH_SIZE") in pmc:
+                out.append("| %s | %.1f | %d | %.1f | %d |" % (
+                    k, pmc[(k, "FETCH_SIZE")], round(pmc[(k, "FETCH_SIZE")] * 1024 * fetch_scale),
+                    pmc[(k, "WRITE_SIZE")], round(pmc[(k, "WRITE_SIZE")] * 1024 * write_scale)))
+        out += ["", "partial kernel fetched / algorithmic KV bytes = %.4f" % (fb / kv),
+                "kernel sources hash (bench.kernel_hash): %s" % kernel_hash(), ""]
+        with open(os.path.join(prof, "partial_kernel_%s.md" % w), "w") as f:
+            f.write("\n".join(out))
+    with open(os.path.join(prof, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+        f.write("\n")
+    print("wrote profiles/ for %s (kernel hash %s)" % (", ".join(PROFILED), kernel_hash()))
 
 
 def p_lens(p):

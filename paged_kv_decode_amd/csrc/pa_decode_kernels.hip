@@ -58,6 +58,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kPage = 16;
 constexpr float kLn2 = 0.693147180559945309f;
+// Headroom (log2 units) of the softmax reference value over the running max.
+constexpr float kSlack = 8.f;
 
 template <int DT> struct Elt;
 template <> struct Elt<PA_DTYPE_F32> { static constexpr int bytes = 4; };
@@ -101,6 +103,25 @@ __device__ __forceinline__ float sum_rows(float x)
         x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
     if constexpr (CH <= 32) x += __shfl_xor(x, 32);
     return x;
+}
+
+// Max / sum over the four 16-lane rows of the wave, for each lane % 16:
+// permlane32_swap pairs rows {0,1} with {2,3}, permlane16_swap row 0 with 1
+// and row 2 with 3 (VALU lane swaps, no LDS round trip).
+__device__ __forceinline__ float rows4_max(float x)
+{
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows4_sum(float x)
+{
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ void wave_lds_sync()
@@ -183,10 +204,17 @@ __device__ __forceinline__ u32x4 load16_stream(const void* p)
 template <int DT> struct PV;
 
 template <> struct PV<PA_DTYPE_F16> {
+    // p = hi + lo in two f16 parts (22 significant bits): f16 p alone leaves
+    // a relative error near 2^-12 per probability, which alone would use a
+    // third of the output tolerance after rounding to f16.
     __device__ static f32x4 mma(const float p[4], s16x4 v, f32x4 c)
     {
-        const f16x4 a = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, __builtin_bit_cast(f16x4, v), c, 0, 0, 0);
+        const f16x4 hi = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+        const f16x4 lo = {(_Float16)(p[0] - (float)hi[0]), (_Float16)(p[1] - (float)hi[1]),
+                          (_Float16)(p[2] - (float)hi[2]), (_Float16)(p[3] - (float)hi[3])};
+        const f16x4 vh = __builtin_bit_cast(f16x4, v);
+        c = __builtin_amdgcn_mfma_f32_16x16x16f16(hi, vh, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(lo, vh, c, 0, 0, 0);
     }
 };
 
@@ -242,8 +270,6 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     constexpr int NDB = D / 16;       // 16-column blocks of the output
     constexpr int GP4 = (G + 3) / 4 * 4;
     constexpr int IPV = kWave / NB;   // loop iterations one page-id vector covers
-    constexpr bool QLDS = KS >= 8;    // q operand read from LDS (saves 4*KS VGPRs)
-    constexpr int QTILE = QLDS ? KS * kWave * 4 : 0;  // floats
     constexpr int KT = NB * kPage * CH;  // 16-byte chunks of one block's K (or V) tile
     static_assert(KS * 4 == CH && R * CH == kWave && R * KS == kPage, "lane map");
     static_assert(KT == 8 * kWave && (CH == 8 || CH == 16 || CH == 32), "tiles");
@@ -281,33 +307,19 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         ids = load_ids(pgs, min(pgs + S / kPage, prm.pt_stride), 0);
     }
 
-    // q as the MFMA B operand: column i16 = query head kvh*G + i16 (zero past G).
-    u32x4 qa[QLDS ? 1 : KS];
+    // q as the MFMA B operand, held in VGPRs: column i16 = query head
+    // kvh*G + i16 (zero past G), chunk 4*ks + grp of head_dim.
+    u32x4 qa[KS];
     {
         const bool real = i16 < Gact;
         const char* qrow = static_cast<const char*>(prm.q) +
                            (size_t(b) * prm.num_q_heads + size_t(kvh) * Gact + (real ? i16 : 0)) * D * EB;
-        if constexpr (QLDS) {
-            // One copy per workgroup: [ks][lane] 16-byte chunks.
-            u32x4* qt = reinterpret_cast<u32x4*>(smem);
-            for (int ks = wave; ks < KS; ks += nw) {
-                u32x4 z = {0u, 0u, 0u, 0u};
-                qt[ks * kWave + lane] = real ? load16(qrow + (4 * ks + grp) * 16) : z;
-            }
-        } else {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                u32x4 z = {0u, 0u, 0u, 0u};
-                qa[ks] = real ? load16(qrow + (4 * ks + grp) * 16) : z;
-            }
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 z = {0u, 0u, 0u, 0u};
+            qa[ks] = real ? load16(qrow + (4 * ks + grp) * 16) : z;
         }
     }
-    auto q_operand = [&](int ks) -> u32x4 {
-        if constexpr (QLDS)
-            return reinterpret_cast<const u32x4*>(smem)[ks * kWave + lane];
-        else
-            return qa[ks];
-    };
 
     const int n = prm.context_lens[b];
     const int lo = (prm.window > 0 && n > prm.window) ? n - prm.window : 0;
@@ -331,7 +343,7 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4* ktile = reinterpret_cast<u32x4*>(smem + QTILE + wave * 8 * KT);
+    u32x4* ktile = reinterpret_cast<u32x4*>(smem + wave * 8 * KT);
     u32x4* vtile = ktile + KT;
     // Tile layout (K and V alike): chunk j of tile row r (page r / 16, token
     // r % 16) sits at r * CH + (j ^ swz(r)); swz permutes within aligned
@@ -342,7 +354,6 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
 
     const int nblk = active ? (pg1 - pg0 + NB - 1) / NB : 0;
     const int nit = nblk > wi ? (nblk - wi + wpp - 1) / wpp : 0;
-    if constexpr (QLDS) __syncthreads();   // q tile written
 
     // Software pipeline over the wave's blocks: as soon as block it's K and V
     // rows are in the LDS tiles, the registers take block it+1's loads, so the
@@ -396,6 +407,120 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
             }
     };
 
+    // One pipeline step: block it's rows go from the registers to the tiles,
+    // the registers take block it+1's loads, then block it is computed.
+    auto step = [&](int it, int it0, int it1) {
+        const int pgb = pg0 + (wi + wpp * it) * NB;
+        const int nbv = min(NB, pg1 - pgb);
+        // Edge blocks only (partition or window ends, short blocks) need
+        // the V mask (wave-uniform).
+        const bool edge = nbv < NB || pgb * kPage < t0 || (pgb + NB) * kPage > t1;
+
+        stage(ktile, kr, false, pgb, nbv);
+        if (edge)
+            stage(vtile, vr, true, pgb, nbv);
+        else
+            stage(vtile, vr, false, pgb, nbv);
+        wave_lds_sync();
+        fetch_ids(it + 1, it0, it1);
+        issue(kbase, kr);
+        pin_loads();
+        issue(vbase, vr);
+        pin_loads();
+
+        // Scores (base 2) of head i16 against token 4*grp + r of each page.
+        float s[NB][4];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+            const u32x4* krow = ktile + (nb * kPage + i16) * CH;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                d = Chunk<DT>::mfma(krow[(4 * ks + grp) ^ kswz], qa[ks], d);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = (pgb + nb) * kPage + 4 * grp + r;
+                const bool ok = nb < nbv && tok >= t0 && tok < t1;
+                s[nb][r] = ok ? d[r] * prm.scale_log2 : -INFINITY;
+            }
+        }
+
+        // Block maximum of head i16: the lane's own 4*NB scores, then the
+        // four lane groups.
+        float bm = s[0][0];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bm = fmaxf(bm, s[nb][r]);
+        bm = rows4_max(bm);
+        // The reference value m_run the exponentials are taken against
+        // moves only when the block maximum passes it by more than
+        // kSlack (so p <= 2^kSlack, exact in f16 / bf16 hi+lo and f32);
+        // the state (m, l, acc) is exact for any reference, since the
+        // result is acc / l and m + log2(l).  The output accumulators
+        // then need rescaling only on those rare moves (wave-uniform
+        // decision).
+        const bool grow = bm > m_run + kSlack;
+        const float mnew = grow ? bm : m_run;
+        const float alpha = grow ? fast_exp2(m_run - bm) : 1.f;
+        const bool any_rescale = __any(grow && i16 < G);
+        float ps = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                s[nb][r] = fast_exp2(s[nb][r] - mnew);
+                ps += s[nb][r];
+            }
+        l_run = alpha * l_run + ps;
+        m_run = mnew;
+
+        if (any_rescale) {
+            // Row 4*grp + r of the output blocks is head 4*grp + r, whose
+            // alpha sits in lane 4*grp + r.
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float a = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) acc[db][r] *= a;
+            }
+        }
+
+        // P.V: V rows 4*grp + i16/4 of each page, columns 16*db +
+        // 4*(i16%4) .. +3 for the transpose read.
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int vrow = nb * kPage + 4 * grp + (i16 >> 2);
+            const char* vrow_p = reinterpret_cast<const char*>(vtile + vrow * CH);
+            const int vsw = swz(vrow);
+            if constexpr (DT == PA_DTYPE_F32) {
+                // 16x16x4 f32 steps: step r takes token 4*grp + r of
+                // every lane group (k index grp).
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = nb * kPage + 4 * grp + r;
+                    const float* vr_p = reinterpret_cast<const float*>(vtile + row * CH);
+                    const int rsw = swz(row);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const int col = 16 * db + i16;
+                        const float v = vr_p[((col >> 2) ^ rsw) * 4 + (col & 3)];
+                        acc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(s[nb][r], v, acc[db], 0, 0, 0);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const int j = 2 * db + ((i16 & 3) >> 1);
+                    const char* addr = vrow_p + (j ^ vsw) * 16 + (i16 & 1) * 8;
+                    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(addr));
+                    acc[db] = PV<DT>::mma(s[nb], v, acc[db]);
+                }
+            }
+        }
+    };
+
     // Outer loop over chunks of IPV blocks (one page-id vector each); the
     // pipelined inner loop itself issues no load but K/V.
     for (int it0 = 0; it0 < nit; it0 += IPV) {
@@ -407,118 +532,11 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         pin_loads();
         issue(vbase, vr);
         pin_loads();
-
-        for (int it = it0; it < it1; ++it) {
-            const int pgb = pg0 + (wi + wpp * it) * NB;
-            const int nbv = min(NB, pg1 - pgb);
-            // Edge blocks only (partition or window ends, short blocks) need
-            // the V mask (wave-uniform).
-            const bool edge = nbv < NB || pgb * kPage < t0 || (pgb + NB) * kPage > t1;
-
-            stage(ktile, kr, false, pgb, nbv);
-            if (edge)
-                stage(vtile, vr, true, pgb, nbv);
-            else
-                stage(vtile, vr, false, pgb, nbv);
-            wave_lds_sync();
-            fetch_ids(it + 1, it0, it1);
-            issue(kbase, kr);
-            pin_loads();
-            issue(vbase, vr);
-            pin_loads();
-
-            // Scores (base 2) of head i16 against token 4*grp + r of each page.
-            float s[NB][4];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                f32x4 d = {0.f, 0.f, 0.f, 0.f};
-                const u32x4* krow = ktile + (nb * kPage + i16) * CH;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    d = Chunk<DT>::mfma(krow[(4 * ks + grp) ^ kswz], q_operand(ks), d);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tok = (pgb + nb) * kPage + 4 * grp + r;
-                    const bool ok = nb < nbv && tok >= t0 && tok < t1;
-                    s[nb][r] = ok ? d[r] * prm.scale_log2 : -INFINITY;
-                }
-            }
-
-            // Block maximum of head i16: the lane's own 4*NB scores, then the
-            // four lane groups (xor 16 by ds_swizzle, xor 32 by ds_bpermute).
-            float bm = s[0][0];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) bm = fmaxf(bm, s[nb][r]);
-            bm = fmaxf(bm, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(bm), 0x401F)));
-            bm = fmaxf(bm, __shfl_xor(bm, 32));
-            const float mnew = fmaxf(m_run, bm);
-            const float alpha = fast_exp2(m_run - mnew);
-            // The output accumulators need rescaling only when some head's
-            // running maximum moved (wave-uniform decision).
-            const bool any_rescale = __any(mnew != m_run && i16 < G);
-            float ps = 0.f;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    s[nb][r] = fast_exp2(s[nb][r] - mnew);
-                    ps += s[nb][r];
-                }
-            l_run = alpha * l_run + ps;
-            m_run = mnew;
-
-            if (any_rescale) {
-                // Row 4*grp + r of the output blocks is head 4*grp + r, whose
-                // alpha sits in lane 4*grp + r.
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float a = __shfl(alpha, 4 * grp + r);
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) acc[db][r] *= a;
-                }
-            }
-
-            // P.V: V rows 4*grp + i16/4 of each page, columns 16*db +
-            // 4*(i16%4) .. +3 for the transpose read.
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const int vrow = nb * kPage + 4 * grp + (i16 >> 2);
-                const char* vrow_p = reinterpret_cast<const char*>(vtile + vrow * CH);
-                const int vsw = swz(vrow);
-                if constexpr (DT == PA_DTYPE_F32) {
-                    // 16x16x4 f32 steps: step r takes token 4*grp + r of
-                    // every lane group (k index grp).
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = nb * kPage + 4 * grp + r;
-                        const float* vr_p = reinterpret_cast<const float*>(vtile + row * CH);
-                        const int rsw = swz(row);
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db) {
-                            const int col = 16 * db + i16;
-                            const float v = vr_p[((col >> 2) ^ rsw) * 4 + (col & 3)];
-                            acc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(s[nb][r], v, acc[db], 0, 0, 0);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const int j = 2 * db + ((i16 & 3) >> 1);
-                        const char* addr = vrow_p + (j ^ vsw) * 16 + (i16 & 1) * 8;
-                        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) s16x4*)(addr));
-                        acc[db] = PV<DT>::mma(s[nb], v, acc[db]);
-                    }
-                }
-            }
-        }
+        for (int it = it0; it < it1; ++it) step(it, it0, it1);
     }  // chunks of IPV blocks
 
     // Denominator of head i16 over the four lane groups.
-    l_run += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(l_run), 0x401F));
-    l_run += __shfl_xor(l_run, 32);
+    l_run = rows4_sum(l_run);
 
     // Combine the waves of each partition slot in LDS: maximum first, then
     // the rescaled denominators and outputs.  A wave without blocks holds

@@ -199,13 +199,10 @@ size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan)
     const int G = template_group(d.num_q_heads / d.num_kv_heads);
     const int gp4 = (G + 3) / 4 * 4;
     const int nw = plan.waves_per_group;
-    // q tile of the 16-bit head_dim-256 kernels: 8 chunks x 64 lanes x 16 B.
-    const int ks = d.head_dim * dtype_bytes(d.dtype) / 64;
-    const size_t qtile = ks >= 8 ? size_t(ks) * 64 * 4 : 0;
     // per wave: the block's K and V tiles (8 KiB each)
     const size_t ktile = size_t(plan.pages_per_block) * kPageSize * d.head_dim *
                          dtype_bytes(d.dtype) / sizeof(float);
-    const size_t loop = qtile + size_t(nw) * 2 * ktile;
+    const size_t loop = size_t(nw) * 2 * ktile;
     const size_t comb = size_t(nw) * size_t(2 * gp4 + G * d.head_dim);
     return std::max(loop, comb) * sizeof(float);
 }
