@@ -218,6 +218,51 @@ template <> struct PV<PA_DTYPE_F16> {
     }
 };
 
+// Two pages at once (16x16x32): k slots 0..3 of a lane group are page a's
+// tokens 4*grp + j, slots 4..7 page b's; the V operand is the two transpose
+// reads side by side.
+template <int DT> struct PV2;
+
+template <> struct PV2<PA_DTYPE_F16> {
+    __device__ static f32x4 mma(const float pa[4], const float pb[4], s16x4 va, s16x4 vb, f32x4 c)
+    {
+        f16x8 hi, lo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            hi[j] = (_Float16)pa[j];
+            hi[4 + j] = (_Float16)pb[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            lo[j] = (_Float16)(pa[j] - (float)hi[j]);
+            lo[4 + j] = (_Float16)(pb[j] - (float)hi[4 + j]);
+        }
+        const f16x8 v = __builtin_bit_cast(f16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, v, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, v, c, 0, 0, 0);
+    }
+};
+
+template <> struct PV2<PA_DTYPE_BF16> {
+    __device__ static f32x4 mma(const float pa[4], const float pb[4], s16x4 va, s16x4 vb, f32x4 c)
+    {
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            hi[j] = (__bf16)pa[j];
+            hi[4 + j] = (__bf16)pb[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            lo[j] = (__bf16)(pa[j] - (float)hi[j]);
+            lo[4 + j] = (__bf16)(pb[j] - (float)hi[4 + j]);
+        }
+        const bf16x8 v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, v, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, v, c, 0, 0, 0);
+    }
+};
+
 template <> struct PV<PA_DTYPE_BF16> {
     // p = hi + lo in two bf16 parts (16 significant bits): one bf16 part alone
     // would leave a relative error near 2^-9 in every probability.
@@ -272,7 +317,7 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     constexpr int IPV = kWave / NB;   // loop iterations one page-id vector covers
     constexpr int KT = NB * kPage * CH;  // 16-byte chunks of one block's K (or V) tile
     static_assert(KS * 4 == CH && R * CH == kWave && R * KS == kPage, "lane map");
-    static_assert(KT == 8 * kWave && (CH == 8 || CH == 16 || CH == 32), "tiles");
+    static_assert(KT % kWave == 0 && (CH == 8 || CH == 16 || CH == 32), "tiles");
     static_assert(G <= 16, "one 16-row MFMA block of query heads");
 
     extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -488,14 +533,18 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
 
         // P.V: V rows 4*grp + i16/4 of each page, columns 16*db +
         // 4*(i16%4) .. +3 for the transpose read.
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+        auto tr_read = [&](int nb, int db) -> s16x4 {
             const int vrow = nb * kPage + 4 * grp + (i16 >> 2);
             const char* vrow_p = reinterpret_cast<const char*>(vtile + vrow * CH);
-            const int vsw = swz(vrow);
-            if constexpr (DT == PA_DTYPE_F32) {
-                // 16x16x4 f32 steps: step r takes token 4*grp + r of
-                // every lane group (k index grp).
+            const int j = 2 * db + ((i16 & 3) >> 1);
+            const char* addr = vrow_p + (j ^ swz(vrow)) * 16 + (i16 & 1) * 8;
+            return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(addr));
+        };
+        if constexpr (DT == PA_DTYPE_F32) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                // 16x16x4 f32 steps: step r takes token 4*grp + r of every
+                // lane group (k index grp).
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = nb * kPage + 4 * grp + r;
@@ -508,15 +557,20 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
                         acc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(s[nb][r], v, acc[db], 0, 0, 0);
                     }
                 }
-            } else {
+            }
+        } else if constexpr (NB % 2 == 0) {
+            // Pages in pairs: 32 tokens per MFMA (the same issue cost as 16).
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const int j = 2 * db + ((i16 & 3) >> 1);
-                    const char* addr = vrow_p + (j ^ vsw) * 16 + (i16 & 1) * 8;
-                    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4*)(addr));
-                    acc[db] = PV<DT>::mma(s[nb], v, acc[db]);
-                }
+            for (int nb = 0; nb < NB; nb += 2) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    acc[db] = PV2<DT>::mma(s[nb], s[nb + 1], tr_read(nb, db), tr_read(nb + 1, db), acc[db]);
+            }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) acc[db] = PV<DT>::mma(s[nb], tr_read(nb, db), acc[db]);
             }
         }
     };

@@ -18,6 +18,9 @@ int dtype_bytes(int dtype)
 
 int pages_per_block(int head_dim, int dtype)
 {
+    // 8 KiB of K per block.  (Two 512-byte-row pages per block, for 32-token
+    // P.V MFMAs, measured slower on MI355X: the doubled load registers push
+    // the kernel to one wave per SIMD with AGPR spills.)
     int row = head_dim * dtype_bytes(dtype);
     return std::max(1, std::min(4, 512 / row));
 }
@@ -122,13 +125,15 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
         S = ceil_div(max_context_len, ps) * ps;
     }
 
-    // Waves per workgroup: four, fewer when the combine buffer would pass
-    // 64 KiB of LDS.
+    // Waves per workgroup: four, fewer when the K/V tiles or the combine
+    // buffer would pass 64 KiB of LDS.
     int nw = kMaxWavesPerGroup;
     {
         const int Gt = template_group(G);
         const int gp4 = (Gt + 3) / 4 * 4;
-        const int64_t per_wave = int64_t(2 * gp4 + Gt * d.head_dim) * 4;
+        const int64_t comb = int64_t(2 * gp4 + Gt * d.head_dim) * 4;
+        const int64_t tiles = int64_t(2) * nb * ps * d.head_dim * dtype_bytes(d.dtype);
+        const int64_t per_wave = std::max(comb, tiles);
         while (nw > 1 && nw * per_wave > 65536) nw /= 2;
     }
     // Waves sharing one partition: the count (1, 2 or 4, at most one per
