@@ -69,7 +69,8 @@ def log(msg):
 class Replicas:
     """R page-permuted copies of one problem, resident on the GPU."""
 
-    def __init__(self, p: W.Problem, R: int, eng: binding.PagedDecode, partition_size: int):
+    def __init__(self, p: W.Problem, R: int, eng: binding.PagedDecode, partition_size: int,
+                 table: str = "dense"):
         self.p = p
         dev = torch.device("cuda", 0)
         k0 = p.k_cache.to(dev)
@@ -80,7 +81,15 @@ class Replicas:
         B, Hq, D = p.q.shape
         self.out = torch.empty((B, Hq, D), dtype=p.q.dtype, device=dev)
         self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-        ws_bytes = eng.workspace_size(B, p.max_context_len, p.window, partition_size)
+        csr = W.to_csr(p) if table == "csr" else None
+        if csr is not None:
+            ws_bytes = binding.pa_decode_workspace_size_csr(eng.handle, B, csr.nnz_pages,
+                                                            p.max_context_len, p.window,
+                                                            partition_size)
+            self.run = eng.run_csr_args
+        else:
+            ws_bytes = eng.workspace_size(B, p.max_context_len, p.window, partition_size)
+            self.run = eng.run_args
         self.ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
         self.caches = []
         self.args = []
@@ -90,6 +99,7 @@ class Replicas:
         for r in range(R):
             if r == 0:
                 k, v, pt = k0, v0, pt0
+                perm = None
             else:
                 perm = torch.randperm(num_pages, generator=gen).to(dev)
                 k = torch.empty_like(k0)
@@ -98,10 +108,19 @@ class Replicas:
                 v[perm] = v0
                 pt = perm.to(torch.int32)[pt0.long()]
             self.caches.append((k, v, pt))
-            self.args.append(eng.make_args(self.q, k, v, pt, self.lens, p.scale, self.out,
-                                           self.lse, max_context_len=p.max_context_len,
-                                           sliding_window=p.window,
-                                           partition_size=partition_size, workspace=self.ws))
+            if csr is not None:
+                idx = csr.indices.to(dev)
+                if perm is not None and idx.numel():
+                    idx = perm.to(torch.int32)[idx.long()]
+                self.args.append(eng.make_csr_args(
+                    self.q, k, v, csr.indptr.to(dev), idx.contiguous(), csr.last_page_len.to(dev),
+                    csr.nnz_pages, p.scale, self.out, self.lse, max_context_len=p.max_context_len,
+                    sliding_window=p.window, partition_size=partition_size, workspace=self.ws))
+            else:
+                self.args.append(eng.make_args(self.q, k, v, pt, self.lens, p.scale, self.out,
+                                               self.lse, max_context_len=p.max_context_len,
+                                               sliding_window=p.window,
+                                               partition_size=partition_size, workspace=self.ws))
 
 
 def run_oracle_baseline(p: W.Problem, budget_s: float):
@@ -120,7 +139,8 @@ def run_oracle_baseline(p: W.Problem, budget_s: float):
     return out, lse, reps, el, threads
 
 
-def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cache):
+def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cache,
+                   table="dense"):
     w = W.CONFIGS[name]
     S = w.partition_size if partition_size is None else partition_size
     t0 = time.perf_counter()
@@ -139,7 +159,7 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
         R = min(R, max(2, int((64 << 30) // pool_bytes)))
     else:
         R = replicas
-    reps = Replicas(p, R, eng, S)
+    reps = Replicas(p, R, eng, S, table)
     log("%s: %d replicas, %.1f MB KV per step" % (name, R, kv_bytes / 1e6))
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -147,7 +167,7 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
     # Every replica must produce the same bits (page-shuffle invariance).
     outs = []
     for r in (0, R - 1):
-        eng.run_args(reps.args[r], sp)
+        reps.run(reps.args[r], sp)
         torch.cuda.synchronize()
         outs.append((reps.out.clone(), reps.lse.clone()))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1]), \
@@ -155,7 +175,7 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
     plan = eng.last_plan().as_dict()
 
     for i in range(warmup):
-        eng.run_args(reps.args[i % R], sp)
+        reps.run(reps.args[i % R], sp)
     torch.cuda.synchronize()
 
     if mode == "graph":
@@ -166,7 +186,7 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
             with torch.cuda.graph(g, stream=cap):
                 cs = torch.cuda.current_stream().cuda_stream
                 for i in range(steps):
-                    eng.run_args(reps.args[i % R], cs)
+                    reps.run(reps.args[i % R], cs)
         stream.wait_stream(cap)
         g.replay()  # upload / first replay, untimed
         torch.cuda.synchronize()
@@ -177,7 +197,7 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
         g.replay()
     else:
         for i in range(steps):
-            eng.run_args(reps.args[i % R], sp)
+            reps.run(reps.args[i % R], sp)
     stop.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(stop)
@@ -187,7 +207,7 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
     nprof = min(steps, 2000)
     binding.pa_decode_profile_begin(eng.handle, nprof)
     for i in range(nprof):
-        eng.run_args(reps.args[i % R], sp)
+        reps.run(reps.args[i % R], sp)
     pm, pn, mm, mn = binding.pa_decode_profile_end(eng.handle)
     partial_us = 1e3 * pm / max(pn, 1)
     merge_us = 1e3 * mm / max(mn, 1) if mn else 0.0
@@ -243,6 +263,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--page-table", choices=["dense", "csr"], default="dense",
+                    help="page-table form passed to the library (csr: pa_decode_run_csr)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
     ap.add_argument("--probe", choices=["copy"], default=None,
@@ -278,13 +300,14 @@ def main():
 
     engines = {}
     main_res = bench_workload(args.workload, args.steps, args.warmup, args.replicas,
-                              args.partition_size, args.mode, engines)
+                              args.partition_size, args.mode, engines, args.page_table)
     log("%s: %.2f us/step, %.0f GB/s; partial %.2f us (%.0f GB/s), merge %.2f us" % (
         args.workload, main_res["us_per_step"], main_res["gbps"], main_res["partial_us"],
         main_res["partial_gbps"], main_res["merge_us"]))
     also = {}
     for name in [s for s in args.also.split(",") if s and s != args.workload]:
-        r = bench_workload(name, args.also_steps, 20, None, None, args.mode, engines)
+        r = bench_workload(name, args.also_steps, 20, None, None, args.mode, engines,
+                           args.page_table)
         rel, lerr = parity(r)
         also[name] = {
             "us_per_step": round(r["us_per_step"], 3), "GBps": round(r["gbps"], 1),
@@ -334,6 +357,7 @@ def main():
                    "context_lens": p_lens(main_res["p"]), "page_size": w.page_size,
                    "sliding_window": w.window, "kv_bytes_per_step": main_res["kv_bytes"],
                    "replicas": main_res["replicas"], "mode": args.mode,
+                   "page_table": args.page_table,
                    "plan": main_res["plan"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),

@@ -169,6 +169,68 @@ int pa_decode_plan_query(const pa_decode_desc* desc, int32_t num_cus, int32_t wa
                          int32_t batch, int32_t max_context_len, int32_t sliding_window,
                          int32_t partition_size, pa_decode_plan* plan);
 
+/* ---------------------------------------------------------------------------
+ * CSR page-table form.
+ *
+ * TVM PR #20426, section "Change", chooses between its single-pass kernel
+ * and the sharded one on the host from the number of pages in use,
+ * nnz_pages > B * 256 / page_size.  The page table that count belongs to is
+ * a CSR (compressed-row) table: sequence b owns the pages
+ *   page_indices[page_indptr[b]], ..., page_indices[page_indptr[b+1] - 1]
+ * in token order, and the last of them holds last_page_len[b] tokens, so
+ *   n_b = (page_indptr[b+1] - page_indptr[b] - 1) * page_size + last_page_len[b]
+ * (n_b = 0 when the sequence owns no page; last_page_len is clamped to
+ * [0, page_size]).  Everything else (the operation, windows, strides, out,
+ * lse, workspace, ownership, errors) is as for pa_decode_args /
+ * pa_decode_run: the same kernels run, only the page-id gather differs.
+ * ------------------------------------------------------------------------- */
+typedef struct pa_decode_csr_args {
+    const void* q;                /* device, [batch, Hq, D] contiguous */
+    const void* k_cache;          /* device, paged K/V as in pa_decode_args */
+    const void* v_cache;
+    int64_t kv_stride_page;
+    int64_t kv_stride_head;
+    int64_t kv_stride_slot;
+    int32_t num_pages;            /* pages in the pool (page ids must be < num_pages) */
+    const int32_t* page_indptr;   /* device, int32 [batch + 1], non-decreasing, [0] = 0 */
+    const int32_t* page_indices;  /* device, int32 [nnz_pages] (NULL allowed when 0) */
+    const int32_t* last_page_len; /* device, int32 [batch], 1..page_size for a      */
+                                  /*   sequence that owns pages                      */
+    int32_t nnz_pages;            /* host copy of page_indptr[batch] */
+    int32_t batch;                /* B, 0 <= B <= desc.max_batch */
+    int32_t max_context_len;      /* host upper bound of n_b; 0: nnz_pages * page_size */
+    float scale;
+    int32_t sliding_window;       /* <= 0: no window; else keys [n_b - W, n_b) */
+    int32_t partition_size;       /* 0: the host switch above -- one partition per    */
+                                  /*   (sequence, KV head) when nnz_pages <=          */
+                                  /*   B * 256 / page_size, else the planner's split; */
+                                  /*   > 0: tokens per partition, as in pa_decode_args */
+    void* out;                    /* device, [batch, Hq, D] contiguous, desc.dtype */
+    float* lse;                   /* device, float32 [batch, Hq], may be NULL */
+    void* workspace;              /* device scratch, pa_decode_workspace_size_csr bytes */
+    size_t workspace_bytes;
+} pa_decode_csr_args;
+
+/* Workspace bytes pa_decode_run_csr needs (pure host). */
+int pa_decode_workspace_size_csr(pa_decode_handle handle, int32_t batch, int32_t nnz_pages,
+                                 int32_t max_context_len, int32_t sliding_window,
+                                 int32_t partition_size, size_t* bytes);
+
+/* One decode step from a CSR page table, on `stream`.  Errors as for
+ * pa_decode_run; additionally INVALID_ARG when nnz_pages < 0, when
+ * page_indptr / last_page_len are NULL with batch > 0, or when page_indices
+ * is NULL with nnz_pages > 0.  Device-side contract: page_indptr and
+ * last_page_len describe rows inside page_indices[0, nnz_pages), every page
+ * id < num_pages, n_b <= max_context_len. */
+int pa_decode_run_csr(pa_decode_handle handle, const pa_decode_csr_args* args, void* stream);
+
+/* The plan pa_decode_run_csr makes for these sizes (pure host; as
+ * pa_decode_plan_query, plus the host switch on nnz_pages). */
+int pa_decode_plan_query_csr(const pa_decode_desc* desc, int32_t num_cus, int32_t waves_per_cu,
+                             int32_t batch, int32_t nnz_pages, int32_t max_context_len,
+                             int32_t sliding_window, int32_t partition_size,
+                             pa_decode_plan* plan);
+
 /* Kernel timing for measurement tools.  After pa_decode_profile_begin, the
  * next `max_launches` launches of each kernel (partial, merge) made by
  * pa_decode_run on this handle carry start/stop HIP events recorded on the

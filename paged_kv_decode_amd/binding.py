@@ -35,7 +35,8 @@ DTYPE_CODE = {torch.float32: PA_DTYPE_F32, torch.float16: PA_DTYPE_F16,
 EXPORTED = ["pa_decode_create", "pa_decode_destroy", "pa_decode_workspace_size",
             "pa_decode_run", "pa_decode_last_plan", "pa_decode_plan_query",
             "pa_decode_profile_begin", "pa_decode_profile_end",
-            "pa_decode_last_hip_error", "pa_decode_status_string"]
+            "pa_decode_last_hip_error", "pa_decode_status_string",
+            "pa_decode_workspace_size_csr", "pa_decode_run_csr", "pa_decode_plan_query_csr"]
 
 
 class PaDecodeDesc(ctypes.Structure):
@@ -56,6 +57,19 @@ class PaDecodeArgs(ctypes.Structure):
                 ("partition_size", ctypes.c_int32), ("out", ctypes.c_void_p),
                 ("lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t)]
+
+
+class PaDecodeCsrArgs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p),
+                ("v_cache", ctypes.c_void_p), ("kv_stride_page", ctypes.c_int64),
+                ("kv_stride_head", ctypes.c_int64), ("kv_stride_slot", ctypes.c_int64),
+                ("num_pages", ctypes.c_int32), ("page_indptr", ctypes.c_void_p),
+                ("page_indices", ctypes.c_void_p), ("last_page_len", ctypes.c_void_p),
+                ("nnz_pages", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("max_context_len", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("sliding_window", ctypes.c_int32), ("partition_size", ctypes.c_int32),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class PaDecodePlan(ctypes.Structure):
@@ -112,6 +126,12 @@ def load_library(path: Optional[str] = None):
         lib.pa_decode_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                               ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_double),
                                               ctypes.POINTER(i32)]
+        lib.pa_decode_workspace_size_csr.argtypes = [vp, i32, i32, i32, i32, i32,
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+        lib.pa_decode_run_csr.argtypes = [vp, ctypes.POINTER(PaDecodeCsrArgs), vp]
+        lib.pa_decode_plan_query_csr.argtypes = [ctypes.POINTER(PaDecodeDesc), i32, i32, i32,
+                                                 i32, i32, i32, i32,
+                                                 ctypes.POINTER(PaDecodePlan)]
         lib.pa_decode_last_hip_error.argtypes = [vp]
         lib.pa_decode_status_string.argtypes = [ctypes.c_int]
         lib.pa_decode_status_string.restype = ctypes.c_char_p
@@ -126,6 +146,33 @@ def load_library(path: Optional[str] = None):
 def _check(status: int, what: str):
     if status != PA_DECODE_OK:
         raise PaDecodeError(status, what)
+
+
+def pa_decode_workspace_size_csr(handle, batch: int, nnz_pages: int, max_context_len: int = 0,
+                                 sliding_window: int = 0, partition_size: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().pa_decode_workspace_size_csr(handle, batch, nnz_pages, max_context_len,
+                                                       sliding_window, partition_size,
+                                                       ctypes.byref(n)),
+           "pa_decode_workspace_size_csr")
+    return int(n.value)
+
+
+def pa_decode_run_csr(handle, args: PaDecodeCsrArgs, stream: int = 0) -> None:
+    _check(load_library().pa_decode_run_csr(handle, ctypes.byref(args), ctypes.c_void_p(stream)),
+           "pa_decode_run_csr")
+
+
+def pa_decode_plan_query_csr(desc: PaDecodeDesc, num_cus: int, waves_per_cu: int, batch: int,
+                             nnz_pages: int, max_context_len: int = 0, sliding_window: int = 0,
+                             partition_size: int = 0) -> PaDecodePlan:
+    plan = PaDecodePlan()
+    _check(load_library().pa_decode_plan_query_csr(ctypes.byref(desc), num_cus, waves_per_cu,
+                                                   batch, nnz_pages, max_context_len,
+                                                   sliding_window, partition_size,
+                                                   ctypes.byref(plan)),
+           "pa_decode_plan_query_csr")
+    return plan
 
 
 def pa_decode_status_string(status: int) -> str:
@@ -307,6 +354,66 @@ class PagedDecode:
                               max_context_len, sliding_window, partition_size)
         self.run_args(args)
         return out, lse
+
+    def make_csr_args(self, q, k_cache, v_cache, page_indptr, page_indices, last_page_len,
+                      nnz_pages, scale, out, lse=None, max_context_len=0, sliding_window=0,
+                      partition_size=0, workspace=None) -> PaDecodeCsrArgs:
+        """Argument block of pa_decode_run_csr; nnz_pages is the host copy of
+        page_indptr[-1]."""
+        for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                        ("page_indptr", page_indptr), ("page_indices", page_indices),
+                        ("last_page_len", last_page_len), ("out", out)):
+            if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+                raise TypeError("%s must be a device tensor" % name)
+        if q.dtype != self.dtype or k_cache.dtype != self.dtype or \
+                v_cache.dtype != self.dtype or out.dtype != self.dtype:
+            raise TypeError("q, k/v caches and out must be %s" % self.dtype)
+        if not q.is_contiguous() or not out.is_contiguous():
+            raise ValueError("q and out must be contiguous")
+        if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+            raise ValueError("k_cache and v_cache must share shape and strides")
+        if k_cache.dim() != 4 or k_cache.stride(3) != 1:
+            raise ValueError("caches must be [num_pages, Hkv, page_size, D] with D contiguous")
+        for name, t in (("page_indptr", page_indptr), ("page_indices", page_indices),
+                        ("last_page_len", last_page_len)):
+            if t.dtype != torch.int32 or not t.is_contiguous():
+                raise TypeError("%s must be contiguous int32" % name)
+        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+            raise TypeError("lse must be contiguous float32")
+        B = q.shape[0]
+        ws_bytes = pa_decode_workspace_size_csr(self.handle, B, nnz_pages, max_context_len,
+                                                sliding_window, partition_size)
+        if workspace is None:
+            workspace = self.workspace(ws_bytes)
+        a = PaDecodeCsrArgs()
+        a.q = q.data_ptr()
+        a.k_cache = k_cache.data_ptr()
+        a.v_cache = v_cache.data_ptr()
+        a.kv_stride_page = k_cache.stride(0)
+        a.kv_stride_head = k_cache.stride(1)
+        a.kv_stride_slot = k_cache.stride(2)
+        a.num_pages = k_cache.shape[0]
+        a.page_indptr = page_indptr.data_ptr()
+        a.page_indices = page_indices.data_ptr() if page_indices.numel() else None
+        a.last_page_len = last_page_len.data_ptr()
+        a.nnz_pages = int(nnz_pages)
+        a.batch = B
+        a.max_context_len = int(max_context_len)
+        a.scale = float(scale)
+        a.sliding_window = int(sliding_window)
+        a.partition_size = int(partition_size)
+        a.out = out.data_ptr()
+        a.lse = lse.data_ptr() if lse is not None else None
+        a.workspace = workspace.data_ptr() if workspace is not None else None
+        a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        a._keep = (q, k_cache, v_cache, page_indptr, page_indices, last_page_len, out, lse,
+                   workspace)
+        return a
+
+    def run_csr_args(self, args: PaDecodeCsrArgs, stream: Optional[int] = None) -> None:
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        pa_decode_run_csr(self.handle, args, stream)
 
     def last_plan(self) -> PaDecodePlan:
         return pa_decode_last_plan(self.handle)

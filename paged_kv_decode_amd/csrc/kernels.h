@@ -13,9 +13,11 @@ struct PartialParams {
     const void* k;            // paged K, element strides below (D contiguous)
     const void* v;            // paged V, same strides
     int64_t stride_page, stride_head, stride_slot;
-    const int32_t* page_table;
+    const int32_t* page_table;    // dense: [B, pt_stride]; CSR: page indices
     int32_t pt_stride;
-    const int32_t* context_lens;
+    const int32_t* context_lens;  // dense form only
+    const int32_t* page_indptr;   // CSR form ([B + 1]); null for the dense form
+    const int32_t* last_page_len; // CSR form ([B])
     int32_t num_q_heads;
     int32_t group;            // actual G = Hq / Hkv
     int32_t partition_size;   // S tokens
@@ -33,11 +35,8 @@ struct PartialParams {
 
 // Arguments of the merge kernel (one workgroup per (query head, b)).
 struct MergeParams {
-    const int32_t* context_lens;
     int32_t num_q_heads;
-    int32_t partition_size;
     int32_t num_partitions;
-    int32_t window;
     const float* ws_o;
     const float* ws_m;
     const float* ws_l;

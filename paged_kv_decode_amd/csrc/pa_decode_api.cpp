@@ -55,7 +55,48 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_args(const pa_decode_desc& d, const pa_decode_args& a)
+// The arguments both page-table forms share.
+struct StepArgs {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    int64_t kv_stride_page, kv_stride_head, kv_stride_slot;
+    int32_t num_pages;
+    int32_t batch;
+    int32_t max_context_len;
+    float scale;
+    int32_t sliding_window;
+    int32_t partition_size;
+    void* out;
+    float* lse;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+template <typename A>
+StepArgs common_args(const A& a)
+{
+    StepArgs c;
+    c.q = a.q;
+    c.k_cache = a.k_cache;
+    c.v_cache = a.v_cache;
+    c.kv_stride_page = a.kv_stride_page;
+    c.kv_stride_head = a.kv_stride_head;
+    c.kv_stride_slot = a.kv_stride_slot;
+    c.num_pages = a.num_pages;
+    c.batch = a.batch;
+    c.max_context_len = a.max_context_len;
+    c.scale = a.scale;
+    c.sliding_window = a.sliding_window;
+    c.partition_size = a.partition_size;
+    c.out = a.out;
+    c.lse = a.lse;
+    c.workspace = a.workspace;
+    c.workspace_bytes = a.workspace_bytes;
+    return c;
+}
+
+int check_common(const pa_decode_desc& d, const StepArgs& a)
 {
     if (a.batch < 0 || a.batch > d.max_batch || a.max_context_len < 0 ||
         a.max_context_len > d.max_context_len || a.partition_size < 0)
@@ -66,11 +107,7 @@ int check_args(const pa_decode_desc& d, const pa_decode_args& a)
         return PA_DECODE_INVALID_ARG;
     if (a.batch == 0)
         return PA_DECODE_OK;
-    if (!a.q || !a.k_cache || !a.v_cache || !a.page_table || !a.context_lens || !a.out)
-        return PA_DECODE_INVALID_ARG;
-    if (a.num_pages <= 0 || a.pt_stride <= 0)
-        return PA_DECODE_INVALID_ARG;
-    if (int64_t(a.pt_stride) * d.page_size < int64_t(a.max_context_len))
+    if (!a.q || !a.k_cache || !a.v_cache || !a.out || a.num_pages <= 0)
         return PA_DECODE_INVALID_ARG;
     const int eb = pa::dtype_bytes(d.dtype);
     // Strides: non-negative, 16-byte granular (each lane reads 16-byte chunks).
@@ -82,6 +119,115 @@ int check_args(const pa_decode_desc& d, const pa_decode_args& a)
         return PA_DECODE_INVALID_ARG;
     if (!aligned16(a.q) || !aligned16(a.k_cache) || !aligned16(a.v_cache) || !aligned16(a.out))
         return PA_DECODE_INVALID_ARG;
+    return PA_DECODE_OK;
+}
+
+int check_args(const pa_decode_desc& d, const pa_decode_args& a)
+{
+    int st = check_common(d, common_args(a));
+    if (st != PA_DECODE_OK || a.batch == 0)
+        return st;
+    if (!a.page_table || !a.context_lens || a.pt_stride <= 0)
+        return PA_DECODE_INVALID_ARG;
+    if (int64_t(a.pt_stride) * d.page_size < int64_t(a.max_context_len))
+        return PA_DECODE_INVALID_ARG;
+    return PA_DECODE_OK;
+}
+
+int check_csr_args(const pa_decode_desc& d, const pa_decode_csr_args& a)
+{
+    if (a.nnz_pages < 0 || (a.batch == 0 && a.nnz_pages != 0))
+        return PA_DECODE_INVALID_ARG;
+    int st = check_common(d, common_args(a));
+    if (st != PA_DECODE_OK || a.batch == 0)
+        return st;
+    if (!a.page_indptr || !a.last_page_len || (a.nnz_pages > 0 && !a.page_indices))
+        return PA_DECODE_INVALID_ARG;
+    return PA_DECODE_OK;
+}
+
+// Where the kernels find page ids and context lengths.
+struct PageSource {
+    const int32_t* page_table;    // dense rows, or CSR page indices
+    int32_t pt_stride;
+    const int32_t* context_lens;
+    const int32_t* page_indptr;   // null for the dense form
+    const int32_t* last_page_len;
+};
+
+// Launches one planned decode step on `stream` (arguments already checked).
+int launch_step(pa_decode_handle handle, const StepArgs& a, const PageSource& src,
+                const pa_decode_plan& plan, void* stream)
+{
+    const pa_decode_desc& d = handle->desc;
+    if (plan.split && (!a.workspace || a.workspace_bytes < size_t(plan.workspace_bytes)))
+        return PA_DECODE_WORKSPACE_TOO_SMALL;
+    if (plan.split && !aligned16(a.workspace))
+        return PA_DECODE_INVALID_ARG;
+    handle->last_plan = plan;
+    handle->has_plan = true;
+    if (a.batch == 0)
+        return PA_DECODE_OK;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int G = d.num_q_heads / d.num_kv_heads;
+    const pa::WorkspaceLayout wl = pa::workspace_layout(d, a.batch, plan.num_partitions);
+    char* ws = static_cast<char*>(a.workspace);
+
+    pa::PartialParams pp;
+    pp.q = a.q;
+    pp.k = a.k_cache;
+    pp.v = a.v_cache;
+    pp.stride_page = a.kv_stride_page;
+    pp.stride_head = a.kv_stride_head;
+    pp.stride_slot = a.kv_stride_slot;
+    pp.page_table = src.page_table;
+    pp.pt_stride = src.pt_stride;
+    pp.context_lens = src.context_lens;
+    pp.page_indptr = src.page_indptr;
+    pp.last_page_len = src.last_page_len;
+    pp.num_q_heads = d.num_q_heads;
+    pp.group = G;
+    pp.partition_size = plan.partition_size;
+    pp.num_partitions = plan.num_partitions;
+    pp.waves_per_partition = plan.waves_per_partition;
+    pp.window = a.sliding_window;
+    pp.scale_log2 = float(double(a.scale) * 1.4426950408889634);
+    pp.split = plan.split;
+    pp.ws_o = plan.split ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
+    pp.ws_m = plan.split ? reinterpret_cast<float*>(ws + wl.m_off) : nullptr;
+    pp.ws_l = plan.split ? reinterpret_cast<float*>(ws + wl.l_off) : nullptr;
+    pp.out = a.out;
+    pp.lse = a.lse;
+
+    const dim3 grid(plan.grid_partial[0], plan.grid_partial[1], plan.grid_partial[2]);
+    const dim3 block(plan.block_partial);
+    const pa::LaunchEvents ev_partial =
+        handle->profiling ? handle->prof_partial.next() : pa::LaunchEvents();
+    hipError_t e = pa::launch_partial(d.dtype, d.head_dim, pa::template_group(G), pp, grid, block,
+                                      pa::partial_lds_bytes(d, plan), s, ev_partial);
+    if (e != hipSuccess) {
+        handle->last_hip_error = int(e);
+        return PA_DECODE_HIP_ERROR;
+    }
+    if (plan.split) {
+        pa::MergeParams mp;
+        mp.num_q_heads = d.num_q_heads;
+        mp.num_partitions = plan.num_partitions;
+        mp.ws_o = pp.ws_o;
+        mp.ws_m = pp.ws_m;
+        mp.ws_l = pp.ws_l;
+        mp.out = a.out;
+        mp.lse = a.lse;
+        const dim3 mgrid(plan.grid_merge[0], plan.grid_merge[1], plan.grid_merge[2]);
+        const pa::LaunchEvents ev_merge =
+            handle->profiling ? handle->prof_merge.next() : pa::LaunchEvents();
+        e = pa::launch_merge(d.dtype, d.head_dim, mp, mgrid, dim3(plan.block_merge), s, ev_merge);
+        if (e != hipSuccess) {
+            handle->last_hip_error = int(e);
+            return PA_DECODE_HIP_ERROR;
+        }
+    }
     return PA_DECODE_OK;
 }
 
@@ -231,80 +377,59 @@ int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* str
         return st;
     pa_decode_plan plan;
     st = pa::make_plan(d, handle->num_cus, handle->waves_per_cu, a.batch, a.max_context_len,
-                       a.sliding_window,
-                       a.partition_size, &plan);
+                       a.sliding_window, a.partition_size, &plan);
     if (st != PA_DECODE_OK)
         return st;
-    if (plan.split && (!a.workspace || a.workspace_bytes < size_t(plan.workspace_bytes)))
-        return PA_DECODE_WORKSPACE_TOO_SMALL;
-    if (plan.split && !aligned16(a.workspace))
+    PageSource src = {a.page_table, a.pt_stride, a.context_lens, nullptr, nullptr};
+    return launch_step(handle, common_args(a), src, plan, stream);
+}
+
+int pa_decode_workspace_size_csr(pa_decode_handle handle, int32_t batch, int32_t nnz_pages,
+                                 int32_t max_context_len, int32_t sliding_window,
+                                 int32_t partition_size, size_t* bytes)
+{
+    if (!handle || !bytes)
         return PA_DECODE_INVALID_ARG;
-    handle->last_plan = plan;
-    handle->has_plan = true;
-    if (a.batch == 0)
-        return PA_DECODE_OK;
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int G = d.num_q_heads / d.num_kv_heads;
-    const pa::WorkspaceLayout wl = pa::workspace_layout(d, a.batch, plan.num_partitions);
-    char* ws = static_cast<char*>(a.workspace);
-
-    pa::PartialParams pp;
-    pp.q = a.q;
-    pp.k = a.k_cache;
-    pp.v = a.v_cache;
-    pp.stride_page = a.kv_stride_page;
-    pp.stride_head = a.kv_stride_head;
-    pp.stride_slot = a.kv_stride_slot;
-    pp.page_table = a.page_table;
-    pp.pt_stride = a.pt_stride;
-    pp.context_lens = a.context_lens;
-    pp.num_q_heads = d.num_q_heads;
-    pp.group = G;
-    pp.partition_size = plan.partition_size;
-    pp.num_partitions = plan.num_partitions;
-    pp.waves_per_partition = plan.waves_per_partition;
-    pp.window = a.sliding_window;
-    pp.scale_log2 = float(double(a.scale) * 1.4426950408889634);
-    pp.split = plan.split;
-    pp.ws_o = plan.split ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
-    pp.ws_m = plan.split ? reinterpret_cast<float*>(ws + wl.m_off) : nullptr;
-    pp.ws_l = plan.split ? reinterpret_cast<float*>(ws + wl.l_off) : nullptr;
-    pp.out = a.out;
-    pp.lse = a.lse;
-
-    const dim3 grid(plan.grid_partial[0], plan.grid_partial[1], plan.grid_partial[2]);
-    const dim3 block(plan.block_partial);
-    const pa::LaunchEvents ev_partial =
-        handle->profiling ? handle->prof_partial.next() : pa::LaunchEvents();
-    hipError_t e = pa::launch_partial(d.dtype, d.head_dim, pa::template_group(G), pp, grid, block,
-                                      pa::partial_lds_bytes(d, plan), s, ev_partial);
-    if (e != hipSuccess) {
-        handle->last_hip_error = int(e);
-        return PA_DECODE_HIP_ERROR;
-    }
-    if (plan.split) {
-        pa::MergeParams mp;
-        mp.context_lens = a.context_lens;
-        mp.num_q_heads = d.num_q_heads;
-        mp.partition_size = plan.partition_size;
-        mp.num_partitions = plan.num_partitions;
-        mp.window = a.sliding_window;
-        mp.ws_o = pp.ws_o;
-        mp.ws_m = pp.ws_m;
-        mp.ws_l = pp.ws_l;
-        mp.out = a.out;
-        mp.lse = a.lse;
-        const dim3 mgrid(plan.grid_merge[0], plan.grid_merge[1], plan.grid_merge[2]);
-        const pa::LaunchEvents ev_merge =
-            handle->profiling ? handle->prof_merge.next() : pa::LaunchEvents();
-        e = pa::launch_merge(d.dtype, d.head_dim, mp, mgrid, dim3(plan.block_merge), s, ev_merge);
-        if (e != hipSuccess) {
-            handle->last_hip_error = int(e);
-            return PA_DECODE_HIP_ERROR;
-        }
-    }
+    pa_decode_plan plan;
+    int st = pa::make_plan_csr(handle->desc, handle->num_cus, handle->waves_per_cu, batch,
+                               nnz_pages, max_context_len, sliding_window, partition_size, &plan,
+                               nullptr);
+    if (st != PA_DECODE_OK)
+        return st;
+    *bytes = size_t(plan.workspace_bytes);
     return PA_DECODE_OK;
+}
+
+int pa_decode_plan_query_csr(const pa_decode_desc* desc, int32_t num_cus, int32_t waves_per_cu,
+                             int32_t batch, int32_t nnz_pages, int32_t max_context_len,
+                             int32_t sliding_window, int32_t partition_size,
+                             pa_decode_plan* plan)
+{
+    if (!desc || !plan)
+        return PA_DECODE_INVALID_ARG;
+    return pa::make_plan_csr(*desc, num_cus, waves_per_cu, batch, nnz_pages, max_context_len,
+                             sliding_window, partition_size, plan, nullptr);
+}
+
+int pa_decode_run_csr(pa_decode_handle handle, const pa_decode_csr_args* args, void* stream)
+{
+    if (!handle || !args)
+        return PA_DECODE_INVALID_ARG;
+    const pa_decode_desc& d = handle->desc;
+    const pa_decode_csr_args& a = *args;
+    int st = check_csr_args(d, a);
+    if (st != PA_DECODE_OK)
+        return st;
+    pa_decode_plan plan;
+    int max_ctx = 0;
+    st = pa::make_plan_csr(d, handle->num_cus, handle->waves_per_cu, a.batch, a.nnz_pages,
+                           a.max_context_len, a.sliding_window, a.partition_size, &plan, &max_ctx);
+    if (st != PA_DECODE_OK)
+        return st;
+    StepArgs c = common_args(a);
+    c.max_context_len = max_ctx;
+    PageSource src = {a.page_indices, 0, nullptr, a.page_indptr, a.last_page_len};
+    return launch_step(handle, c, src, plan, stream);
 }
 
 int pa_decode_last_plan(pa_decode_handle handle, pa_decode_plan* plan)

@@ -332,7 +332,22 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     const int kvh = blockIdx.y, b = blockIdx.z;
     const int Gact = prm.group;
     const int S = prm.partition_size;
-    const int32_t* pt_row = prm.page_table + size_t(b) * prm.pt_stride;
+    // Page-table row and context length of sequence b: dense rows of
+    // pt_stride entries with context_lens, or CSR rows (page_indptr,
+    // last_page_len).  row_len bounds the entries a row may be read at.
+    const int32_t* pt_row;
+    int row_len, n;
+    if (prm.page_indptr) {
+        const int i0 = prm.page_indptr[b], i1 = prm.page_indptr[b + 1];
+        pt_row = prm.page_table + i0;
+        row_len = i1 - i0;
+        const int last = min(max(prm.last_page_len[b], 0), kPage);
+        n = row_len > 0 ? (row_len - 1) * kPage + last : 0;
+    } else {
+        pt_row = prm.page_table + size_t(b) * prm.pt_stride;
+        row_len = prm.pt_stride;
+        n = prm.context_lens[b];
+    }
     const int i16 = lane & 15, grp = lane >> 4;
     const int rho = lane / CH, c = lane % CH;
 
@@ -349,7 +364,7 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     int ids = 0;
     if (prm.window <= 0 && prel < prm.num_partitions) {
         const int pgs = prel * (S / kPage);
-        ids = load_ids(pgs, min(pgs + S / kPage, prm.pt_stride), 0);
+        ids = load_ids(pgs, min(pgs + S / kPage, row_len), 0);
     }
 
     // q as the MFMA B operand, held in VGPRs: column i16 = query head
@@ -366,7 +381,6 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         }
     }
 
-    const int n = prm.context_lens[b];
     const int lo = (prm.window > 0 && n > prm.window) ? n - prm.window : 0;
     const int pabs = lo / S + prel;
     const int t0 = max(pabs * S, lo);

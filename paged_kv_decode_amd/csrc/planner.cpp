@@ -199,6 +199,31 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
     return PA_DECODE_OK;
 }
 
+int make_plan_csr(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
+                  int nnz_pages, int max_context_len, int sliding_window, int partition_size,
+                  pa_decode_plan* plan, int* max_ctx_used)
+{
+    if (!plan || nnz_pages < 0 || batch < 0 || max_context_len < 0 || partition_size < 0)
+        return PA_DECODE_INVALID_ARG;
+    if (batch == 0 && nnz_pages != 0)
+        return PA_DECODE_INVALID_ARG;
+    const int64_t ps = d.page_size > 0 ? d.page_size : kPageSize;
+    int64_t mc = max_context_len;
+    if (mc == 0)
+        mc = std::min<int64_t>(int64_t(nnz_pages) * ps, d.max_context_len);
+    if (max_ctx_used)
+        *max_ctx_used = int(mc);
+    int S = partition_size;
+    if (S == 0 && int64_t(nnz_pages) * ps <= int64_t(batch) * 256) {
+        // Short contexts on average: a single partition covers every context.
+        const int64_t cover = std::max<int64_t>(1, (std::max<int64_t>(mc, 1) + ps - 1) / ps) * ps;
+        if (cover > INT32_MAX)
+            return PA_DECODE_UNSUPPORTED;
+        S = int(cover);
+    }
+    return make_plan(d, num_cus, waves_per_cu, batch, int(mc), sliding_window, S, plan);
+}
+
 size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan)
 {
     const int G = template_group(d.num_q_heads / d.num_kv_heads);

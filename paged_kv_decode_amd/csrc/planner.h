@@ -44,6 +44,15 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
               int max_context_len, int sliding_window, int partition_size,
               pa_decode_plan* plan);
 
+// The plan for a CSR page table (nnz_pages pages in use): the host switch of
+// TVM PR #20426, section "Change" -- with partition_size 0, one partition per
+// (sequence, KV head) when nnz_pages <= batch * 256 / page_size, else the
+// planner's split.  max_context_len 0 stands for nnz_pages * page_size; the
+// bound actually used is returned in *max_ctx_used (may be null).
+int make_plan_csr(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
+                  int nnz_pages, int max_context_len, int sliding_window, int partition_size,
+                  pa_decode_plan* plan, int* max_ctx_used);
+
 // Dynamic LDS bytes of the partial kernel for a plan.
 size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan);
 

@@ -242,3 +242,46 @@ def permute_pages(p: Problem, seed: int) -> Problem:
     v[perm] = p.v_cache
     pt = perm.to(torch.int32)[p.page_table.long()]
     return dataclasses.replace(p, k_cache=k, v_cache=v, page_table=pt)
+
+
+@dataclasses.dataclass
+class CsrTable:
+    """A page table in CSR form: sequence b owns pages
+    indices[indptr[b]:indptr[b+1]] in token order, the last holding
+    last_page_len[b] tokens."""
+    indptr: torch.Tensor         # int32 [B + 1]
+    indices: torch.Tensor        # int32 [nnz_pages]
+    last_page_len: torch.Tensor  # int32 [B]
+
+    @property
+    def nnz_pages(self) -> int:
+        return int(self.indptr[-1].item())
+
+
+def to_csr(p: Problem, page_size: int = 16) -> CsrTable:
+    """The CSR form of a problem's dense page table (rows cut to
+    ceil(n_b / page_size) pages)."""
+    lens = p.context_lens.tolist()
+    counts = [(n + page_size - 1) // page_size for n in lens]
+    indptr = [0]
+    for c in counts:
+        indptr.append(indptr[-1] + c)
+    indices = [int(x) for b, c in enumerate(counts) for x in p.page_table[b, :c].tolist()]
+    last = [n - (c - 1) * page_size if c > 0 else 0 for n, c in zip(lens, counts)]
+    return CsrTable(torch.tensor(indptr, dtype=torch.int32),
+                    torch.tensor(indices, dtype=torch.int32),
+                    torch.tensor(last, dtype=torch.int32))
+
+
+def from_csr(csr: CsrTable, page_size: int = 16):
+    """(page_table [B, max_pages] int32, context_lens [B] int32) of a CSR table."""
+    ip = csr.indptr.tolist()
+    counts = [ip[b + 1] - ip[b] for b in range(len(ip) - 1)]
+    width = max(1, max(counts) if counts else 1)
+    pt = torch.zeros((len(counts), width), dtype=torch.int32)
+    lens = []
+    for b, c in enumerate(counts):
+        pt[b, :c] = csr.indices[ip[b]:ip[b + 1]]
+        last = min(max(int(csr.last_page_len[b]), 0), page_size)
+        lens.append((c - 1) * page_size + last if c > 0 else 0)
+    return pt, torch.tensor(lens, dtype=torch.int32)

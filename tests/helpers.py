@@ -53,6 +53,23 @@ def run_gpu(p: W.Problem, partition_size=None, dev=None):
     return out.cpu(), lse.cpu(), eng.last_plan().as_dict()
 
 
+def run_gpu_csr(p: W.Problem, csr: W.CsrTable, partition_size=None, max_context_len=None):
+    """Run the HIP path from a CSR page table (pa_decode_run_csr); returns
+    (out, lse) on the CPU and the plan."""
+    eng = engine(p)
+    S = p.workload.partition_size if partition_size is None else partition_size
+    q, k, v = p.q.cuda(), p.k_cache.cuda(), p.v_cache.cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    mc = p.max_context_len if max_context_len is None else max_context_len
+    args = eng.make_csr_args(q, k, v, csr.indptr.cuda(), csr.indices.cuda(),
+                             csr.last_page_len.cuda(), csr.nnz_pages, p.scale, out, lse,
+                             max_context_len=mc, sliding_window=p.window, partition_size=S)
+    eng.run_csr_args(args)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu(), eng.last_plan().as_dict()
+
+
 def run_oracle(p: W.Problem):
     return oracle.decode(p.q, p.k_cache, p.v_cache, p.page_table, p.context_lens, p.scale,
                          window=p.window)

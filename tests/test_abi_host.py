@@ -171,3 +171,67 @@ def test_plan_rejects_bad_partition_sizes():
         plan(w, S=24)
     with pytest.raises(B.PaDecodeError):
         plan(w, num_cus=0)
+
+
+# ---- CSR page-table form ------------------------------------------------
+
+def csr_plan(w: W.Workload, batch, nnz, max_ctx=0, S=0, window=0, num_cus=256, waves_per_cu=8):
+    d = B.make_desc(w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype, max_batch=4096,
+                    max_context_len=1 << 20)
+    return B.pa_decode_plan_query_csr(d, num_cus, waves_per_cu, batch, nnz, max_ctx, window, S)
+
+
+@pytest.mark.parametrize("batch,avg_tokens", [(1, 16), (1, 3060), (8, 100), (8, 256), (8, 272),
+                                              (16, 2048), (64, 240), (64, 4096)])
+def test_csr_host_switch_follows_the_page_count(batch, avg_tokens):
+    """TVM PR #20426, section "Change": the sharded path only when
+    nnz_pages > B * 256 / page_size; otherwise one partition per context."""
+    w = W.CONFIGS["llama8b_b16_ragged_f16"]
+    nnz = batch * (-(-avg_tokens // 16))
+    max_ctx = 2 * avg_tokens
+    p = csr_plan(w, batch, nnz, max_ctx=max_ctx)
+    if nnz * 16 <= batch * 256:
+        assert p.split == 0 and p.num_partitions == 1 and p.partition_size >= max_ctx
+        assert p.workspace_bytes == 0
+    else:
+        dense = plan(w, batch=batch, max_ctx=max_ctx, S=0)
+        assert p.as_dict() == dense.as_dict()
+
+
+def test_csr_plan_defaults_and_forced_partitions():
+    w = W.CONFIGS["ctx100k_gqa6_f16"]
+    # forced 512-token partitions over 6250 pages: 196 partitions, as the dense form
+    p = csr_plan(w, 1, 6250, max_ctx=100000, S=512)
+    assert p.partition_size == 512 and p.num_partitions == 196 and p.split == 1
+    # max_context_len 0 stands for nnz_pages * page_size
+    p0 = csr_plan(w, 1, 6250, max_ctx=0, S=512)
+    assert p0.num_partitions == 196
+    # window: partitions cover only the window
+    w4 = W.CONFIGS["d256_window4096_bf16"]
+    pw = csr_plan(w4, 4, 4 * 512, max_ctx=8192, S=512, window=4096)
+    assert pw.num_partitions == 9
+
+
+@pytest.mark.parametrize("batch,nnz", [(1, -1), (0, 3)])
+def test_csr_plan_rejects_bad_counts(batch, nnz):
+    with pytest.raises(B.PaDecodeError):
+        csr_plan(W.CONFIGS["llama1b_ctx3060_f16"], batch, nnz, max_ctx=64)
+
+
+def test_csr_null_arguments_are_rejected():
+    assert lib().pa_decode_run_csr(None, None, None) == B.PA_DECODE_INVALID_ARG
+    n = ctypes.c_size_t()
+    assert lib().pa_decode_workspace_size_csr(None, 1, 1, 16, 0, 0, ctypes.byref(n)) == \
+        B.PA_DECODE_INVALID_ARG
+
+
+def test_csr_conversion_round_trips():
+    for name in W.CONFIG_ORDER:
+        p = W.generate(W.CONFIGS[name])
+        c = W.to_csr(p)
+        pt, lens = W.from_csr(c)
+        assert torch.equal(lens, p.context_lens)
+        for b, n in enumerate(lens.tolist()):
+            k = -(-n // 16)
+            assert torch.equal(pt[b, :k], p.page_table[b, :k])
+        assert c.nnz_pages == sum(-(-n // 16) for n in lens.tolist())
