@@ -140,7 +140,10 @@ def run_oracle_baseline(p: W.Problem, budget_s: float):
 
 
 def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cache,
-                   table="dense"):
+                   table="dense", layers=1):
+    """One step = `layers` decode-attention calls on distinct KV caches
+    (page-permuted copies of the workload's pool, one per layer), launched
+    back to back."""
     w = W.CONFIGS[name]
     S = w.partition_size if partition_size is None else partition_size
     t0 = time.perf_counter()
@@ -155,10 +158,11 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
     kv_bytes = p.kv_bytes()
     if replicas is None:
         pool_bytes = 2 * p.k_cache.numel() * p.k_cache.element_size()
-        R = max(2, math.ceil(4 * CACHE_BYTES / kv_bytes))
-        R = min(R, max(2, int((64 << 30) // pool_bytes)))
+        R = max(2 * layers, math.ceil(4 * CACHE_BYTES / kv_bytes))
+        R = min(R, max(2 * layers, int((64 << 30) // pool_bytes)))
     else:
-        R = replicas
+        R = max(replicas, layers)
+    R = -(-R // layers) * layers   # whole steps of `layers` distinct caches
     reps = Replicas(p, R, eng, S, table)
     log("%s: %d replicas, %.1f MB KV per step" % (name, R, kv_bytes / 1e6))
     stream = torch.cuda.current_stream()
@@ -174,7 +178,8 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
         "replicas disagree"
     plan = eng.last_plan().as_dict()
 
-    for i in range(warmup):
+    L = layers
+    for i in range(warmup * L):
         reps.run(reps.args[i % R], sp)
     torch.cuda.synchronize()
 
@@ -185,7 +190,7 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
         with torch.cuda.stream(cap):
             with torch.cuda.graph(g, stream=cap):
                 cs = torch.cuda.current_stream().cuda_stream
-                for i in range(steps):
+                for i in range(steps * L):
                     reps.run(reps.args[i % R], cs)
         stream.wait_stream(cap)
         g.replay()  # upload / first replay, untimed
@@ -196,7 +201,7 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
     if mode == "graph":
         g.replay()
     else:
-        for i in range(steps):
+        for i in range(steps * L):
             reps.run(reps.args[i % R], sp)
     stop.record(stream)
     torch.cuda.synchronize()
@@ -213,11 +218,12 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
     merge_us = 1e3 * mm / max(mn, 1) if mn else 0.0
 
     res = {
-        "workload": name, "p": p, "plan": plan, "kv_bytes": kv_bytes, "replicas": R,
-        "ms_per_step": ms_per_step, "us_per_step": 1e3 * ms_per_step,
-        "gbps": kv_bytes / (ms_per_step * 1e-3) / 1e9,
+        "workload": name, "p": p, "plan": plan, "kv_bytes": kv_bytes * L, "replicas": R,
+        "layers": L, "ms_per_step": ms_per_step, "us_per_step": 1e3 * ms_per_step,
+        "us_per_layer": 1e3 * ms_per_step / L,
+        "gbps": kv_bytes * L / (ms_per_step * 1e-3) / 1e9,
         "partial_us": partial_us, "merge_us": merge_us,
-        "partial_gbps": kv_bytes / (partial_us * 1e-6) / 1e9,
+        "partial_gbps": kv_bytes / (partial_us * 1e-6) / 1e9, "kv_bytes_per_layer": kv_bytes,
         "gpu_out": outs[0][0].cpu(), "gpu_lse": outs[0][1].cpu(),
     }
     del reps
@@ -263,6 +269,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="decode-attention calls per step, each on its own KV cache (a "
+                         "layer-stacked decode step); the extra workloads keep 1")
     ap.add_argument("--page-table", choices=["dense", "csr"], default="dense",
                     help="page-table form passed to the library (csr: pa_decode_run_csr)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
@@ -299,8 +308,11 @@ def main():
     binding.load_library()
 
     engines = {}
+    if args.layers < 1:
+        ap.error("--layers must be >= 1")
     main_res = bench_workload(args.workload, args.steps, args.warmup, args.replicas,
-                              args.partition_size, args.mode, engines, args.page_table)
+                              args.partition_size, args.mode, engines, args.page_table,
+                              args.layers)
     log("%s: %.2f us/step, %.0f GB/s; partial %.2f us (%.0f GB/s), merge %.2f us" % (
         args.workload, main_res["us_per_step"], main_res["gbps"], main_res["partial_us"],
         main_res["partial_gbps"], main_res["merge_us"]))
@@ -329,9 +341,9 @@ def main():
     if args.cpu_budget > 0:
         p = main_res["p"]
         _, _, reps, el, threads = run_oracle_baseline(p, args.cpu_budget)
-        cpu = {"value": round(main_res["kv_bytes"] * reps / el / 1e9, 4), "unit": "GB/s",
+        cpu = {"value": round(main_res["kv_bytes_per_layer"] * reps / el / 1e9, 4), "unit": "GB/s",
                "cores": threads, "kind": "oracle",
-               "sample": "%d full steps of the %s workload (float64 C oracle, OpenMP), %.1f s"
+               "sample": "%d decode-attention calls (one layer each) of the %s workload (float64 C oracle, OpenMP), %.1f s"
                          % (reps, args.workload, el),
                "us_per_step": round(1e6 * el / reps, 1)}
     dtype_name = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}
@@ -357,7 +369,8 @@ def main():
                    "context_lens": p_lens(main_res["p"]), "page_size": w.page_size,
                    "sliding_window": w.window, "kv_bytes_per_step": main_res["kv_bytes"],
                    "replicas": main_res["replicas"], "mode": args.mode,
-                   "page_table": args.page_table,
+                   "page_table": args.page_table, "layers": args.layers,
+                   "us_per_layer": round(main_res["us_per_layer"], 3),
                    "plan": main_res["plan"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),

@@ -5,6 +5,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "planner.h"
+
 namespace pa {
 
 // Arguments of the partial kernel (one workgroup per (partition, KV head, b)).
@@ -35,6 +37,7 @@ struct PartialParams {
 
 // Arguments of the merge kernel (one workgroup per (query head, b)).
 struct MergeParams {
+    int32_t batch;
     int32_t num_q_heads;
     int32_t num_partitions;
     const float* ws_o;

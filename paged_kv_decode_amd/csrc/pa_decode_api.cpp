@@ -212,6 +212,7 @@ int launch_step(pa_decode_handle handle, const StepArgs& a, const PageSource& sr
     }
     if (plan.split) {
         pa::MergeParams mp;
+        mp.batch = a.batch;
         mp.num_q_heads = d.num_q_heads;
         mp.num_partitions = plan.num_partitions;
         mp.ws_o = pp.ws_o;

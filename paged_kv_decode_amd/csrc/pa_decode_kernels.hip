@@ -760,16 +760,61 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams prm)
     if (prm.lse && dsl == 0 && threadIdx.x == 0) prm.lse[hrow] = (M + log2f(L)) * kLn2;
 }
 
+// Merge kernel for up to PMAX (<= 64) partitions: one wave per (sequence,
+// query head, 64-dim slice of head_dim).  Lane p holds partition p's max and
+// denominator; both phases reduce across the wave with DPP and permlane
+// swaps (no barrier), and every o row the wave needs is loaded before the
+// first reduction (rows past P re-read row P-1 and get weight 0).
+template <int DT, int D, int PMAX>
+__global__ __launch_bounds__(256) void merge_wave_kernel(const MergeParams prm, int units)
+{
+    constexpr int NS = D / 64;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int unit = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x / kWave) +
+                                                    threadIdx.x / kWave);
+    if (unit >= units)
+        return;
+    const int P = prm.num_partitions;
+    const int slice = unit % NS;
+    const size_t hrow = size_t(unit / NS);   // b * Hq + h
+    const float* o = prm.ws_o + hrow * P * D + slice * 64 + lane;
+    float orow[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) orow[p] = o[size_t(min(p, P - 1)) * D];
+    const float mp = lane < P ? prm.ws_m[hrow * P + lane] : -INFINITY;
+    const float lp = lane < P ? prm.ws_l[hrow * P + lane] : 0.f;
+
+    // Phase 1: global max of the partition maxima.
+    const float M = rows4_max(row16_max(mp));
+    if (M == -INFINITY) {
+        // Every partition empty: out = 0, lse = -inf.
+        store_out<DT>(prm.out, hrow * D + slice * 64 + lane, 0.f);
+        if (prm.lse && slice == 0 && lane == 0) prm.lse[hrow] = -INFINITY;
+        return;
+    }
+    // Phase 2: rescale each partition's denominator (rescale_p =
+    // 2^(m_p - M) * l_p), sum them, and weight the partition outputs.
+    const float w = lp > 0.f ? fast_exp2(mp - M) * lp : 0.f;
+    const float L = rows4_sum(row16_sum(w));
+    float a = 0.f;
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p)
+        a = __builtin_fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), p)), orow[p], a);
+    store_out<DT>(prm.out, hrow * D + slice * 64 + lane, a / L);
+    if (prm.lse && slice == 0 && lane == 0) prm.lse[hrow] = (M + log2f(L)) * kLn2;
+}
+
 // Launch through hipExtLaunchKernelGGL so optional start/stop events bracket
 // the kernel itself.
-template <typename K, typename P>
+template <typename K, typename... Args>
 hipError_t launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
-                  LaunchEvents ev, const P& p)
+                  LaunchEvents ev, const Args&... args)
 {
     if (ev.start || ev.stop)
-        hipExtLaunchKernelGGL(kernel, grid, block, uint32_t(lds), stream, ev.start, ev.stop, 0, p);
+        hipExtLaunchKernelGGL(kernel, grid, block, uint32_t(lds), stream, ev.start, ev.stop, 0,
+                              args...);
     else
-        hipLaunchKernelGGL(kernel, grid, block, lds, stream, p);
+        hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
     return hipGetLastError();
 }
 
@@ -867,10 +912,25 @@ int partial_waves_per_cu(int dtype, int head_dim, int group_t, size_t lds)
     return 0;
 }
 
+template <int DT, int D>
+hipError_t launch_merge_t(const MergeParams& p, dim3 grid, dim3 block, hipStream_t stream,
+                          LaunchEvents ev)
+{
+    if (p.num_partitions <= kMergeWaveMaxPartitions) {
+        const int units = p.batch * p.num_q_heads * (D / 64);
+        if (p.num_partitions <= 16)
+            return launch(merge_wave_kernel<DT, D, 16>, grid, block, 0, stream, ev, p, units);
+        if (p.num_partitions <= 32)
+            return launch(merge_wave_kernel<DT, D, 32>, grid, block, 0, stream, ev, p, units);
+        return launch(merge_wave_kernel<DT, D, 64>, grid, block, 0, stream, ev, p, units);
+    }
+    return launch(merge_kernel<DT, D>, grid, block, 0, stream, ev, p);
+}
+
 hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, dim3 grid, dim3 block,
                         hipStream_t stream, LaunchEvents ev)
 {
-#define PA_MERGE(DT, D) return launch(merge_kernel<DT, D>, grid, block, 0, stream, ev, p);
+#define PA_MERGE(DT, D) return launch_merge_t<DT, D>(p, grid, block, stream, ev);
     if (dtype == PA_DTYPE_F32 && head_dim == 64) { PA_MERGE(PA_DTYPE_F32, 64) }
     if (dtype == PA_DTYPE_F16) {
         if (head_dim == 64) { PA_MERGE(PA_DTYPE_F16, 64) }

@@ -187,9 +187,17 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
     p.grid_partial[2] = batch;
     p.block_partial = nw * 64;
     if (split) {
-        p.grid_merge[0] = d.num_q_heads;
-        p.grid_merge[1] = batch;
-        p.grid_merge[2] = d.head_dim / 64;
+        if (P <= kMergeWaveMaxPartitions) {
+            // one wave per (sequence, query head, 64-dim slice), four per workgroup
+            const int64_t units = int64_t(batch) * d.num_q_heads * (d.head_dim / 64);
+            p.grid_merge[0] = int32_t(ceil_div(units, 4));
+            p.grid_merge[1] = 1;
+            p.grid_merge[2] = 1;
+        } else {
+            p.grid_merge[0] = d.num_q_heads;
+            p.grid_merge[1] = batch;
+            p.grid_merge[2] = d.head_dim / 64;
+        }
         p.block_merge = kMergeThreads;
         p.workspace_bytes = int64_t(workspace_layout(d, batch, int(P)).total);
     }

@@ -109,8 +109,12 @@ def test_plan_covers_every_context(name):
             assert p.grid_partial[0] == -(-p.num_partitions // slots)
             assert p.grid_partial[1] == w.num_kv_heads
             assert 64 <= p.block_partial <= 256 and p.block_partial == 64 * p.waves_per_group
-            if p.split:
+            if p.split and p.num_partitions <= 64:
+                units = w.batch * w.num_q_heads * (w.head_dim // 64)   # one wave each
+                assert list(p.grid_merge) == [-(-units // 4), 1, 1]
+            elif p.split:
                 assert list(p.grid_merge) == [w.num_q_heads, w.batch, w.head_dim // 64]
+            if p.split:
                 rows = w.batch * w.num_q_heads * p.num_partitions
                 assert p.workspace_bytes >= rows * (w.head_dim + 2) * 4
             else:

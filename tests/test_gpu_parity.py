@@ -220,3 +220,42 @@ def test_graph_replays_match_eager(name):
         eng.run_args(args)  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(out, eager[0])
+
+
+def test_layer_stacked_step_under_one_graph():
+    """A decode step over L layers (distinct KV caches and queries, one shared
+    page table, as in a model's stack) captured as one graph of L back-to-back
+    calls: every layer's output equals the oracle's on every replay (the
+    pages measure attention time per decode step summed over 16-32 layers,
+    TVM PR #20426, "Measurements")."""
+    base = W.CONFIGS["llama1b_ctx3060_f16"]
+    L = 4
+    layers = [W.generate(dataclasses.replace(base, seed=1000 + l)) for l in range(L)]
+    pt = layers[0].page_table
+    layers = [dataclasses.replace(p, page_table=pt) for p in layers]   # one shared table
+    eng = engine(layers[0])
+    dev = [to_device(p) for p in layers]
+    outs = [torch.empty_like(d.q) for d in dev]
+    lses = [torch.empty(d.q.shape[:2], dtype=torch.float32, device="cuda") for d in dev]
+    args = [eng.make_args(d.q, d.k_cache, d.v_cache, d.page_table, d.context_lens, p.scale, o, ls,
+                          max_context_len=p.max_context_len,
+                          workspace=torch.zeros(1 << 22, dtype=torch.uint8, device="cuda"))
+            for p, d, o, ls in zip(layers, dev, outs, lses)]
+    refs = [run_oracle(p) for p in layers]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for a in args:
+                eng.run_args(a, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for o, ls in zip(outs, lses):
+            o.zero_()
+            ls.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for l in range(L):
+            compare(outs[l].cpu(), lses[l].cpu(), refs[l][0], refs[l][1], base.dtype,
+                    "layer %d replay %d" % (l, rep))
