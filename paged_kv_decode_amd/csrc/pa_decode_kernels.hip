@@ -606,10 +606,51 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     // Denominator of head i16 over the four lane groups.
     l_run = rows4_sum(l_run);
 
-    // Combine the waves of each partition slot in LDS: maximum first, then
-    // the rescaled denominators and outputs.  A wave without blocks holds
-    // max = -inf, denominator 0 and contributes nothing; a slot whose
-    // partition is empty ends with max = -inf.
+    // Result of (query head g of the group, partition p_rel): the partition
+    // state (o normalised, max, denominator) for the merge, or, when one
+    // partition covers the context, out and lse (an empty context gives
+    // out = 0, lse = -inf).
+    auto emit = [&](int g, int p_rel, int dd, float o, float M, float L, bool head_lane) {
+        const size_t h = size_t(b) * prm.num_q_heads + size_t(kvh) * Gact + g;
+        if (prm.split) {
+            const size_t row = h * prm.num_partitions + p_rel;
+            prm.ws_o[row * D + dd] = o;
+            if (head_lane) {
+                prm.ws_m[row] = M;
+                prm.ws_l[row] = L;
+            }
+        } else {
+            store_out<DT>(prm.out, h * D + dd, o);
+            if (head_lane && prm.lse) prm.lse[h] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
+        }
+    };
+
+    if (wpp == 1) {
+        // Every wave owns its partition: write straight from the output
+        // blocks (row 4*grp + r of block db is head 4*grp + r, column
+        // 16*db + i16); the max and denominator of head 4*grp + r sit in
+        // lane 4*grp + r.  No LDS, no barrier.
+        if (prel < prm.num_partitions) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int g = 4 * grp + r;
+                const float M = __shfl(m_run, g);
+                const float L = __shfl(l_run, g);
+                if (g < Gact) {
+                    const float inv = M == -INFINITY ? 0.f : 1.f / L;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        emit(g, prel, 16 * db + i16, acc[db][r] * inv, M, L, db == 0 && i16 == 0);
+                }
+            }
+        }
+        return;
+    }
+
+    // Several waves share each partition: combine them in LDS, maximum
+    // first, then the rescaled denominators and outputs.  A wave without
+    // blocks holds max = -inf, denominator 0 and contributes nothing; a slot
+    // whose partition is empty ends with max = -inf.
     __syncthreads();
     float* cm = smem;               // [nw][GP4]
     float* cl = cm + nw * GP4;      // [nw][GP4]
@@ -629,34 +670,24 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     __syncthreads();
 
     const int nslots = nw / wpp;
-    for (int idx = threadIdx.x; idx < nslots * Gact * D; idx += blockDim.x) {
-        const int sl = idx / (Gact * D), g = (idx / D) % Gact, dd = idx % D;
+    for (int sl = 0; sl < nslots; ++sl) {
         const int p_rel = blockIdx.x * nslots + sl;
-        if (p_rel >= prm.num_partitions) continue;
-        float M = -INFINITY;
-        for (int w = sl * wpp; w < sl * wpp + wpp; ++w) M = fmaxf(M, cm[w * GP4 + g]);
-        float L = 0.f, o = 0.f;
-        if (M != -INFINITY) {
-            for (int w = sl * wpp; w < sl * wpp + wpp; ++w) {
-                const float sc = fast_exp2(cm[w * GP4 + g] - M);
-                L += sc * cl[w * GP4 + g];
-                o += sc * ca[(w * G + g) * D + dd];
+        if (p_rel >= prm.num_partitions)
+            break;
+        for (int e = threadIdx.x; e < Gact * D; e += blockDim.x) {
+            const int g = e / D, dd = e % D;   // D is a power of two
+            float M = -INFINITY;
+            for (int w = sl * wpp; w < sl * wpp + wpp; ++w) M = fmaxf(M, cm[w * GP4 + g]);
+            float L = 0.f, o = 0.f;
+            if (M != -INFINITY) {
+                for (int w = sl * wpp; w < sl * wpp + wpp; ++w) {
+                    const float sc = fast_exp2(cm[w * GP4 + g] - M);
+                    L += sc * cl[w * GP4 + g];
+                    o += sc * ca[(w * G + g) * D + dd];
+                }
+                o = o / L;
             }
-            o = o / L;
-        }
-        const size_t h = size_t(b) * prm.num_q_heads + size_t(kvh) * Gact + g;
-        if (prm.split) {
-            const size_t row = h * prm.num_partitions + p_rel;
-            prm.ws_o[row * D + dd] = o;
-            if (dd == 0) {
-                prm.ws_m[row] = M;
-                prm.ws_l[row] = L;
-            }
-        } else {
-            // One partition covers the context: write the result (an empty
-            // context gives out = 0, lse = -inf).
-            store_out<DT>(prm.out, h * D + dd, o);
-            if (dd == 0 && prm.lse) prm.lse[h] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
+            emit(g, p_rel, dd, o, M, L, dd == 0);
         }
     }
 }
