@@ -445,9 +445,14 @@ def _csv_rows(path):
 
 
 def _short(name):
-    for k in ("partial_kernel", "merge_kernel", "copyBuffer"):
-        if k in name:
-            return k
+    """Kernel family of a trace or counter row (both merge kernels count as
+    the merge)."""
+    if "partial_kernel" in name:
+        return "partial_kernel"
+    if "merge_kernel" in name or "merge_wave_kernel" in name:
+        return "merge_kernel"
+    if "copyBuffer" in name:
+        return "copyBuffer"
     return None
 
 
