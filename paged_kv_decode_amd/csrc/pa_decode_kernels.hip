@@ -92,19 +92,6 @@ __device__ __forceinline__ float row16_sum(float x)
     return x;
 }
 
-// Sum of x over the lanes that share lane % CH (CH = 8, 16, 32 or 64):
-// xor 8 by a DPP rotate within 16-lane rows, xor 16 by ds_swizzle within
-// 32-lane halves, xor 32 by ds_bpermute.
-template <int CH>
-__device__ __forceinline__ float sum_rows(float x)
-{
-    if constexpr (CH <= 8) x += dpp<0x128>(x);
-    if constexpr (CH <= 16)
-        x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
-    if constexpr (CH <= 32) x += __shfl_xor(x, 32);
-    return x;
-}
-
 // Max / sum over the four 16-lane rows of the wave, for each lane % 16:
 // permlane32_swap pairs rows {0,1} with {2,3}, permlane16_swap row 0 with 1
 // and row 2 with 3 (VALU lane swaps, no LDS round trip).
@@ -285,8 +272,10 @@ template <> struct PV<PA_DTYPE_BF16> {
 // prm.waves_per_partition waves; slot j of workgroup x handles partition
 // x * slots + j of KV head blockIdx.y of sequence blockIdx.z.
 // Lane maps (lane = 0..63, i16 = lane % 16, grp = lane / 16):
-//   loads:   K and V alike: lane loads chunk c = lane % CH of token rows
-//            rho = lane / CH, rho + R, ..., rho + R*(KS-1) of a page, so each
+//   loads:   K and V alike: load instruction i of a page reads chunks
+//            64*i .. 64*i + 63 of the page's 16 x CH chunk grid, lane l chunk
+//            x = 64*i + l, i.e. row x / CH, chunk x % CH (for CH a power of
+//            two: chunk c = l % CH of rows l / CH + (64 / CH) * i), so each
 //            load instruction reads whole 128-byte lines; the rows go to
 //            per-wave LDS tiles (16-byte chunks XOR-swizzled by row so that
 //            the reads below are bank-conflict free);
@@ -310,14 +299,16 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     constexpr int EB = Elt<DT>::bytes;
     constexpr int CH = D * EB / 16;   // 16-byte chunks per key row
     constexpr int EPC = 16 / EB;      // elements per chunk
-    constexpr int KS = CH / 4;        // chunks per lane per page (K and V alike)
-    constexpr int R = kWave / CH;     // token rows per load instruction
+    constexpr int KS = CH / 4;        // load instructions per page = MFMA k-steps per page
+    constexpr bool POW2 = (CH & (CH - 1)) == 0;
+    constexpr int R = POW2 ? kWave / CH : 0;  // token rows per load instruction (power of two)
+    constexpr int CHP = POW2 ? CH : CH + 1;   // tile row stride in chunks (odd when padded)
     constexpr int NDB = D / 16;       // 16-column blocks of the output
     constexpr int GP4 = (G + 3) / 4 * 4;
     constexpr int IPV = kWave / NB;   // loop iterations one page-id vector covers
-    constexpr int KT = NB * kPage * CH;  // 16-byte chunks of one block's K (or V) tile
-    static_assert(KS * 4 == CH && R * CH == kWave && R * KS == kPage, "lane map");
-    static_assert(KT % kWave == 0 && (CH == 8 || CH == 16 || CH == 32), "tiles");
+    constexpr int KT = NB * kPage * CHP;  // 16-byte slots of one block's K (or V) tile
+    static_assert(KS * 4 == CH && KS * kWave == kPage * CH, "lane map");
+    static_assert(CH == 8 || CH == 12 || CH == 16 || CH == 32, "tiles");
     static_assert(G <= 16, "one 16-row MFMA block of query heads");
 
     extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -349,7 +340,9 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         n = prm.context_lens[b];
     }
     const int i16 = lane & 15, grp = lane >> 4;
-    const int rho = lane / CH, c = lane % CH;
+    // Load map: row and chunk of instruction i's chunk for this lane.
+    auto lrow = [&](int i) { if constexpr (POW2) return R * i + lane / CH; else return (kWave * i + lane) / CH; };
+    auto lchk = [&](int i) { if constexpr (POW2) return lane % CH; else return (kWave * i + lane) % CH; };
 
     // Page ids of this wave's pages, one per lane: lane j holds the page of
     // block (wi + wpp * (it0 + j / NB)), page j % NB of the partition that
@@ -391,7 +384,6 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         ids = load_ids(pg0, pg1, 0);
 
     const int64_t ss = prm.stride_slot;
-    const int64_t lane_off = int64_t(rho) * ss + int64_t(c) * EPC;
     const char* kbase = static_cast<const char*>(prm.k) + int64_t(kvh) * prm.stride_head * EB;
     const char* vbase = static_cast<const char*>(prm.v) + int64_t(kvh) * prm.stride_head * EB;
 
@@ -405,11 +397,17 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     u32x4* ktile = reinterpret_cast<u32x4*>(smem + wave * 8 * KT);
     u32x4* vtile = ktile + KT;
     // Tile layout (K and V alike): chunk j of tile row r (page r / 16, token
-    // r % 16) sits at r * CH + (j ^ swz(r)); swz permutes within aligned
-    // groups of 8 chunks, so a 128-byte line still lands whole, and the 16
-    // rows one read touches fall in distinct 16-byte bank groups.
+    // r % 16) sits at slot tix(r, j).  Power-of-two rows: r * CH + (j ^
+    // swz(r)), where swz permutes within aligned groups of 8 chunks, so a
+    // 128-byte line still lands whole, and the 16 rows one read touches fall
+    // in distinct 16-byte bank groups.  12-chunk rows (head_dim 96): rows
+    // padded to an odd 13 slots, which spreads 16 consecutive rows over all
+    // 16 bank groups without a swizzle.
     auto swz = [](int r) { return CH >= 16 ? (r & 15) : ((r >> 1) & 7); };
-    const int kswz = swz(i16);
+    auto tix = [&](int r, int j) {
+        if constexpr (POW2) return r * CH + (j ^ swz(r));
+        else return r * CHP + j;
+    };
 
     const int nblk = active ? (pg1 - pg0 + NB - 1) / NB : 0;
     const int nit = nblk > wi ? (nblk - wi + wpp - 1) / wpp : 0;
@@ -424,7 +422,10 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     u32x4 kr[NB][KS], vr[NB][KS];
     int64_t page[NB];
     uint32_t pmask[NB];
-    const uint32_t lane_off32 = uint32_t(lane_off * EB);
+    uint32_t loff[KS];   // byte offset of this lane's chunk of instruction i in a page
+#pragma unroll
+    for (int i = 0; i < KS; ++i)
+        loff[i] = uint32_t((int64_t(lrow(i)) * ss + int64_t(lchk(i)) * EPC) * EB);
     auto fetch_ids = [&](int itn, int it0, int it1) {
         // Page ids of block `itn` into scalar registers (ids holds the blocks
         // it0 .. it0 + IPV - 1).
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
             const char* pb = base + page[nb] * prm.stride_page * EB;
 #pragma unroll
             for (int i = 0; i < KS; ++i)
-                r[nb][i] = load16_stream(pb + ((lane_off32 + uint32_t(R * i * ss * EB)) & pmask[nb]));
+                r[nb][i] = load16_stream(pb + (loff[i] & pmask[nb]));
         }
     };
     // Registers -> swizzled tile; V rows of tokens outside [t0, t1) (or of
@@ -455,14 +456,14 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int i = 0; i < KS; ++i) {
-                const int row = nb * kPage + R * i + rho;
+                const int row = nb * kPage + lrow(i);
                 u32x4 x = r[nb][i];
                 if (zero_invalid) {
-                    const int tok = (pgb + nb) * kPage + R * i + rho;
+                    const int tok = (pgb + nb) * kPage + lrow(i);
                     const u32x4 z = {0u, 0u, 0u, 0u};
                     x = (nb < nbv && tok >= t0 && tok < t1) ? x : z;
                 }
-                tile[row * CH + (c ^ swz(row))] = x;
+                tile[tix(row, lchk(i))] = x;
             }
     };
 
@@ -492,10 +493,9 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             f32x4 d = {0.f, 0.f, 0.f, 0.f};
-            const u32x4* krow = ktile + (nb * kPage + i16) * CH;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                d = Chunk<DT>::mfma(krow[(4 * ks + grp) ^ kswz], qa[ks], d);
+                d = Chunk<DT>::mfma(ktile[tix(nb * kPage + i16, 4 * ks + grp)], qa[ks], d);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tok = (pgb + nb) * kPage + 4 * grp + r;
@@ -549,9 +549,8 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         // 4*(i16%4) .. +3 for the transpose read.
         auto tr_read = [&](int nb, int db) -> s16x4 {
             const int vrow = nb * kPage + 4 * grp + (i16 >> 2);
-            const char* vrow_p = reinterpret_cast<const char*>(vtile + vrow * CH);
             const int j = 2 * db + ((i16 & 3) >> 1);
-            const char* addr = vrow_p + (j ^ swz(vrow)) * 16 + (i16 & 1) * 8;
+            const char* addr = reinterpret_cast<const char*>(vtile + tix(vrow, j)) + (i16 & 1) * 8;
             return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(addr));
         };
         if constexpr (DT == PA_DTYPE_F32) {
@@ -562,12 +561,10 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = nb * kPage + 4 * grp + r;
-                    const float* vr_p = reinterpret_cast<const float*>(vtile + row * CH);
-                    const int rsw = swz(row);
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) {
                         const int col = 16 * db + i16;
-                        const float v = vr_p[((col >> 2) ^ rsw) * 4 + (col & 3)];
+                        const float v = reinterpret_cast<const float*>(vtile + tix(row, col >> 2))[col & 3];
                         acc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(s[nb][r], v, acc[db], 0, 0, 0);
                     }
                 }
@@ -730,7 +727,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams prm)
     const size_t hrow = size_t(b) * prm.num_q_heads + h;
     const float* m = prm.ws_m + hrow * P;
     const float* l = prm.ws_l + hrow * P;
-    const f32x4* o = reinterpret_cast<const f32x4*>(prm.ws_o + hrow * P * D) + dsl * TPR + c4;
+    // Columns dsl*64 + 4*c4 .. +3; the last slice of head_dim 96 has 8
+    // float4 columns, so threads past D read column 0 and store nothing.
+    const bool has_col = dsl * 64 + 4 * c4 < D;
+    const f32x4* o = reinterpret_cast<const f32x4*>(prm.ws_o + hrow * P * D) + (has_col ? dsl * TPR + c4 : 0);
 
     // Rows rg, rg + RG, ... of the first pass, all loads in flight together.
     float mr[RPT], lr[RPT];
@@ -752,7 +752,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams prm)
     const float M = block_reduce(mx, red[0], true);
     if (M == -INFINITY) {
         // Every partition empty: out = 0, lse = -inf.
-        if (rg == 0) {
+        if (rg == 0 && has_col) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) store_out<DT>(prm.out, hrow * D + dsl * 64 + 4 * c4 + e, 0.f);
         }
@@ -780,7 +780,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams prm)
     const float L = block_reduce(c4 == 0 ? tl : 0.f, red[1], false);
     part[threadIdx.x] = a;
     __syncthreads();
-    if (threadIdx.x < TPR) {
+    if (threadIdx.x < TPR && dsl * 64 + 4 * int(threadIdx.x) < D) {
         f32x4 t = part[threadIdx.x];
         for (int r = 1; r < RG; ++r) t += part[r * TPR + threadIdx.x];
         const float inv = 1.f / L;
@@ -799,7 +799,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams prm)
 template <int DT, int D, int PMAX>
 __global__ __launch_bounds__(256) void merge_wave_kernel(const MergeParams prm, int units)
 {
-    constexpr int NS = D / 64;
+    constexpr int NS = (D + 63) / 64;   // 64-column slices (the last may be partial)
     const int lane = threadIdx.x & (kWave - 1);
     const int unit = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x / kWave) +
                                                     threadIdx.x / kWave);
@@ -808,7 +808,9 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(const MergeParams prm, 
     const int P = prm.num_partitions;
     const int slice = unit % NS;
     const size_t hrow = size_t(unit / NS);   // b * Hq + h
-    const float* o = prm.ws_o + hrow * P * D + slice * 64 + lane;
+    const int col = slice * 64 + lane;
+    const bool has_col = col < D;
+    const float* o = prm.ws_o + hrow * P * D + (has_col ? col : 0);
     float orow[PMAX];
 #pragma unroll
     for (int p = 0; p < PMAX; ++p) orow[p] = o[size_t(min(p, P - 1)) * D];
@@ -819,7 +821,7 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(const MergeParams prm, 
     const float M = rows4_max(row16_max(mp));
     if (M == -INFINITY) {
         // Every partition empty: out = 0, lse = -inf.
-        store_out<DT>(prm.out, hrow * D + slice * 64 + lane, 0.f);
+        if (has_col) store_out<DT>(prm.out, hrow * D + col, 0.f);
         if (prm.lse && slice == 0 && lane == 0) prm.lse[hrow] = -INFINITY;
         return;
     }
@@ -831,7 +833,7 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(const MergeParams prm, 
 #pragma unroll
     for (int p = 0; p < PMAX; ++p)
         a = __builtin_fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), p)), orow[p], a);
-    store_out<DT>(prm.out, hrow * D + slice * 64 + lane, a / L);
+    if (has_col) store_out<DT>(prm.out, hrow * D + col, a / L);
     if (prm.lse && slice == 0 && lane == 0) prm.lse[hrow] = (M + log2f(L)) * kLn2;
 }
 
@@ -913,11 +915,13 @@ hipError_t launch_partial(int dtype, int head_dim, int group_t, const PartialPar
     if (dtype == PA_DTYPE_F32 && head_dim == 64) { PA_PARTIAL(PA_DTYPE_F32, 64) }
     if (dtype == PA_DTYPE_F16) {
         if (head_dim == 64) { PA_PARTIAL(PA_DTYPE_F16, 64) }
+        if (head_dim == 96) { PA_PARTIAL(PA_DTYPE_F16, 96) }
         if (head_dim == 128) { PA_PARTIAL(PA_DTYPE_F16, 128) }
         if (head_dim == 256) { PA_PARTIAL(PA_DTYPE_F16, 256) }
     }
     if (dtype == PA_DTYPE_BF16) {
         if (head_dim == 64) { PA_PARTIAL(PA_DTYPE_BF16, 64) }
+        if (head_dim == 96) { PA_PARTIAL(PA_DTYPE_BF16, 96) }
         if (head_dim == 128) { PA_PARTIAL(PA_DTYPE_BF16, 128) }
         if (head_dim == 256) { PA_PARTIAL(PA_DTYPE_BF16, 256) }
     }
@@ -931,11 +935,13 @@ int partial_waves_per_cu(int dtype, int head_dim, int group_t, size_t lds)
     if (dtype == PA_DTYPE_F32 && head_dim == 64) { PA_OCC(PA_DTYPE_F32, 64) }
     if (dtype == PA_DTYPE_F16) {
         if (head_dim == 64) { PA_OCC(PA_DTYPE_F16, 64) }
+        if (head_dim == 96) { PA_OCC(PA_DTYPE_F16, 96) }
         if (head_dim == 128) { PA_OCC(PA_DTYPE_F16, 128) }
         if (head_dim == 256) { PA_OCC(PA_DTYPE_F16, 256) }
     }
     if (dtype == PA_DTYPE_BF16) {
         if (head_dim == 64) { PA_OCC(PA_DTYPE_BF16, 64) }
+        if (head_dim == 96) { PA_OCC(PA_DTYPE_BF16, 96) }
         if (head_dim == 128) { PA_OCC(PA_DTYPE_BF16, 128) }
         if (head_dim == 256) { PA_OCC(PA_DTYPE_BF16, 256) }
     }
@@ -948,7 +954,7 @@ hipError_t launch_merge_t(const MergeParams& p, dim3 grid, dim3 block, hipStream
                           LaunchEvents ev)
 {
     if (p.num_partitions <= kMergeWaveMaxPartitions) {
-        const int units = p.batch * p.num_q_heads * (D / 64);
+        const int units = p.batch * p.num_q_heads * ((D + 63) / 64);
         if (p.num_partitions <= 16)
             return launch(merge_wave_kernel<DT, D, 16>, grid, block, 0, stream, ev, p, units);
         if (p.num_partitions <= 32)
@@ -965,11 +971,13 @@ hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, dim3 grid
     if (dtype == PA_DTYPE_F32 && head_dim == 64) { PA_MERGE(PA_DTYPE_F32, 64) }
     if (dtype == PA_DTYPE_F16) {
         if (head_dim == 64) { PA_MERGE(PA_DTYPE_F16, 64) }
+        if (head_dim == 96) { PA_MERGE(PA_DTYPE_F16, 96) }
         if (head_dim == 128) { PA_MERGE(PA_DTYPE_F16, 128) }
         if (head_dim == 256) { PA_MERGE(PA_DTYPE_F16, 256) }
     }
     if (dtype == PA_DTYPE_BF16) {
         if (head_dim == 64) { PA_MERGE(PA_DTYPE_BF16, 64) }
+        if (head_dim == 96) { PA_MERGE(PA_DTYPE_BF16, 96) }
         if (head_dim == 128) { PA_MERGE(PA_DTYPE_BF16, 128) }
         if (head_dim == 256) { PA_MERGE(PA_DTYPE_BF16, 256) }
     }

@@ -25,6 +25,12 @@ int pages_per_block(int head_dim, int dtype)
     return std::max(1, std::min(4, 512 / row));
 }
 
+int tile_row_slots(int head_dim, int dtype)
+{
+    const int ch = head_dim * dtype_bytes(dtype) / 16;
+    return (ch & (ch - 1)) == 0 ? ch : ch + 1;
+}
+
 int template_group(int G)
 {
     static const int built[] = {1, 2, 4, 6, 8, 16};
@@ -44,7 +50,7 @@ int check_desc(const pa_decode_desc& d)
         return PA_DECODE_UNSUPPORTED;
     if (d.page_size != kPageSize)
         return PA_DECODE_UNSUPPORTED;
-    if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256)
+    if (d.head_dim != 64 && d.head_dim != 96 && d.head_dim != 128 && d.head_dim != 256)
         return PA_DECODE_UNSUPPORTED;
     if (d.dtype == PA_DTYPE_F32 && d.head_dim != 64)
         return PA_DECODE_UNSUPPORTED;
@@ -132,7 +138,7 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
         const int Gt = template_group(G);
         const int gp4 = (Gt + 3) / 4 * 4;
         const int64_t comb = int64_t(2 * gp4 + Gt * d.head_dim) * 4;
-        const int64_t tiles = int64_t(2) * nb * ps * d.head_dim * dtype_bytes(d.dtype);
+        const int64_t tiles = int64_t(2) * nb * ps * 16 * tile_row_slots(d.head_dim, d.dtype);
         const int64_t per_wave = std::max(comb, tiles);
         while (nw > 1 && nw * per_wave > 65536) nw /= 2;
     }
@@ -189,14 +195,14 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
     if (split) {
         if (P <= kMergeWaveMaxPartitions) {
             // one wave per (sequence, query head, 64-dim slice), four per workgroup
-            const int64_t units = int64_t(batch) * d.num_q_heads * (d.head_dim / 64);
+            const int64_t units = int64_t(batch) * d.num_q_heads * ceil_div(d.head_dim, 64);
             p.grid_merge[0] = int32_t(ceil_div(units, 4));
             p.grid_merge[1] = 1;
             p.grid_merge[2] = 1;
         } else {
             p.grid_merge[0] = d.num_q_heads;
             p.grid_merge[1] = batch;
-            p.grid_merge[2] = d.head_dim / 64;
+            p.grid_merge[2] = int32_t(ceil_div(d.head_dim, 64));
         }
         p.block_merge = kMergeThreads;
         p.workspace_bytes = int64_t(workspace_layout(d, batch, int(P)).total);
@@ -238,8 +244,8 @@ size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan)
     const int gp4 = (G + 3) / 4 * 4;
     const int nw = plan.waves_per_group;
     // per wave: the block's K and V tiles (8 KiB each)
-    const size_t ktile = size_t(plan.pages_per_block) * kPageSize * d.head_dim *
-                         dtype_bytes(d.dtype) / sizeof(float);
+    const size_t ktile = size_t(plan.pages_per_block) * kPageSize * 16 *
+                         size_t(tile_row_slots(d.head_dim, d.dtype)) / sizeof(float);
     const size_t loop = size_t(nw) * 2 * ktile;
     const size_t comb = size_t(nw) * size_t(2 * gp4 + G * d.head_dim);
     return std::max(loop, comb) * sizeof(float);

@@ -33,6 +33,10 @@ int dtype_bytes(int dtype);
 // 8 KiB of V per wave, i.e. 512 bytes of one token row times 16 rows.
 int pages_per_block(int head_dim, int dtype);
 
+// 16-byte slots per key row in the kernel's LDS tiles: the row's chunks,
+// plus one when that count is not a power of two (head_dim 96).
+int tile_row_slots(int head_dim, int dtype);
+
 // The instantiated group size that serves an actual GQA group size G
 // (the smallest built one >= G); 0 when G is not supported.
 int template_group(int G);

@@ -45,7 +45,8 @@ def test_status_strings():
 @pytest.mark.parametrize("fields,status", [
     (dict(num_q_heads=0), B.PA_DECODE_INVALID_ARG),
     (dict(num_q_heads=6, num_kv_heads=4), B.PA_DECODE_INVALID_ARG),
-    (dict(head_dim=96), B.PA_DECODE_UNSUPPORTED),
+    (dict(head_dim=80), B.PA_DECODE_UNSUPPORTED),
+    (dict(dtype=B.PA_DTYPE_F32, head_dim=96), B.PA_DECODE_UNSUPPORTED),
     (dict(page_size=32), B.PA_DECODE_UNSUPPORTED),
     (dict(dtype=7), B.PA_DECODE_UNSUPPORTED),
     (dict(dtype=B.PA_DTYPE_F32, head_dim=128), B.PA_DECODE_UNSUPPORTED),
@@ -239,3 +240,24 @@ def test_csr_conversion_round_trips():
             k = -(-n // 16)
             assert torch.equal(pt[b, :k], p.page_table[b, :k])
         assert c.nnz_pages == sum(-(-n // 16) for n in lens.tolist())
+
+
+@pytest.mark.parametrize("dtype", [B.PA_DTYPE_F16, B.PA_DTYPE_BF16])
+def test_head_dim_96_is_planned(dtype):
+    """head_dim 96 (12 chunks of 16 bytes per row, TVM PR #20426, "Tests",
+    lays out D = 96 too): accepted, two pages per block, the merge grid covers
+    a partial 64-column slice, LDS within 64 KiB per workgroup."""
+    d = B.PaDecodeDesc(num_q_heads=32, num_kv_heads=8, head_dim=96, page_size=16, dtype=dtype,
+                       max_batch=64, max_context_len=8192, device=0)
+    h = ctypes.c_void_p()
+    assert lib().pa_decode_create(ctypes.byref(d), ctypes.byref(h)) in (B.PA_DECODE_OK,
+                                                                         B.PA_DECODE_HIP_ERROR)
+    for S, P in ((16, 256), (512, 8)):
+        p = B.pa_decode_plan_query(d, 256, 8, 2, 4096, 0, S)
+        assert p.pages_per_block == 2 and p.num_partitions == P
+        if P <= 64:
+            assert list(p.grid_merge) == [-(-2 * 32 * 2 // 4), 1, 1]
+        else:
+            assert list(p.grid_merge) == [32, 2, 2]
+        rows = 2 * 32 * P
+        assert p.workspace_bytes >= rows * (96 + 2) * 4

@@ -9,8 +9,9 @@ lse (absolute error) with the tolerances in helpers.py.  Covered:
     window; 100,000 tokens GQA-6 cut into 196 partitions of 512) in the
     launch configuration the benchmark times;
   * nine context lengths from 1 to 3060 with a shuffled page table, for
-    head_dim 64 / 128 / 256 (TVM PR #20426, section "Correctness", checks
-    nine lengths in that range with a shuffled table);
+    head_dim 64 / 96 / 128 / 256 (TVM PR #20426, section "Correctness", checks
+    nine lengths in that range with a shuffled table; its "Tests" lay out
+    D = 96 too);
   * forced partition sizes (16 ... 1024 tokens) and the unsplit path;
   * every built group size G in 1..16;
   * NaN in every slot the method must not read (tail slots, keys before the
@@ -51,8 +52,9 @@ def test_workload_full_size(name):
     _check(p, what=name)
 
 
-@pytest.mark.parametrize("D,dtype", [(64, torch.float16), (128, torch.float16),
-                                     (256, torch.bfloat16), (64, torch.float32)])
+@pytest.mark.parametrize("D,dtype", [(64, torch.float16), (96, torch.float16), (128, torch.float16),
+                                     (96, torch.bfloat16), (256, torch.bfloat16),
+                                     (64, torch.float32)])
 def test_nine_context_lengths_shuffled_pages(D, dtype):
     lens = [1, 2, 15, 16, 17, 255, 257, 1000, 3060]
     G = 4
@@ -71,10 +73,21 @@ def test_forced_partition_sizes(S):
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16])
 def test_every_group_size(G):
     Hkv = 2
-    for D, dtype in ((64, torch.float16), (256, torch.bfloat16)):
+    for D, dtype in ((64, torch.float16), (96, torch.bfloat16), (256, torch.bfloat16)):
         w = W.custom(batch=2, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D, dtype=dtype,
                      context_lens=[333, 1200], seed=300 + G)
         _check(W.generate(w), what="G=%d D=%d" % (G, D))
+
+
+@pytest.mark.parametrize("S", [16, 64, 256, 4096])
+def test_head_dim_96_partitions_and_merges(S):
+    """head_dim 96: 12-chunk rows through the padded LDS tiles; S = 16
+    gives more than 64 partitions (workgroup merge with a partial 64-column
+    slice), the others the wave merge or the unsplit path; NaN in every
+    slot the method must not read."""
+    w = W.custom(batch=3, num_q_heads=12, num_kv_heads=4, head_dim=96, dtype=torch.float16,
+                 context_lens=[1, 2000, 777], seed=250)
+    _check(W.generate(w, poison=True, extra_pages=2), S=S, what="D96")
 
 
 @pytest.mark.parametrize("name", W.CONFIG_ORDER[:4])
