@@ -262,7 +262,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="llama1b_ctx3060_f16", choices=W.CONFIG_ORDER)
+    ap.add_argument("--workload", default="llama1b_ctx3060_f16",
+                    choices=W.CONFIG_ORDER + W.EXTRA_ORDER)
     ap.add_argument("--also", default="ctx100k_gqa6_f16,llama8b_b16_ragged_f16,d256_window4096_bf16",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--also-steps", type=int, default=300)

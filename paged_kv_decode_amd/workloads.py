@@ -82,11 +82,21 @@ CONFIGS = {
         name="ctx100k_gqa6_f16", batch=1, num_q_heads=24, num_kv_heads=4, head_dim=256,
         dtype=torch.float16, context_lens=[100000], num_pages=6250, seed=5,
         partition_size=512),
+    # head_dim 96 (not one of the five; measures the 12-chunk-row path)
+    "d96_b16_ragged_f16": Workload(
+        name="d96_b16_ragged_f16", batch=16, num_q_heads=32, num_kv_heads=8, head_dim=96,
+        dtype=torch.float16, context_lens=None, num_pages=4096, seed=6,
+        random_lens=(1, 4096, {0: 1, 1: 4096, 2: 17})),
+    "d96_ctx32k_f16": Workload(
+        name="d96_ctx32k_f16", batch=1, num_q_heads=32, num_kv_heads=8, head_dim=96,
+        dtype=torch.float16, context_lens=[32768], num_pages=2048, seed=7),
 }
 
 # The five workloads in the order they are usually listed.
 CONFIG_ORDER = ["tiny_gqa4_f32", "llama1b_ctx3060_f16", "llama8b_b16_ragged_f16",
                 "d256_window4096_bf16", "ctx100k_gqa6_f16"]
+# Further shapes (head_dim 96), measured but not part of the five.
+EXTRA_ORDER = ["d96_b16_ragged_f16", "d96_ctx32k_f16"]
 
 
 @dataclasses.dataclass
