@@ -7,7 +7,10 @@ The C file holds all of the arithmetic; this module only compiles it with gcc,
 marshals CPU tensors into raw pointers and allocates the float64 outputs.
 The definition it follows is the one stated at the top of ``pa_oracle.c``:
 out = softmax(scale * q K^T) V per query head over the visible keys, walking
-the page table; lse = ln sum exp(scale * q K^T).
+the page table; lse = ln sum exp(scale * q K^T); with rotary_mode 1, q and
+every key are first turned by the rotary embedding (rotate-half pairing,
+theta_i = rope_theta^(-2i/D) / rope_scale, key j at position j, the query at
+position n_b - 1).
 """
 from __future__ import annotations
 
@@ -59,8 +62,9 @@ def _load():
 
 def _declare(lib):
     i32, i64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+    f64 = ctypes.c_double
     problem = [i32, i32, i32, i32, i32, i32, vp, i32, vp, vp, i32, i64, i64, i64,
-               vp, i32, vp, ctypes.c_double, i32]
+               vp, i32, vp, f64, i32, i32, f64, f64]
     lib.pa_oracle_decode.argtypes = problem + [i32, vp, vp]
     lib.pa_oracle_decode.restype = i32
     lib.pa_oracle_decode_split.argtypes = problem + [i32, i32, vp, vp]
@@ -85,7 +89,7 @@ def bf16_to_f64(bits: int) -> float:
     return float(_load().pa_oracle_bf16_to_f64(bits))
 
 
-def _problem_args(q, k_cache, v_cache, page_table, context_lens, scale, window):
+def _problem_args(q, k_cache, v_cache, page_table, context_lens, scale, window, rotary):
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                     ("page_table", page_table), ("context_lens", context_lens)):
         if not isinstance(t, torch.Tensor) or t.device.type != "cpu":
@@ -112,6 +116,8 @@ def _problem_args(q, k_cache, v_cache, page_table, context_lens, scale, window):
             _DTYPE_CODE[k_cache.dtype], k_cache.data_ptr(), v_cache.data_ptr(), num_pages,
             k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), page_table.data_ptr(),
             page_table.stride(0), context_lens.data_ptr(), float(scale), int(window)]
+    mode, theta, rscale = (0, 1.0, 1.0) if rotary is None else (1, float(rotary[0]), float(rotary[1]))
+    args += [mode, theta, rscale]
     keep = (q, k_cache, v_cache, page_table, context_lens)
     return args, keep, (B, Hq, D)
 
@@ -124,13 +130,15 @@ def _outputs(shape):
 
 
 def decode(q, k_cache, v_cache, page_table, context_lens, scale, window=0, threads=0,
-           lib=None):
+           lib=None, rotary=None):
     """Direct f64 decode attention. Returns (out [B,Hq,D], lse [B,Hq]) as float64 numpy.
 
     ``scale`` is used as given (pass float(np.float32(s)) to match a float32 scale).
+    ``rotary``: None (no rotary embedding) or (rope_theta, rope_scale) for
+    rotary_mode 1, each used as given.
     """
     args, keep, shape = _problem_args(q, k_cache, v_cache, page_table, context_lens, scale,
-                                      window)
+                                      window, rotary)
     out, lse = _outputs(shape)
     rc = (lib or _load()).pa_oracle_decode(*args, int(threads), out.ctypes.data,
                                            lse.ctypes.data)
@@ -141,10 +149,10 @@ def decode(q, k_cache, v_cache, page_table, context_lens, scale, window=0, threa
 
 
 def decode_split(q, k_cache, v_cache, page_table, context_lens, scale, partition_size,
-                 window=0, threads=0):
+                 window=0, threads=0, rotary=None):
     """Partitioned f64 decode attention: per-partition states then the LSE merge."""
     args, keep, shape = _problem_args(q, k_cache, v_cache, page_table, context_lens, scale,
-                                      window)
+                                      window, rotary)
     out, lse = _outputs(shape)
     rc = _load().pa_oracle_decode_split(*args, int(partition_size), int(threads),
                                         out.ctypes.data, lse.ctypes.data)

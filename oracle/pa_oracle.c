@@ -22,6 +22,19 @@
  *   - Query head h reads KV head floor(h / G): the same commit page, the
  *     [kv_h, gqa, ...] -> [H, ...] reshape of the scores@V broadcast.
  *
+ * Rotary position embedding (rotary_mode 1), applied to q and to every key
+ * as they are read.  TVM PR #20426, section "Correctness", names the option
+ * (`rotary_mode = 1`) without defining it; the reading taken is the rotary
+ * embedding of the RoFormer paper with the rotate-half pairing that the
+ * pages' models (Llama 3.x, Qwen3, Gemma 2) use:
+ *   for i < D/2, the pair (x[i], x[i + D/2]) of a vector at position pos is
+ *   turned by the angle pos * theta_i, theta_i = rope_theta^(-2i/D) /
+ *   rope_scale:
+ *     x'[i]       = x[i] cos(a) - x[i + D/2] sin(a)
+ *     x'[i + D/2] = x[i + D/2] cos(a) + x[i] sin(a)
+ *   Key j of a sequence sits at position j; the query is the newest token,
+ *   position n_b - 1.  The score uses the rotated q and rotated key.
+ *
  * pa_oracle_decode_split() computes the same result the partitioned way,
  * following the commit page's "Phase 1: Per-partition attention" (per
  * partition: max, exp-sum, normalised weighted V) and "Phase 2:
@@ -37,6 +50,8 @@
  *   - n_b - lo_b == 0 (empty context): out = 0, lse = -inf.
  *   - Partitions are aligned to absolute multiples of the partition size and
  *     clipped to [lo_b, n_b).
+ *   - Rotary positions are the token indices in the sequence (no offset), the
+ *     whole head is rotated, and a sliding window does not renumber them.
  *
  * Layouts:
  *   q            [B, Hq, D] contiguous, dtype q_dtype
@@ -111,6 +126,9 @@ typedef struct {
     const int32_t* context_lens;
     double scale;
     int window;
+    int rotary;        /* 0: none; 1: rotary embedding of q and keys */
+    double rope_theta; /* frequency base */
+    double rope_scale; /* positions are divided by it */
 } problem;
 
 static int check_problem(const problem* p)
@@ -120,6 +138,10 @@ static int check_problem(const problem* p)
     if (p->Hq % p->Hkv != 0)
         return -1;
     if (p->q_dtype < 0 || p->q_dtype > 2 || p->kv_dtype < 0 || p->kv_dtype > 2)
+        return -1;
+    if (p->rotary != 0 && p->rotary != 1)
+        return -1;
+    if (p->rotary && (p->D % 2 != 0 || !(p->rope_theta > 0.0) || !(p->rope_scale > 0.0)))
         return -1;
     for (int b = 0; b < p->B; ++b) {
         int n = p->context_lens[b];
@@ -148,15 +170,40 @@ static int64_t kv_offset(const problem* p, int b, int j, int g)
            (int64_t)slot * p->stride_slot;
 }
 
-/* Scaled score s_j = scale * q[b,h,:] . K[j, g, :]. */
-static double score(const problem* p, int b, int h, int j)
+/* Element d of the vector of D elements at `base + off`, rotated to position
+ * `pos` (rotary embedding, rotate-half pairing; see the header comment). */
+static double rotated_elt(const problem* p, const void* base, int64_t off, int dtype, int d,
+                          double pos)
+{
+    int half = p->D / 2;
+    int i = d < half ? d : d - half;
+    double angle = pos / p->rope_scale * pow(p->rope_theta, -2.0 * i / p->D);
+    double x = load_elt(base, off + d, dtype);
+    if (d < half)
+        return x * cos(angle) - load_elt(base, off + d + half, dtype) * sin(angle);
+    return x * cos(angle) + load_elt(base, off + d - half, dtype) * sin(angle);
+}
+
+/* The query vector of (b, h) as the scores use it: q[b,h,:], rotated to
+ * position n_b - 1 when rotary_mode is 1. */
+static void query_vector(const problem* p, int b, int h, double* qv)
+{
+    int64_t qo = ((int64_t)b * p->Hq + h) * p->D;
+    for (int d = 0; d < p->D; ++d)
+        qv[d] = p->rotary ? rotated_elt(p, p->q, qo, p->q_dtype, d, p->context_lens[b] - 1.0)
+                          : load_elt(p->q, qo + d, p->q_dtype);
+}
+
+/* Scaled score s_j = scale * qv . K[j, g, :], the key rotated to position j
+ * when rotary_mode is 1. */
+static double score(const problem* p, int b, int h, const double* qv, int j)
 {
     int g = h / (p->Hq / p->Hkv);
-    int64_t qo = ((int64_t)b * p->Hq + h) * p->D;
     int64_t ko = kv_offset(p, b, j, g);
     double acc = 0.0;
     for (int d = 0; d < p->D; ++d)
-        acc += load_elt(p->q, qo + d, p->q_dtype) * load_elt(p->k_cache, ko + d, p->kv_dtype);
+        acc += qv[d] * (p->rotary ? rotated_elt(p, p->k_cache, ko, p->kv_dtype, d, (double)j)
+                                  : load_elt(p->k_cache, ko + d, p->kv_dtype));
     return p->scale * acc;
 }
 
@@ -180,9 +227,11 @@ static void one_head(const problem* p, int b, int h, double* out, double* lse)
         return;
     }
     double* s = (double*)malloc(sizeof(double) * (size_t)(n - lo));
+    double* qv = (double*)malloc(sizeof(double) * (size_t)D);
+    query_vector(p, b, h, qv);
     double M = -INFINITY;
     for (int j = lo; j < n; ++j) {
-        s[j - lo] = score(p, b, h, j);
+        s[j - lo] = score(p, b, h, qv, j);
         if (s[j - lo] > M)
             M = s[j - lo];
     }
@@ -198,6 +247,7 @@ static void one_head(const problem* p, int b, int h, double* out, double* lse)
         out[d] /= L;
     *lse = M + log(L);
     free(s);
+    free(qv);
 }
 
 /* Partitioned form of one (b, h): per-partition state (m_p, l_p, o_p), then
@@ -219,6 +269,8 @@ static void one_head_split(const problem* p, int b, int h, int S, double* out, d
     double* m = (double*)malloc(sizeof(double) * (size_t)P);
     double* l = (double*)malloc(sizeof(double) * (size_t)P);
     double* o = (double*)calloc((size_t)P * (size_t)D, sizeof(double));
+    double* qv = (double*)malloc(sizeof(double) * (size_t)D);
+    query_vector(p, b, h, qv);
     /* Phase 1: each partition on its own. */
     for (int pi = 0; pi < P; ++pi) {
         int a = (p0 + pi) * S, e = (p0 + pi + 1) * S;
@@ -226,12 +278,12 @@ static void one_head_split(const problem* p, int b, int h, int S, double* out, d
         if (e > n) e = n;
         double mp = -INFINITY;
         for (int j = a; j < e; ++j) {
-            double sj = score(p, b, h, j);
+            double sj = score(p, b, h, qv, j);
             if (sj > mp) mp = sj;
         }
         double lp = 0.0;
         for (int j = a; j < e; ++j) {
-            double w = exp(score(p, b, h, j) - mp);
+            double w = exp(score(p, b, h, qv, j) - mp);
             lp += w;
             int64_t vo = kv_offset(p, b, j, g);
             for (int d = 0; d < D; ++d)
@@ -258,6 +310,7 @@ static void one_head_split(const problem* p, int b, int h, int S, double* out, d
     free(m);
     free(l);
     free(o);
+    free(qv);
 }
 
 static int run(const problem* p, int S, int threads, double* out, double* lse)
@@ -289,12 +342,14 @@ static int run(const problem* p, int S, int threads, double* out, double* lse)
     int B, int Hq, int Hkv, int D, int page_size, int q_dtype, const void *q, int kv_dtype, \
         const void *k_cache, const void *v_cache, int num_pages, int64_t stride_page,      \
         int64_t stride_head, int64_t stride_slot, const int32_t *page_table, int pt_stride, \
-        const int32_t *context_lens, double scale, int window
+        const int32_t *context_lens, double scale, int window, int rotary_mode,             \
+        double rope_theta, double rope_scale
 
 #define PROBLEM_INIT                                                                      \
     problem p = {B,        Hq,          Hkv,         D,          page_size,    q_dtype, q, \
                  kv_dtype, k_cache,     v_cache,     num_pages,  stride_page,  stride_head, \
-                 stride_slot, page_table, pt_stride, context_lens, scale, window}
+                 stride_slot, page_table, pt_stride, context_lens, scale, window,      \
+                 rotary_mode, rope_theta, rope_scale}
 
 int pa_oracle_decode(PROBLEM_ARGS, int threads, double* out, double* lse)
 {

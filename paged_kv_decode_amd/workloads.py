@@ -52,6 +52,7 @@ class Workload:
     partition_size: int = 0             # 0: the library chooses
     page_size: int = PAGE_SIZE
     random_lens: Optional[tuple] = None  # (lo, hi, forced{index: len}) for drawn lengths
+    rope: Optional[tuple] = None        # (rope_theta, rope_scale): rotary_mode 1; None: off
 
     @property
     def gqa(self) -> int:
@@ -225,7 +226,7 @@ def paginate(w: Workload, q: torch.Tensor, lk: torch.Tensor, lv: torch.Tensor,
 
 def custom(name="custom", batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64,
            dtype=torch.float16, context_lens=(100,), num_pages=0, seed=0, window=0,
-           partition_size=0, page_size=PAGE_SIZE) -> Workload:
+           partition_size=0, page_size=PAGE_SIZE, rope=None) -> Workload:
     """A workload with explicit sizes (used for parity sweeps and edge cases)."""
     lens = list(context_lens)
     assert len(lens) == batch
@@ -233,7 +234,8 @@ def custom(name="custom", batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64,
     return Workload(name=name, batch=batch, num_q_heads=num_q_heads,
                     num_kv_heads=num_kv_heads, head_dim=head_dim, dtype=dtype,
                     context_lens=lens, num_pages=max(num_pages, need, 1), seed=seed,
-                    window=window, partition_size=partition_size, page_size=page_size)
+                    window=window, partition_size=partition_size, page_size=page_size,
+                    rope=rope)
 
 
 def permute_pages(p: Problem, seed: int) -> Problem:
