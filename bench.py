@@ -131,7 +131,7 @@ def run_oracle_baseline(p: W.Problem, budget_s: float):
     out = lse = None
     while True:
         out, lse = oracle.decode(p.q, p.k_cache, p.v_cache, p.page_table, p.context_lens,
-                                 p.scale, window=p.window)
+                                 p.scale, window=p.window, rotary=p.workload.rope)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -149,11 +149,12 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
     t0 = time.perf_counter()
     p = W.generate(w)
     log("%s: generated in %.1fs" % (name, time.perf_counter() - t0))
-    key = (w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype)
+    key = (w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype, w.rope)
     eng = eng_cache.get(key)
     if eng is None:
         eng = binding.PagedDecode(w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype,
-                                  max_batch=max(w.batch, 64), max_context_len=1 << 20)
+                                  max_batch=max(w.batch, 64), max_context_len=1 << 20,
+                                  rope=w.rope)
         eng_cache[key] = eng
     kv_bytes = p.kv_bytes()
     if replicas is None:
@@ -235,7 +236,7 @@ def parity(res):
     import oracle
     p = res["p"]
     ref_out, ref_lse = oracle.decode(p.q, p.k_cache, p.v_cache, p.page_table, p.context_lens,
-                                     p.scale, window=p.window)
+                                     p.scale, window=p.window, rotary=p.workload.rope)
     ref = torch.from_numpy(ref_out).to(p.q.dtype).double()
     rel = ((res["gpu_out"].double() - ref).norm() / ref.norm()).item()
     fin = np.isfinite(ref_lse)

@@ -11,6 +11,15 @@
  *   where n_b = context_lens[b] and lo_b = max(0, n_b - sliding_window) when a
  *   window is set (the window holds the W most recent keys, current one
  *   included), else 0.  n_b - lo_b == 0 gives out = 0, lse = -inf.
+ *   With desc.rotary_mode == 1 the scores use q and K after the rotary
+ *   position embedding (TVM PR #20426, section "Correctness", checks the
+ *   kernel with `rotary_mode = 1`; the pages do not define it further, and
+ *   this library takes the RoFormer rotation with the rotate-half pairing):
+ *   for i < D/2 the pair (x[i], x[i + D/2]) of a vector at position p turns
+ *   by the angle p * theta_i, theta_i = rope_theta^(-2i/D) / rope_scale,
+ *     x'[i] = x[i] cos - x[i + D/2] sin,   x'[i + D/2] = x[i + D/2] cos + x[i] sin,
+ *   key j of sequence b at position j and its query at position n_b - 1.
+ *   The cache holds keys as they were before the embedding.
  *   Passages: output and LSE of paged-KV decode attention with a shuffled page
  *   table, sliding window and batch > 1 -- TVM PR #20426, section
  *   "Correctness"; K/V gathered per page through a block table and the
@@ -65,9 +74,10 @@ enum {
 };
 
 /* Static problem description, fixed at pa_decode_create.
- * Supported: head_dim in {64, 128, 256}; page_size 16; dtype in
+ * Supported: head_dim in {64, 96, 128, 256}; page_size 16; dtype in
  * {F32 (head_dim 64 only), F16, BF16}; G = num_q_heads / num_kv_heads an
- * integer in [1, 16]. */
+ * integer in [1, 16]; rotary_mode 0 or 1 with any of these.  A zeroed tail
+ * (rotary_mode 0) is the plain operation. */
 typedef struct pa_decode_desc {
     int32_t num_q_heads;     /* Hq > 0 */
     int32_t num_kv_heads;    /* Hkv > 0, divides Hq */
@@ -77,6 +87,11 @@ typedef struct pa_decode_desc {
     int32_t max_batch;       /* upper bound of args.batch */
     int32_t max_context_len; /* upper bound of args.max_context_len */
     int32_t device;          /* HIP device ordinal the handle runs on */
+    int32_t rotary_mode;     /* 0: none; 1: rotary embedding of q and keys, applied */
+                             /*   in the kernel as the keys are read (see above)   */
+    float rope_theta;        /* rotary_mode 1: frequency base, finite and > 0     */
+    float rope_scale;        /* rotary_mode 1: positions are divided by it, finite */
+                             /*   and > 0 (1: no scaling)                           */
 } pa_decode_desc;
 
 /* Per-call arguments.  Element strides are in elements of the cache dtype. */
@@ -135,8 +150,10 @@ typedef struct pa_decode_plan {
 typedef struct pa_decode_handle_s* pa_decode_handle;
 
 /* Validate desc, read the device's properties and return a handle.
- * Errors: INVALID_ARG (null pointer, non-positive sizes, Hq % Hkv != 0),
- * UNSUPPORTED (shape or dtype not built), HIP_ERROR (no such device). */
+ * Errors: INVALID_ARG (null pointer, non-positive sizes, Hq % Hkv != 0,
+ * rotary_mode not 0 or 1, rope_theta or rope_scale not finite and > 0 with
+ * rotary_mode 1), UNSUPPORTED (shape or dtype not built), HIP_ERROR (no such
+ * device). */
 int pa_decode_create(const pa_decode_desc* desc, pa_decode_handle* handle);
 
 /* Release the handle (host memory only).  NULL is accepted. */

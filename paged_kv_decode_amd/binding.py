@@ -43,7 +43,9 @@ class PaDecodeDesc(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("max_batch", ctypes.c_int32),
-                ("max_context_len", ctypes.c_int32), ("device", ctypes.c_int32)]
+                ("max_context_len", ctypes.c_int32), ("device", ctypes.c_int32),
+                ("rotary_mode", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("rope_scale", ctypes.c_float)]
 
 
 class PaDecodeArgs(ctypes.Structure):
@@ -241,10 +243,14 @@ def pa_decode_last_hip_error(handle) -> int:
 
 
 def make_desc(num_q_heads, num_kv_heads, head_dim, dtype, max_batch, max_context_len,
-              page_size=16, device=0) -> PaDecodeDesc:
+              page_size=16, device=0, rope=None, rotary_mode=None) -> PaDecodeDesc:
+    """rope: None (rotary_mode 0) or (rope_theta, rope_scale) for rotary_mode 1;
+    rotary_mode overrides the mode (to pass invalid values through in tests)."""
     code = DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    mode = (0 if rope is None else 1) if rotary_mode is None else int(rotary_mode)
+    theta, rscale = (0.0, 0.0) if rope is None else (float(rope[0]), float(rope[1]))
     return PaDecodeDesc(num_q_heads, num_kv_heads, head_dim, page_size, code, max_batch,
-                        max_context_len, device)
+                        max_context_len, device, mode, theta, rscale)
 
 
 class PagedDecode:
@@ -255,9 +261,9 @@ class PagedDecode:
     """
 
     def __init__(self, num_q_heads, num_kv_heads, head_dim, dtype, max_batch,
-                 max_context_len, page_size=16, device=0):
+                 max_context_len, page_size=16, device=0, rope=None):
         self.desc = make_desc(num_q_heads, num_kv_heads, head_dim, dtype, max_batch,
-                              max_context_len, page_size, device)
+                              max_context_len, page_size, device, rope=rope)
         self.dtype = dtype
         self.device = torch.device("cuda", device)
         self.handle = pa_decode_create(self.desc)

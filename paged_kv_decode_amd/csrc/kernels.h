@@ -33,6 +33,9 @@ struct PartialParams {
     float* ws_l;              // [B, Hq, P], denominators
     void* out;                // [B, Hq, D]
     float* lse;               // [B, Hq] or null
+    int32_t rotary;           // 1: rotary embedding of q and keys (rotary_mode 1)
+    double rope_rho;          // rope_theta^(-2/D): theta_i = rope_rho^i / rope_scale
+    double rope_f0;           // 1 / (2 pi rope_scale): theta_0 in revolutions
 };
 
 // Arguments of the merge kernel (one workgroup per (query head, b)).
@@ -61,7 +64,8 @@ hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, dim3 grid
                         hipStream_t stream, LaunchEvents ev);
 
 // Waves of the partial kernel (256-thread workgroups with `lds_bytes` of
-// dynamic LDS) that one compute unit holds at once; 0 when unknown.
-int partial_waves_per_cu(int dtype, int head_dim, int group_t, size_t lds_bytes);
+// dynamic LDS, with or without rotary) that one compute unit holds at once;
+// 0 when unknown.
+int partial_waves_per_cu(int dtype, int head_dim, int group_t, bool rotary, size_t lds_bytes);
 
 }  // namespace pa

@@ -199,6 +199,10 @@ int launch_step(pa_decode_handle handle, const StepArgs& a, const PageSource& sr
     pp.ws_l = plan.split ? reinterpret_cast<float*>(ws + wl.l_off) : nullptr;
     pp.out = a.out;
     pp.lse = a.lse;
+    pp.rotary = d.rotary_mode;
+    // theta_i = rope_theta^(-2i/D) / rope_scale = rope_rho^i / rope_scale
+    pp.rope_rho = d.rotary_mode ? std::pow(double(d.rope_theta), -2.0 / d.head_dim) : 1.0;
+    pp.rope_f0 = d.rotary_mode ? 1.0 / (6.283185307179586477 * double(d.rope_scale)) : 0.0;
 
     const dim3 grid(plan.grid_partial[0], plan.grid_partial[1], plan.grid_partial[2]);
     const dim3 block(plan.block_partial);
@@ -265,6 +269,7 @@ int pa_decode_create(const pa_decode_desc* desc, pa_decode_handle* handle)
         probe.pages_per_block = pa::pages_per_block(desc->head_dim, desc->dtype);
         const int G = desc->num_q_heads / desc->num_kv_heads;
         int w = pa::partial_waves_per_cu(desc->dtype, desc->head_dim, pa::template_group(G),
+                                         desc->rotary_mode == 1,
                                          pa::partial_lds_bytes(*desc, probe));
         h->waves_per_cu = w > 0 ? w : 8;
     }

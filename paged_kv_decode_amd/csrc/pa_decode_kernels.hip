@@ -158,6 +158,94 @@ template <> struct Chunk<PA_DTYPE_F32> {
     }
 };
 
+// sin and cos of 2 pi x for |x| <= 1/2 (x in revolutions, already reduced):
+// the nearest quarter turn q/4 is split off, the rest |a| <= pi/4 goes
+// through the Taylor series of sin (to degree 9) and cos (to degree 10),
+// whose truncation error on |a| <= pi/4 is below 2e-9, and the result is
+// turned by q quarter turns.
+__device__ __forceinline__ void sincos_rev(float x, float* s, float* c)
+{
+    const float q = rintf(4.f * x);
+    const float a = (x - 0.25f * q) * 6.28318530717958648f;
+    const float a2 = a * a;
+    const float sp =
+        a * (1.f + a2 * (-1.f / 6.f + a2 * (1.f / 120.f + a2 * (-1.f / 5040.f + a2 * (1.f / 362880.f)))));
+    const float cp =
+        1.f + a2 * (-0.5f + a2 * (1.f / 24.f + a2 * (-1.f / 720.f +
+                                                     a2 * (1.f / 40320.f + a2 * (-1.f / 3628800.f)))));
+    const int k = int(q) & 3;
+    // sin(a + k pi/2), cos(a + k pi/2)
+    *s = k == 0 ? sp : k == 1 ? cp : k == 2 ? -sp : -cp;
+    *c = k == 0 ? cp : k == 1 ? -sp : k == 2 ? -cp : sp;
+}
+
+// ---- turned (rotary-embedded) key chunks ----
+// widen(): a key chunk as EPC floats.  mfma(): the score MFMA of a turned
+// chunk (floats) against q.  A turned key is no longer a 16-bit value, so
+// f16 / bf16 keys enter as two parts, hi = round(x) and lo = round(x - hi)
+// (about 22 / 18 significant bits together, two MFMAs); rounding the turned
+// key once would move each score by ~2^-12 (f16) or ~2^-9 (bf16) relative.
+template <int DT> struct TurnedKey;
+
+template <> struct TurnedKey<PA_DTYPE_F16> {
+    static constexpr int EPC = 8;
+    __device__ static void widen(u32x4 c, float (&x)[8])
+    {
+        const f16x8 h = __builtin_bit_cast(f16x8, c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (float)h[e];
+    }
+    __device__ static f32x4 mfma(const float (&x)[8], u32x4 q, f32x4 acc)
+    {
+        f16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            hi[e] = (_Float16)x[e];
+            lo[e] = (_Float16)(x[e] - (float)hi[e]);
+        }
+        acc = Chunk<PA_DTYPE_F16>::mfma(__builtin_bit_cast(u32x4, hi), q, acc);
+        return Chunk<PA_DTYPE_F16>::mfma(__builtin_bit_cast(u32x4, lo), q, acc);
+    }
+};
+
+template <> struct TurnedKey<PA_DTYPE_BF16> {
+    static constexpr int EPC = 8;
+    __device__ static void widen(u32x4 c, float (&x)[8])
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = __uint_as_float(c[j] << 16);
+            x[2 * j + 1] = __uint_as_float(c[j] & 0xffff0000u);
+        }
+    }
+    __device__ static f32x4 mfma(const float (&x)[8], u32x4 q, f32x4 acc)
+    {
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            hi[e] = (__bf16)x[e];
+            lo[e] = (__bf16)(x[e] - (float)hi[e]);
+        }
+        acc = Chunk<PA_DTYPE_BF16>::mfma(__builtin_bit_cast(u32x4, hi), q, acc);
+        return Chunk<PA_DTYPE_BF16>::mfma(__builtin_bit_cast(u32x4, lo), q, acc);
+    }
+};
+
+template <> struct TurnedKey<PA_DTYPE_F32> {
+    static constexpr int EPC = 4;
+    __device__ static void widen(u32x4 c, float (&x)[4])
+    {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(c[e]);
+    }
+    __device__ static f32x4 mfma(const float (&x)[4], u32x4 q, f32x4 acc)
+    {
+        const u32x4 a = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                         __float_as_uint(x[3])};
+        return Chunk<PA_DTYPE_F32>::mfma(a, q, acc);
+    }
+};
+
 template <int DT> __device__ __forceinline__ void store_out(void* out, size_t idx, float x);
 template <> __device__ __forceinline__ void store_out<PA_DTYPE_F32>(void* out, size_t idx, float x)
 {
@@ -267,7 +355,7 @@ template <> struct PV<PA_DTYPE_BF16> {
 // ---------------------------------------------------------------------------
 // Partial kernel.
 //   DT: element type; D: head_dim; G: instantiated group size (>= actual);
-//   NB: pages per block.
+//   NB: pages per block; ROT: rotary embedding of q and keys (rotary_mode 1).
 // Workgroup: blockDim.x / 64 waves split into partition slots of
 // prm.waves_per_partition waves; slot j of workgroup x handles partition
 // x * slots + j of KV head blockIdx.y of sequence blockIdx.z.
@@ -290,10 +378,11 @@ template <> struct PV<PA_DTYPE_BF16> {
 // The MFMA operand layout read straight from memory would fetch 16 rows x 64
 // bytes per instruction: twice the L1 tag lookups of whole lines, and with
 // non-temporal loads two L2 requests per line.
-// LDS: [q tile (head_dim 256 only)][per wave: K tile, V tile]; after the main
-// loop the whole area is reused for the combine of the slot's waves.
+// LDS: per wave [K tile, V tile, rotary base table (ROT only)], then (ROT
+// only) the workgroup's rotary offset table; after the main loop the wave
+// areas are reused for the combine of the slot's waves.
 // ---------------------------------------------------------------------------
-template <int DT, int D, int G, int NB>
+template <int DT, int D, int G, int NB, bool ROT>
 __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
 {
     constexpr int EB = Elt<DT>::bytes;
@@ -307,6 +396,9 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     constexpr int GP4 = (G + 3) / 4 * 4;
     constexpr int IPV = kWave / NB;   // loop iterations one page-id vector covers
     constexpr int KT = NB * kPage * CHP;  // 16-byte slots of one block's K (or V) tile
+    constexpr int HD = D / 2;         // rotary frequencies
+    constexpr int NE = ROT ? (NB * HD + kWave - 1) / kWave : 1;  // base-table entries per lane
+    constexpr int WS = 8 * KT + (ROT ? NB * D : 0);  // floats of LDS per wave
     static_assert(KS * 4 == CH && KS * kWave == kPage * CH, "lane map");
     static_assert(CH == 8 || CH == 12 || CH == 16 || CH == 32, "tiles");
     static_assert(G <= 16, "one 16-row MFMA block of query heads");
@@ -394,8 +486,9 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4* ktile = reinterpret_cast<u32x4*>(smem + wave * 8 * KT);
+    u32x4* ktile = reinterpret_cast<u32x4*>(smem + wave * WS);
     u32x4* vtile = ktile + KT;
+    float2* rtab = reinterpret_cast<float2*>(vtile + KT);   // ROT: [NB][HD] (cos, sin)
     // Tile layout (K and V alike): chunk j of tile row r (page r / 16, token
     // r % 16) sits at slot tix(r, j).  Power-of-two rows: r * CH + (j ^
     // swz(r)), where swz permutes within aligned groups of 8 chunks, so a
@@ -407,6 +500,111 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     auto tix = [&](int r, int j) {
         if constexpr (POW2) return r * CH + (j ^ swz(r));
         else return r * CHP + j;
+    };
+
+    // Rotary embedding, relative form.  With q turned to its position m =
+    // n - 1 and key j to position j, the score is q . R((j - m) theta) k_j:
+    // the key turned by its distance to the query, q as it is.  The lane's
+    // token is j = 16 P + i16 for page P, so the angle of frequency i is the
+    // page's base (16 P - m) theta_i plus the in-page offset i16 theta_i:
+    // for each block the wave writes the bases of its pages to rtab (angle
+    // reduced to one turn in f64, then sincos_rev), and the workgroup keeps the (cos, sin)
+    // of every offset t theta_i (t < 16) in otab.  Element e of key chunk c
+    // (c < CH/2) pairs with element e of chunk c + CH/2; both use frequency
+    // i = EPC * c + e.
+    constexpr int TS = D + 4;   // otab row stride in floats (16-byte rows, spread banks)
+    float* otab = smem + nw * WS;
+    double fbase[NE];
+    // Revolutions per position of frequency i: theta_i / (2 pi) =
+    // rope_f0 * rope_rho^i, by binary powering in f64 (i < 128).
+    auto rev_per_pos = [&](int i) {
+        double r = prm.rope_f0, x = prm.rope_rho;
+#pragma unroll
+        for (int bit = 0; bit < 7; ++bit) {
+            r = ((i >> bit) & 1) ? r * x : r;
+            x *= x;
+        }
+        return r;
+    };
+    // Every wave of the workgroup runs this exactly once (it holds the one
+    // barrier that publishes otab).
+    auto rotary_setup = [&]() {
+        for (int e = threadIdx.x; e < kPage * HD; e += blockDim.x) {
+            const int t = e / HD, i = e % HD;
+            double x = t * rev_per_pos(i);
+            x -= rint(x);
+            float sn, c;
+            sincos_rev(float(x), &sn, &c);
+            otab[t * TS + 2 * i] = c;
+            otab[t * TS + 2 * i + 1] = sn;
+        }
+#pragma unroll
+        for (int k = 0; k < NE; ++k) fbase[k] = rev_per_pos((lane + kWave * k) % HD);
+        __syncthreads();
+    };
+    // Bases of the block's pages: entry nb * HD + i of rtab.
+    auto fill_bases = [&](int pgb) {
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+            const int e = lane + kWave * k;
+            if (NE * kWave == NB * HD || e < NB * HD) {
+                const int pos = (pgb + e / HD) * kPage - (n - 1);
+                double x = double(pos) * fbase[k];
+                x -= rint(x);
+                float sn, c;
+                sincos_rev(float(x), &sn, &c);
+                rtab[e] = make_float2(c, sn);
+            }
+        }
+    };
+    // The score MFMAs of page nb with turned keys.
+    auto turned_scores = [&](int nb) {
+        using TK = TurnedKey<DT>;
+        const int row = nb * kPage + i16;
+        const float2* bt = rtab + nb * HD;
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        const float2* ot = reinterpret_cast<const float2*>(otab + i16 * TS);
+        auto angle = [&](int i0, float (&cs)[EPC], float (&sn)[EPC]) {
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+                const float2 bb = bt[i0 + e], oo = ot[i0 + e];
+                cs[e] = bb.x * oo.x - bb.y * oo.y;
+                sn[e] = bb.y * oo.x + bb.x * oo.y;
+            }
+        };
+        if constexpr (KS % 2 == 0) {
+            // Chunk fs (first half) and fs + KS/2 (second half) of the lane.
+#pragma unroll
+            for (int fs = 0; fs < KS / 2; ++fs) {
+                float cs[EPC], sn[EPC], x[EPC], y[EPC], xr[EPC], yr[EPC];
+                angle(EPC * (4 * fs + grp), cs, sn);
+                TK::widen(ktile[tix(row, 4 * fs + grp)], x);
+                TK::widen(ktile[tix(row, 4 * (fs + KS / 2) + grp)], y);
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) {
+                    xr[e] = x[e] * cs[e] - y[e] * sn[e];
+                    yr[e] = y[e] * cs[e] + x[e] * sn[e];
+                }
+                d = TK::mfma(xr, qa[fs], d);
+                d = TK::mfma(yr, qa[fs + KS / 2], d);
+            }
+        } else {
+            // Odd chunk count (head_dim 96): the partner chunk of the other
+            // half is a second LDS read.
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int c = 4 * ks + grp;
+                const bool first = c < CH / 2;
+                float cs[EPC], sn[EPC], x[EPC], y[EPC], xr[EPC];
+                angle(EPC * (first ? c : c - CH / 2), cs, sn);
+                TK::widen(ktile[tix(row, c)], x);
+                TK::widen(ktile[tix(row, first ? c + CH / 2 : c - CH / 2)], y);
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) xr[e] = x[e] * cs[e] + (first ? -y[e] : y[e]) * sn[e];
+                d = TK::mfma(xr, qa[ks], d);
+            }
+        }
+        return d;
     };
 
     const int nblk = active ? (pg1 - pg0 + NB - 1) / NB : 0;
@@ -476,6 +674,8 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         // the V mask (wave-uniform).
         const bool edge = nbv < NB || pgb * kPage < t0 || (pgb + NB) * kPage > t1;
 
+        if constexpr (ROT)
+            fill_bases(pgb);
         stage(ktile, kr, false, pgb, nbv);
         if (edge)
             stage(vtile, vr, true, pgb, nbv);
@@ -493,9 +693,16 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             f32x4 d = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (ROT) {
+                // One page at a time: the turned keys of a page take ~90
+                // VGPRs while they are formed.
+                pin_loads();
+                d = turned_scores(nb);
+            } else {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                d = Chunk<DT>::mfma(ktile[tix(nb * kPage + i16, 4 * ks + grp)], qa[ks], d);
+                for (int ks = 0; ks < KS; ++ks)
+                    d = Chunk<DT>::mfma(ktile[tix(nb * kPage + i16, 4 * ks + grp)], qa[ks], d);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tok = (pgb + nb) * kPage + 4 * grp + r;
@@ -504,6 +711,8 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
             }
         }
 
+        if constexpr (ROT)
+            pin_loads();   // keeps the V reads below out of the score phase
         // Block maximum of head i16: the lane's own 4*NB scores, then the
         // four lane groups.
         float bm = s[0][0];
@@ -587,7 +796,12 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     };
 
     // Outer loop over chunks of IPV blocks (one page-id vector each); the
-    // pipelined inner loop itself issues no load but K/V.
+    // pipelined inner loop itself issues no load but K/V.  A wave without
+    // blocks still takes part in the rotary set-up.
+    if constexpr (ROT) {
+        if (nit == 0)
+            rotary_setup();
+    }
     for (int it0 = 0; it0 < nit; it0 += IPV) {
         const int it1 = min(nit, it0 + IPV);
         if (it0 > 0)
@@ -597,6 +811,11 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         pin_loads();
         issue(vbase, vr);
         pin_loads();
+        if constexpr (ROT) {
+            // While the first block's rows are in flight.
+            if (it0 == 0)
+                rotary_setup();
+        }
         for (int it = it0; it < it1; ++it) step(it, it0, it1);
     }  // chunks of IPV blocks
 
@@ -859,49 +1078,52 @@ constexpr int pages_per_block_t()
 }
 
 template <int DT, int D, int G>
-hipError_t launch_partial_t(const PartialParams& p, dim3 grid, dim3 block, size_t lds,
+hipError_t launch_partial_t(bool rot, const PartialParams& p, dim3 grid, dim3 block, size_t lds,
                             hipStream_t stream, LaunchEvents ev)
 {
-    return launch(partial_kernel<DT, D, G, pages_per_block_t<DT, D>()>, grid, block, lds, stream, ev,
-                  p);
+    constexpr int NB = pages_per_block_t<DT, D>();
+    if (rot)
+        return launch(partial_kernel<DT, D, G, NB, true>, grid, block, lds, stream, ev, p);
+    return launch(partial_kernel<DT, D, G, NB, false>, grid, block, lds, stream, ev, p);
 }
 
 template <int DT, int D, int G>
-int waves_per_cu_t(size_t lds)
+int waves_per_cu_t(bool rot, size_t lds)
 {
+    constexpr int NB = pages_per_block_t<DT, D>();
+    const void* k = rot ? reinterpret_cast<const void*>(partial_kernel<DT, D, G, NB, true>)
+                        : reinterpret_cast<const void*>(partial_kernel<DT, D, G, NB, false>);
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, reinterpret_cast<const void*>(partial_kernel<DT, D, G, pages_per_block_t<DT, D>()>),
-            256, lds) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, 256, lds) != hipSuccess)
         return 0;
     return blocks * 4;
 }
 
 template <int DT, int D>
-int waves_per_cu_g(int group_t, size_t lds)
+int waves_per_cu_g(int group_t, bool rot, size_t lds)
 {
     switch (group_t) {
-    case 1: return waves_per_cu_t<DT, D, 1>(lds);
-    case 2: return waves_per_cu_t<DT, D, 2>(lds);
-    case 4: return waves_per_cu_t<DT, D, 4>(lds);
-    case 6: return waves_per_cu_t<DT, D, 6>(lds);
-    case 8: return waves_per_cu_t<DT, D, 8>(lds);
-    case 16: return waves_per_cu_t<DT, D, 16>(lds);
+    case 1: return waves_per_cu_t<DT, D, 1>(rot, lds);
+    case 2: return waves_per_cu_t<DT, D, 2>(rot, lds);
+    case 4: return waves_per_cu_t<DT, D, 4>(rot, lds);
+    case 6: return waves_per_cu_t<DT, D, 6>(rot, lds);
+    case 8: return waves_per_cu_t<DT, D, 8>(rot, lds);
+    case 16: return waves_per_cu_t<DT, D, 16>(rot, lds);
     default: return 0;
     }
 }
 
 template <int DT, int D>
-hipError_t launch_partial_g(int group_t, const PartialParams& p, dim3 grid, dim3 block, size_t lds,
-                            hipStream_t stream, LaunchEvents ev)
+hipError_t launch_partial_g(int group_t, bool rot, const PartialParams& p, dim3 grid, dim3 block,
+                            size_t lds, hipStream_t stream, LaunchEvents ev)
 {
     switch (group_t) {
-    case 1: return launch_partial_t<DT, D, 1>(p, grid, block, lds, stream, ev);
-    case 2: return launch_partial_t<DT, D, 2>(p, grid, block, lds, stream, ev);
-    case 4: return launch_partial_t<DT, D, 4>(p, grid, block, lds, stream, ev);
-    case 6: return launch_partial_t<DT, D, 6>(p, grid, block, lds, stream, ev);
-    case 8: return launch_partial_t<DT, D, 8>(p, grid, block, lds, stream, ev);
-    case 16: return launch_partial_t<DT, D, 16>(p, grid, block, lds, stream, ev);
+    case 1: return launch_partial_t<DT, D, 1>(rot, p, grid, block, lds, stream, ev);
+    case 2: return launch_partial_t<DT, D, 2>(rot, p, grid, block, lds, stream, ev);
+    case 4: return launch_partial_t<DT, D, 4>(rot, p, grid, block, lds, stream, ev);
+    case 6: return launch_partial_t<DT, D, 6>(rot, p, grid, block, lds, stream, ev);
+    case 8: return launch_partial_t<DT, D, 8>(rot, p, grid, block, lds, stream, ev);
+    case 16: return launch_partial_t<DT, D, 16>(rot, p, grid, block, lds, stream, ev);
     default: return hipErrorInvalidValue;
     }
 }
@@ -911,7 +1133,8 @@ hipError_t launch_partial_g(int group_t, const PartialParams& p, dim3 grid, dim3
 hipError_t launch_partial(int dtype, int head_dim, int group_t, const PartialParams& p, dim3 grid,
                           dim3 block, size_t lds, hipStream_t stream, LaunchEvents ev)
 {
-#define PA_PARTIAL(DT, D) return launch_partial_g<DT, D>(group_t, p, grid, block, lds, stream, ev);
+    const bool rot = p.rotary != 0;
+#define PA_PARTIAL(DT, D) return launch_partial_g<DT, D>(group_t, rot, p, grid, block, lds, stream, ev);
     if (dtype == PA_DTYPE_F32 && head_dim == 64) { PA_PARTIAL(PA_DTYPE_F32, 64) }
     if (dtype == PA_DTYPE_F16) {
         if (head_dim == 64) { PA_PARTIAL(PA_DTYPE_F16, 64) }
@@ -929,9 +1152,9 @@ hipError_t launch_partial(int dtype, int head_dim, int group_t, const PartialPar
     return hipErrorInvalidValue;
 }
 
-int partial_waves_per_cu(int dtype, int head_dim, int group_t, size_t lds)
+int partial_waves_per_cu(int dtype, int head_dim, int group_t, bool rotary, size_t lds)
 {
-#define PA_OCC(DT, D) return waves_per_cu_g<DT, D>(group_t, lds);
+#define PA_OCC(DT, D) return waves_per_cu_g<DT, D>(group_t, rotary, lds);
     if (dtype == PA_DTYPE_F32 && head_dim == 64) { PA_OCC(PA_DTYPE_F32, 64) }
     if (dtype == PA_DTYPE_F16) {
         if (head_dim == 64) { PA_OCC(PA_DTYPE_F16, 64) }

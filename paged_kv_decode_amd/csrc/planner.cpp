@@ -2,6 +2,7 @@
 #include "planner.h"
 
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 
 namespace pa {
@@ -45,6 +46,12 @@ int check_desc(const pa_decode_desc& d)
         d.max_batch < 0 || d.max_context_len < 0 || d.device < 0)
         return PA_DECODE_INVALID_ARG;
     if (d.num_q_heads % d.num_kv_heads != 0)
+        return PA_DECODE_INVALID_ARG;
+    if (d.rotary_mode != 0 && d.rotary_mode != 1)
+        return PA_DECODE_INVALID_ARG;
+    if (d.rotary_mode == 1 &&
+        !(std::isfinite(d.rope_theta) && d.rope_theta > 0.f && std::isfinite(d.rope_scale) &&
+          d.rope_scale > 0.f))
         return PA_DECODE_INVALID_ARG;
     if (d.dtype != PA_DTYPE_F32 && d.dtype != PA_DTYPE_F16 && d.dtype != PA_DTYPE_BF16)
         return PA_DECODE_UNSUPPORTED;
@@ -238,6 +245,20 @@ int make_plan_csr(const pa_decode_desc& d, int num_cus, int waves_per_cu, int ba
     return make_plan(d, num_cus, waves_per_cu, batch, int(mc), sliding_window, S, plan);
 }
 
+int64_t rotary_table_bytes(const pa_decode_desc& d)
+{
+    // [pages per block][head_dim / 2] (cos, sin) pairs of f32
+    return d.rotary_mode == 1
+               ? int64_t(pages_per_block(d.head_dim, d.dtype)) * (d.head_dim / 2) * 8
+               : 0;
+}
+
+int64_t rotary_offset_table_bytes(const pa_decode_desc& d)
+{
+    // [16 in-page offsets][head_dim + 4] f32: (cos, sin) pairs, padded rows
+    return d.rotary_mode == 1 ? int64_t(kPageSize) * (d.head_dim + 4) * 4 : 0;
+}
+
 size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan)
 {
     const int G = template_group(d.num_q_heads / d.num_kv_heads);
@@ -246,7 +267,9 @@ size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan)
     // per wave: the block's K and V tiles (8 KiB each)
     const size_t ktile = size_t(plan.pages_per_block) * kPageSize * 16 *
                          size_t(tile_row_slots(d.head_dim, d.dtype)) / sizeof(float);
-    const size_t loop = size_t(nw) * 2 * ktile;
+    const size_t loop =
+        size_t(nw) * (2 * ktile + size_t(rotary_table_bytes(d)) / sizeof(float)) +
+        size_t(rotary_offset_table_bytes(d)) / sizeof(float);
     const size_t comb = size_t(nw) * size_t(2 * gp4 + G * d.head_dim);
     return std::max(loop, comb) * sizeof(float);
 }

@@ -60,6 +60,14 @@ int make_plan_csr(const pa_decode_desc& d, int num_cus, int waves_per_cu, int ba
                   int nnz_pages, int max_context_len, int sliding_window, int partition_size,
                   pa_decode_plan* plan, int* max_ctx_used);
 
+// LDS bytes of one wave's rotary base table (0 without rotary): the (cos,
+// sin) of every frequency at each page of a block.
+int64_t rotary_table_bytes(const pa_decode_desc& d);
+
+// LDS bytes of a workgroup's rotary offset table (0 without rotary): the
+// (cos, sin) of t theta_i for the 16 in-page offsets t.
+int64_t rotary_offset_table_bytes(const pa_decode_desc& d);
+
 // Dynamic LDS bytes of the partial kernel for a plan.
 size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan);
 

@@ -24,6 +24,9 @@ sequence-sharded nest's measurements, TVM PR #20426 section "Measurements"),
 a Llama-3.1-8B-shaped batch of 16 with ragged lengths, head_dim 256 with a
 sliding window, and a 100,000-token GQA-6 context cut into 512-token
 partitions (the paged_attention_v2_pytorch.py commit page's 100K example).
+The ``*_rope_f16`` variants are the same inputs with the rotary embedding
+switched on (rope_theta 500000, rope_scale 1): the cache holds keys before the
+embedding, which the kernel applies as it reads them.
 """
 from __future__ import annotations
 
@@ -93,11 +96,19 @@ CONFIGS = {
         dtype=torch.float16, context_lens=[32768], num_pages=2048, seed=7),
 }
 
+# Rotary embedding in the kernel (rotary_mode 1; TVM PR #20426, "Correctness"),
+# with the frequency base 500000 of the Llama 3.x models the PR measures.
+for _base in ("llama1b_ctx3060_f16", "llama8b_b16_ragged_f16", "ctx100k_gqa6_f16"):
+    _w = CONFIGS[_base]
+    _name = _base[:-len("_f16")] + "_rope_f16"
+    CONFIGS[_name] = dataclasses.replace(_w, name=_name, rope=(500000.0, 1.0))
+
 # The five workloads in the order they are usually listed.
 CONFIG_ORDER = ["tiny_gqa4_f32", "llama1b_ctx3060_f16", "llama8b_b16_ragged_f16",
                 "d256_window4096_bf16", "ctx100k_gqa6_f16"]
-# Further shapes (head_dim 96), measured but not part of the five.
-EXTRA_ORDER = ["d96_b16_ragged_f16", "d96_ctx32k_f16"]
+# Further shapes (head_dim 96; rotary embedding), measured but not part of the five.
+EXTRA_ORDER = ["d96_b16_ragged_f16", "d96_ctx32k_f16", "llama1b_ctx3060_rope_f16",
+               "llama8b_b16_ragged_rope_f16", "ctx100k_gqa6_rope_f16"]
 
 
 @dataclasses.dataclass

@@ -32,11 +32,11 @@ _HANDLES = {}
 
 def engine(p: W.Problem) -> binding.PagedDecode:
     w = p.workload
-    key = (w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype)
+    key = (w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype, w.rope)
     eng = _HANDLES.get(key)
     if eng is None:
         eng = binding.PagedDecode(w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype,
-                                  max_batch=4096, max_context_len=1 << 20)
+                                  max_batch=4096, max_context_len=1 << 20, rope=w.rope)
         _HANDLES[key] = eng
     return eng
 
@@ -72,7 +72,7 @@ def run_gpu_csr(p: W.Problem, csr: W.CsrTable, partition_size=None, max_context_
 
 def run_oracle(p: W.Problem):
     return oracle.decode(p.q, p.k_cache, p.v_cache, p.page_table, p.context_lens, p.scale,
-                         window=p.window)
+                         window=p.window, rotary=p.workload.rope)
 
 
 def compare(out, lse, ref_out, ref_lse, dtype, what=""):

@@ -52,6 +52,13 @@ def test_status_strings():
     (dict(dtype=B.PA_DTYPE_F32, head_dim=128), B.PA_DECODE_UNSUPPORTED),
     (dict(num_q_heads=32, num_kv_heads=1), B.PA_DECODE_UNSUPPORTED),
     (dict(max_batch=-1), B.PA_DECODE_INVALID_ARG),
+    (dict(rotary_mode=2, rope_theta=1e4, rope_scale=1.0), B.PA_DECODE_INVALID_ARG),
+    (dict(rotary_mode=-1), B.PA_DECODE_INVALID_ARG),
+    (dict(rotary_mode=1, rope_theta=0.0, rope_scale=1.0), B.PA_DECODE_INVALID_ARG),
+    (dict(rotary_mode=1, rope_theta=1e4, rope_scale=0.0), B.PA_DECODE_INVALID_ARG),
+    (dict(rotary_mode=1, rope_theta=-1e4, rope_scale=1.0), B.PA_DECODE_INVALID_ARG),
+    (dict(rotary_mode=1, rope_theta=float("inf"), rope_scale=1.0), B.PA_DECODE_INVALID_ARG),
+    (dict(rotary_mode=1, rope_theta=1e4, rope_scale=float("nan")), B.PA_DECODE_INVALID_ARG),
 ])
 def test_create_rejects_invalid_descriptions(fields, status):
     base = dict(num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=16,
@@ -261,3 +268,29 @@ def test_head_dim_96_is_planned(dtype):
             assert list(p.grid_merge) == [32, 2, 2]
         rows = 2 * 32 * P
         assert p.workspace_bytes >= rows * (96 + 2) * 4
+
+
+@pytest.mark.parametrize("dtype,head_dim", [(B.PA_DTYPE_F32, 64), (B.PA_DTYPE_F16, 64),
+                                            (B.PA_DTYPE_F16, 96), (B.PA_DTYPE_BF16, 128),
+                                            (B.PA_DTYPE_F16, 256)])
+def test_rotary_descriptions_are_planned(dtype, head_dim):
+    """rotary_mode 1 (TVM PR #20426, "Correctness") with a valid base and
+    scale is accepted for every built shape and plans like rotary_mode 0
+    (the embedding changes the kernel's work per key, not the partitioning
+    of the context)."""
+    kw = dict(num_q_heads=32, num_kv_heads=8, head_dim=head_dim, page_size=16, dtype=dtype,
+              max_batch=64, max_context_len=1 << 17, device=0)
+    d0 = B.PaDecodeDesc(**kw)
+    d1 = B.PaDecodeDesc(rotary_mode=1, rope_theta=500000.0, rope_scale=1.0, **kw)
+    h = ctypes.c_void_p()
+    assert lib().pa_decode_create(ctypes.byref(d1), ctypes.byref(h)) in (B.PA_DECODE_OK,
+                                                                          B.PA_DECODE_HIP_ERROR)
+    for batch, ctx, window, S in ((1, 100000, 0, 0), (16, 4096, 0, 0), (4, 8192, 4096, 0),
+                                  (1, 3060, 0, 512), (2, 17, 0, 0)):
+        p0 = B.pa_decode_plan_query(d0, 256, 8, batch, ctx, window, S)
+        p1 = B.pa_decode_plan_query(d1, 256, 8, batch, ctx, window, S)
+        assert p1.partition_size == p0.partition_size
+        assert p1.num_partitions == p0.num_partitions
+        assert p1.split == p0.split
+        assert p1.workspace_bytes == p0.workspace_bytes
+
