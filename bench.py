@@ -265,7 +265,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="llama1b_ctx3060_f16",
                     choices=W.CONFIG_ORDER + W.EXTRA_ORDER)
-    ap.add_argument("--also", default="ctx100k_gqa6_f16,llama8b_b16_ragged_f16,d256_window4096_bf16",
+    ap.add_argument("--also", default="ctx100k_gqa6_f16,llama8b_b16_ragged_f16,d256_window4096_bf16,"
+                    "llama8b_ctx32k_rope_f16",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--also-steps", type=int, default=300)
     ap.add_argument("--replicas", type=int, default=None)
@@ -411,7 +412,7 @@ def copy_probe(nbytes, steps, warmup):
 # Profiling evidence: the rocprofv3 runs behind profiles/ and their summary.
 # ---------------------------------------------------------------------------
 PROFILED = ["llama1b_ctx3060_f16", "llama8b_b16_ragged_f16", "d256_window4096_bf16",
-            "ctx100k_gqa6_f16"]
+            "ctx100k_gqa6_f16", "llama8b_ctx32k_rope_f16", "ctx100k_gqa6_rope_f16"]
 COPY_BYTES = 256 << 20
 
 

@@ -187,6 +187,22 @@ __device__ __forceinline__ void sincos_rev(float x, float* s, float* c)
 // key once would move each score by ~2^-12 (f16) or ~2^-9 (bf16) relative.
 template <int DT> struct TurnedKey;
 
+// f16 pair (x0 - h.lo, x1 - h.hi) for the f16 pair h: two mixed-precision
+// FMAs (f16 source times -1 plus f32 source, rounded to f16 into the low and
+// high halves).  Written out because the compiler turns fma(h, -1, x) into a
+// subtraction, which takes a conversion before and after.
+__device__ __forceinline__ uint32_t minus_f16_pair(uint32_t h, float x0, float x1)
+{
+    // -1 comes from a register: an inline constant in a mixed instruction
+    // is not read as an f32 value.
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, %4, %2 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %1, %4, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(r)
+        : "v"(h), "v"(x0), "v"(x1), "v"(-1.0f));
+    return r;
+}
+
 template <> struct TurnedKey<PA_DTYPE_F16> {
     static constexpr int EPC = 8;
     __device__ static void widen(u32x4 c, float (&x)[8])
@@ -205,6 +221,38 @@ template <> struct TurnedKey<PA_DTYPE_F16> {
         }
         acc = Chunk<PA_DTYPE_F16>::mfma(__builtin_bit_cast(u32x4, hi), q, acc);
         return Chunk<PA_DTYPE_F16>::mfma(__builtin_bit_cast(u32x4, lo), q, acc);
+    }
+    // Turn the pair chunks (x, y) (first / second half of head_dim) by the
+    // angles (cs, sn) and add both score MFMAs.  The f16 keys enter the
+    // mixed-precision FMAs directly; hi is the pair-wise round toward zero of
+    // the turned value and lo = turned - hi (one mixed FMA, rounded to f16).
+    __device__ static f32x4 turn_mfma(u32x4 xc, u32x4 yc, const float (&cs)[8],
+                                      const float (&sn)[8], u32x4 qx, u32x4 qy, f32x4 acc)
+    {
+        typedef __fp16 h2 __attribute__((ext_vector_type(2)));
+        const f16x8 x = __builtin_bit_cast(f16x8, xc), y = __builtin_bit_cast(f16x8, yc);
+        float xr[8], yr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ys = __builtin_fmaf((float)y[e], sn[e], 0.f);
+            const float xs = __builtin_fmaf((float)x[e], sn[e], 0.f);
+            xr[e] = __builtin_fmaf((float)x[e], cs[e], -ys);
+            yr[e] = __builtin_fmaf((float)y[e], cs[e], xs);
+        }
+        u32x4 xh, xl, yh, yl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const h2 a = __builtin_amdgcn_cvt_pkrtz(xr[2 * j], xr[2 * j + 1]);
+            const h2 b = __builtin_amdgcn_cvt_pkrtz(yr[2 * j], yr[2 * j + 1]);
+            xh[j] = __builtin_bit_cast(uint32_t, a);
+            yh[j] = __builtin_bit_cast(uint32_t, b);
+            xl[j] = minus_f16_pair(xh[j], xr[2 * j], xr[2 * j + 1]);
+            yl[j] = minus_f16_pair(yh[j], yr[2 * j], yr[2 * j + 1]);
+        }
+        acc = Chunk<PA_DTYPE_F16>::mfma(xh, qx, acc);
+        acc = Chunk<PA_DTYPE_F16>::mfma(xl, qx, acc);
+        acc = Chunk<PA_DTYPE_F16>::mfma(yh, qy, acc);
+        return Chunk<PA_DTYPE_F16>::mfma(yl, qy, acc);
     }
 };
 
@@ -228,6 +276,38 @@ template <> struct TurnedKey<PA_DTYPE_BF16> {
         }
         acc = Chunk<PA_DTYPE_BF16>::mfma(__builtin_bit_cast(u32x4, hi), q, acc);
         return Chunk<PA_DTYPE_BF16>::mfma(__builtin_bit_cast(u32x4, lo), q, acc);
+    }
+    // As TurnedKey<F16>::turn_mfma.  hi: the pair rounded to nearest bf16
+    // (one packed conversion); lo = turned - hi, exact in f32, truncated to
+    // bf16 (a byte permute keeps the upper halves): |error| < 2^-16 |turned|.
+    __device__ static f32x4 turn_mfma(u32x4 xc, u32x4 yc, const float (&cs)[8],
+                                      const float (&sn)[8], u32x4 qx, u32x4 qy, f32x4 acc)
+    {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        u32x4 xh, xl, yh, yl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float x0 = __uint_as_float(xc[j] << 16), x1 = __uint_as_float(xc[j] & 0xffff0000u);
+            const float y0 = __uint_as_float(yc[j] << 16), y1 = __uint_as_float(yc[j] & 0xffff0000u);
+            const float c0 = cs[2 * j], c1 = cs[2 * j + 1], s0 = sn[2 * j], s1 = sn[2 * j + 1];
+            const f2 xr = {x0 * c0 - y0 * s0, x1 * c1 - y1 * s1};
+            const f2 yr = {y0 * c0 + x0 * s0, y1 * c1 + x1 * s1};
+            const uint32_t hx = __builtin_bit_cast(uint32_t, __builtin_convertvector(xr, b2));
+            const uint32_t hy = __builtin_bit_cast(uint32_t, __builtin_convertvector(yr, b2));
+            xh[j] = hx;
+            yh[j] = hy;
+            const float lx0 = xr[0] - __uint_as_float(hx << 16);
+            const float lx1 = xr[1] - __uint_as_float(hx & 0xffff0000u);
+            const float ly0 = yr[0] - __uint_as_float(hy << 16);
+            const float ly1 = yr[1] - __uint_as_float(hy & 0xffff0000u);
+            xl[j] = __builtin_amdgcn_perm(__float_as_uint(lx1), __float_as_uint(lx0), 0x07060302u);
+            yl[j] = __builtin_amdgcn_perm(__float_as_uint(ly1), __float_as_uint(ly0), 0x07060302u);
+        }
+        acc = Chunk<PA_DTYPE_BF16>::mfma(xh, qx, acc);
+        acc = Chunk<PA_DTYPE_BF16>::mfma(xl, qx, acc);
+        acc = Chunk<PA_DTYPE_BF16>::mfma(yh, qy, acc);
+        return Chunk<PA_DTYPE_BF16>::mfma(yl, qy, acc);
     }
 };
 
@@ -452,6 +532,55 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         ids = load_ids(pgs, min(pgs + S / kPage, row_len), 0);
     }
 
+    // Rotary embedding, relative form.  With q turned to its position m =
+    // n - 1 and key j to position j, the score is q . R((j - m) theta) k_j:
+    // the key turned by its distance to the query, q as it is.  The lane's
+    // token is j = 16 P + i16 for page P, so the angle of frequency i is the
+    // page's base (16 P - m) theta_i plus the in-page offset i16 theta_i:
+    // for each block the wave writes the bases of its pages to rtab (angle
+    // reduced to one turn in f64, then sincos_rev), and the workgroup keeps the (cos, sin)
+    // of every offset t theta_i (t < 16) in otab.  Element e of key chunk c
+    // (c < CH/2) pairs with element e of chunk c + CH/2; both use frequency
+    // i = EPC * c + e.
+    constexpr int TS = D + 4;   // otab row stride in floats (16-byte rows, spread banks)
+    float* otab = smem + nw * WS;
+    double* ftab = reinterpret_cast<double*>(otab + kPage * TS);   // [HD] revolutions per position
+    // Revolutions per position of frequency i: theta_i / (2 pi) =
+    // rope_f0 * rope_rho^i, by binary powering in f64 (i < 128).
+    auto rev_per_pos = [&](int i) {
+        double r = prm.rope_f0, x = prm.rope_rho;
+#pragma unroll
+        for (int bit = 0; bit < 7; ++bit) {
+            r = ((i >> bit) & 1) ? r * x : r;
+            x *= x;
+        }
+        return r;
+    };
+    // Every wave of the workgroup runs this exactly once (it holds the one
+    // barrier that publishes otab), before q is loaded so that the set-up
+    // holds few live registers.
+    auto rotary_setup = [&]() {
+        // Task (i, r): frequency i at offsets t = 4r .. 4r + 3.
+#pragma unroll 1
+        for (int task = threadIdx.x; task < 4 * HD; task += blockDim.x) {
+            const int i = task % HD, r = task / HD;
+            const double f = rev_per_pos(i);
+#pragma unroll 1
+            for (int t = 4 * r; t < 4 * r + 4; ++t) {
+                double x = t * f;
+                x -= rint(x);
+                float sn, c;
+                sincos_rev(float(x), &sn, &c);
+                otab[t * TS + 2 * i] = c;
+                otab[t * TS + 2 * i + 1] = sn;
+            }
+        }
+        for (int i = threadIdx.x; i < HD; i += blockDim.x) ftab[i] = rev_per_pos(i);
+        __syncthreads();
+    };
+    if constexpr (ROT)
+        rotary_setup();
+
     // q as the MFMA B operand, held in VGPRs: column i16 = query head
     // kvh*G + i16 (zero past G), chunk 4*ks + grp of head_dim.
     u32x4 qa[KS];
@@ -502,46 +631,6 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         else return r * CHP + j;
     };
 
-    // Rotary embedding, relative form.  With q turned to its position m =
-    // n - 1 and key j to position j, the score is q . R((j - m) theta) k_j:
-    // the key turned by its distance to the query, q as it is.  The lane's
-    // token is j = 16 P + i16 for page P, so the angle of frequency i is the
-    // page's base (16 P - m) theta_i plus the in-page offset i16 theta_i:
-    // for each block the wave writes the bases of its pages to rtab (angle
-    // reduced to one turn in f64, then sincos_rev), and the workgroup keeps the (cos, sin)
-    // of every offset t theta_i (t < 16) in otab.  Element e of key chunk c
-    // (c < CH/2) pairs with element e of chunk c + CH/2; both use frequency
-    // i = EPC * c + e.
-    constexpr int TS = D + 4;   // otab row stride in floats (16-byte rows, spread banks)
-    float* otab = smem + nw * WS;
-    double fbase[NE];
-    // Revolutions per position of frequency i: theta_i / (2 pi) =
-    // rope_f0 * rope_rho^i, by binary powering in f64 (i < 128).
-    auto rev_per_pos = [&](int i) {
-        double r = prm.rope_f0, x = prm.rope_rho;
-#pragma unroll
-        for (int bit = 0; bit < 7; ++bit) {
-            r = ((i >> bit) & 1) ? r * x : r;
-            x *= x;
-        }
-        return r;
-    };
-    // Every wave of the workgroup runs this exactly once (it holds the one
-    // barrier that publishes otab).
-    auto rotary_setup = [&]() {
-        for (int e = threadIdx.x; e < kPage * HD; e += blockDim.x) {
-            const int t = e / HD, i = e % HD;
-            double x = t * rev_per_pos(i);
-            x -= rint(x);
-            float sn, c;
-            sincos_rev(float(x), &sn, &c);
-            otab[t * TS + 2 * i] = c;
-            otab[t * TS + 2 * i + 1] = sn;
-        }
-#pragma unroll
-        for (int k = 0; k < NE; ++k) fbase[k] = rev_per_pos((lane + kWave * k) % HD);
-        __syncthreads();
-    };
     // Bases of the block's pages: entry nb * HD + i of rtab.
     auto fill_bases = [&](int pgb) {
 #pragma unroll
@@ -549,7 +638,7 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
             const int e = lane + kWave * k;
             if (NE * kWave == NB * HD || e < NB * HD) {
                 const int pos = (pgb + e / HD) * kPage - (n - 1);
-                double x = double(pos) * fbase[k];
+                double x = double(pos) * ftab[e % HD];
                 x -= rint(x);
                 float sn, c;
                 sincos_rev(float(x), &sn, &c);
@@ -576,17 +665,28 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
             // Chunk fs (first half) and fs + KS/2 (second half) of the lane.
 #pragma unroll
             for (int fs = 0; fs < KS / 2; ++fs) {
-                float cs[EPC], sn[EPC], x[EPC], y[EPC], xr[EPC], yr[EPC];
-                angle(EPC * (4 * fs + grp), cs, sn);
-                TK::widen(ktile[tix(row, 4 * fs + grp)], x);
-                TK::widen(ktile[tix(row, 4 * (fs + KS / 2) + grp)], y);
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) {
-                    xr[e] = x[e] * cs[e] - y[e] * sn[e];
-                    yr[e] = y[e] * cs[e] + x[e] * sn[e];
+                if constexpr (KS >= 8) {
+                    if (fs > 0)
+                        pin_loads();   // head_dim 256: one chunk pair at a time
                 }
-                d = TK::mfma(xr, qa[fs], d);
-                d = TK::mfma(yr, qa[fs + KS / 2], d);
+                float cs[EPC], sn[EPC];
+                angle(EPC * (4 * fs + grp), cs, sn);
+                const u32x4 xc = ktile[tix(row, 4 * fs + grp)];
+                const u32x4 yc = ktile[tix(row, 4 * (fs + KS / 2) + grp)];
+                if constexpr (DT != PA_DTYPE_F32) {
+                    d = TK::turn_mfma(xc, yc, cs, sn, qa[fs], qa[fs + KS / 2], d);
+                } else {
+                    float x[EPC], y[EPC], xr[EPC], yr[EPC];
+                    TK::widen(xc, x);
+                    TK::widen(yc, y);
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) {
+                        xr[e] = x[e] * cs[e] - y[e] * sn[e];
+                        yr[e] = y[e] * cs[e] + x[e] * sn[e];
+                    }
+                    d = TK::mfma(xr, qa[fs], d);
+                    d = TK::mfma(yr, qa[fs + KS / 2], d);
+                }
             }
         } else {
             // Odd chunk count (head_dim 96): the partner chunk of the other
@@ -620,10 +720,14 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     u32x4 kr[NB][KS], vr[NB][KS];
     int64_t page[NB];
     uint32_t pmask[NB];
-    uint32_t loff[KS];   // byte offset of this lane's chunk of instruction i in a page
+    // Byte offset of this lane's chunk of load instruction i in a page.  For
+    // power-of-two rows it is loff[0] + i * lstep, with a wave-uniform step
+    // (instruction i reads rows R*i + lane/CH), so one VGPR holds them all.
+    uint32_t loff[POW2 ? 1 : KS];
 #pragma unroll
-    for (int i = 0; i < KS; ++i)
+    for (int i = 0; i < (POW2 ? 1 : KS); ++i)
         loff[i] = uint32_t((int64_t(lrow(i)) * ss + int64_t(lchk(i)) * EPC) * EB);
+    const uint32_t lstep = uint32_t(int64_t(R) * ss * EB);
     auto fetch_ids = [&](int itn, int it0, int it1) {
         // Page ids of block `itn` into scalar registers (ids holds the blocks
         // it0 .. it0 + IPV - 1).
@@ -642,8 +746,13 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         for (int nb = 0; nb < NB; ++nb) {
             const char* pb = base + page[nb] * prm.stride_page * EB;
 #pragma unroll
-            for (int i = 0; i < KS; ++i)
-                r[nb][i] = load16_stream(pb + (loff[i] & pmask[nb]));
+            for (int i = 0; i < KS; ++i) {
+                if constexpr (POW2)
+                    r[nb][i] = load16_stream(pb + ((uint32_t(i) * lstep) & pmask[nb]) +
+                                             (loff[0] & pmask[nb]));
+                else
+                    r[nb][i] = load16_stream(pb + (loff[i] & pmask[nb]));
+            }
         }
     };
     // Registers -> swizzled tile; V rows of tokens outside [t0, t1) (or of
@@ -711,8 +820,6 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
             }
         }
 
-        if constexpr (ROT)
-            pin_loads();   // keeps the V reads below out of the score phase
         // Block maximum of head i16: the lane's own 4*NB scores, then the
         // four lane groups.
         float bm = s[0][0];
@@ -796,12 +903,7 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     };
 
     // Outer loop over chunks of IPV blocks (one page-id vector each); the
-    // pipelined inner loop itself issues no load but K/V.  A wave without
-    // blocks still takes part in the rotary set-up.
-    if constexpr (ROT) {
-        if (nit == 0)
-            rotary_setup();
-    }
+    // pipelined inner loop itself issues no load but K/V.
     for (int it0 = 0; it0 < nit; it0 += IPV) {
         const int it1 = min(nit, it0 + IPV);
         if (it0 > 0)
@@ -811,11 +913,6 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         pin_loads();
         issue(vbase, vr);
         pin_loads();
-        if constexpr (ROT) {
-            // While the first block's rows are in flight.
-            if (it0 == 0)
-                rotary_setup();
-        }
         for (int it = it0; it < it1; ++it) step(it, it0, it1);
     }  // chunks of IPV blocks
 

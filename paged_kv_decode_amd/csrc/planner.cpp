@@ -148,6 +148,12 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
         const int64_t tiles = int64_t(2) * nb * ps * 16 * tile_row_slots(d.head_dim, d.dtype);
         const int64_t per_wave = std::max(comb, tiles);
         while (nw > 1 && nw * per_wave > 65536) nw /= 2;
+        // With rotary, also keep the workgroup (tiles, base tables, offset
+        // table) within half of the compute unit's 160 KiB, so that two
+        // workgroups share a compute unit.
+        while (nw > 1 &&
+               nw * (tiles + rotary_table_bytes(d)) + rotary_offset_table_bytes(d) > 81920)
+            nw /= 2;
     }
     // Waves sharing one partition: the count (1, 2 or 4, at most one per
     // block of the partition) whose grid total is closest to `target` and
@@ -255,8 +261,11 @@ int64_t rotary_table_bytes(const pa_decode_desc& d)
 
 int64_t rotary_offset_table_bytes(const pa_decode_desc& d)
 {
-    // [16 in-page offsets][head_dim + 4] f32: (cos, sin) pairs, padded rows
-    return d.rotary_mode == 1 ? int64_t(kPageSize) * (d.head_dim + 4) * 4 : 0;
+    // [16 in-page offsets][head_dim + 4] f32: (cos, sin) pairs, padded rows;
+    // then [head_dim / 2] f64 revolutions per position
+    return d.rotary_mode == 1
+               ? int64_t(kPageSize) * (d.head_dim + 4) * 4 + int64_t(d.head_dim / 2) * 8
+               : 0;
 }
 
 size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan)

@@ -96,9 +96,15 @@ CONFIGS = {
         dtype=torch.float16, context_lens=[32768], num_pages=2048, seed=7),
 }
 
+# head_dim 128 at one long context (Llama-3.1-8B heads, 32768 tokens).
+CONFIGS["llama8b_ctx32k_f16"] = Workload(
+    name="llama8b_ctx32k_f16", batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128,
+    dtype=torch.float16, context_lens=[32768], num_pages=2048, seed=8)
+
 # Rotary embedding in the kernel (rotary_mode 1; TVM PR #20426, "Correctness"),
 # with the frequency base 500000 of the Llama 3.x models the PR measures.
-for _base in ("llama1b_ctx3060_f16", "llama8b_b16_ragged_f16", "ctx100k_gqa6_f16"):
+for _base in ("llama1b_ctx3060_f16", "llama8b_b16_ragged_f16", "ctx100k_gqa6_f16",
+              "llama8b_ctx32k_f16"):
     _w = CONFIGS[_base]
     _name = _base[:-len("_f16")] + "_rope_f16"
     CONFIGS[_name] = dataclasses.replace(_w, name=_name, rope=(500000.0, 1.0))
@@ -107,8 +113,9 @@ for _base in ("llama1b_ctx3060_f16", "llama8b_b16_ragged_f16", "ctx100k_gqa6_f16
 CONFIG_ORDER = ["tiny_gqa4_f32", "llama1b_ctx3060_f16", "llama8b_b16_ragged_f16",
                 "d256_window4096_bf16", "ctx100k_gqa6_f16"]
 # Further shapes (head_dim 96; rotary embedding), measured but not part of the five.
-EXTRA_ORDER = ["d96_b16_ragged_f16", "d96_ctx32k_f16", "llama1b_ctx3060_rope_f16",
-               "llama8b_b16_ragged_rope_f16", "ctx100k_gqa6_rope_f16"]
+EXTRA_ORDER = ["d96_b16_ragged_f16", "d96_ctx32k_f16", "llama8b_ctx32k_f16",
+               "llama1b_ctx3060_rope_f16", "llama8b_b16_ragged_rope_f16",
+               "ctx100k_gqa6_rope_f16", "llama8b_ctx32k_rope_f16"]
 
 
 @dataclasses.dataclass
