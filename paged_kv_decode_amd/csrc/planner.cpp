@@ -108,8 +108,14 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
     // Waves the grid aims for: about four per compute unit (one per SIMD),
     // never more than the device holds at once.  Measured on MI355X, fewer
     // waves with more pages each stream KV faster than more, shorter waves.
+    // With rotary and a batch, two waves per SIMD: a rotary block costs
+    // about twice the instructions, so the waves of the longest sequences
+    // set the time, and smaller partitions spread them (measured on MI355X:
+    // batch 16 with lengths up to 4096, 38.7 us against 44.5; one sequence
+    // gains nothing, its partitions are all full).
     const int64_t capacity = int64_t(num_cus) * waves_per_cu;
-    const int64_t target = std::min<int64_t>(capacity, int64_t(num_cus) * 4);
+    const int per_cu = (d.rotary_mode == 1 && batch > 1) ? 8 : 4;
+    const int64_t target = std::min<int64_t>(capacity, int64_t(num_cus) * per_cu);
 
     int64_t S;
     if (partition_size > 0) {

@@ -201,7 +201,8 @@ def test_repeated_calls_reuse_the_workspace():
         assert torch.equal(o, base[0][1]) and torch.equal(l, base[0][2])
 
 
-@pytest.mark.parametrize("name", ["llama1b_ctx3060_f16", "ctx100k_gqa6_f16"])
+@pytest.mark.parametrize("name", ["llama1b_ctx3060_f16", "ctx100k_gqa6_f16",
+                                  "llama1b_ctx3060_rope_f16", "llama8b_b16_ragged_rope_f16"])
 def test_graph_replays_match_eager(name):
     """Captured steps replayed several times, with eager work and syncs between
     replays, give the eager result every time."""

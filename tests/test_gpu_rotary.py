@@ -137,3 +137,20 @@ def test_rotary_changes_the_kernel_result():
     p0 = dataclasses.replace(p, workload=dataclasses.replace(w, rope=None))
     b_out, b_lse, _ = run_gpu(p0)
     assert float((a_lse - b_lse).abs().max()) > 1e-2
+
+
+def test_rotary_token_major_cache_layout():
+    """[num_pages, page_size, Hkv, D] storage (slot stride Hkv * D): the key
+    rows reach the turn through the same tiles."""
+    w = W.custom(batch=2, num_q_heads=16, num_kv_heads=4, head_dim=128, dtype=torch.bfloat16,
+                 context_lens=[999, 1500], seed=490, rope=(500000.0, 1.0))
+    p = W.generate(w)
+    k = p.k_cache.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    v = p.v_cache.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    assert k.stride(2) == 4 * 128
+    p2 = dataclasses.replace(p, k_cache=k, v_cache=v)
+    ref_out, ref_lse = run_oracle(p)
+    for S in (0, 64):
+        out, lse, _ = run_gpu(p2, partition_size=S)
+        compare(out, lse, ref_out, ref_lse, w.dtype, what="rope token-major S=%d" % S)
+
