@@ -181,7 +181,12 @@ int pa_decode_last_plan(pa_decode_handle handle, pa_decode_plan* plan);
 /* Plan without a handle or device (pure host): the same planner that
  * pa_decode_run uses, for a given compute-unit count and number of
  * partial-kernel waves a compute unit holds at once (pa_decode_run uses the
- * device's values; the plan of a run reports them). */
+ * device's values; the plan of a run reports them).
+ * Tuning hooks (every planner call reads them): the environment variables
+ * PA_DECODE_WAVES_PER_PARTITION and PA_DECODE_WAVES_PER_GROUP, when set to
+ * 1, 2 or 4, override the plan's waves_per_partition / waves_per_group (other
+ * values are ignored).  They change the work split only, never the result's
+ * definition or the workspace size. */
 int pa_decode_plan_query(const pa_decode_desc* desc, int32_t num_cus, int32_t waves_per_cu,
                          int32_t batch, int32_t max_context_len, int32_t sliding_window,
                          int32_t partition_size, pa_decode_plan* plan);
