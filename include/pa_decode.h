@@ -66,6 +66,16 @@ enum {
     PA_DECODE_HIP_ERROR = -4,           /* a HIP call failed; see pa_decode_last_hip_error */
 };
 
+/* Bits of the device-side contract check (pa_decode_debug_status).  The
+ * kernel never takes an address from a value that breaks the contract: it
+ * clamps the value and, with desc.debug_checks, reports it. */
+enum {
+    PA_DECODE_VIOLATION_PAGE = 1,   /* a page id read is outside [0, num_pages): page 0 used */
+    PA_DECODE_VIOLATION_LENGTH = 2, /* a context length is < 0 or > max_context_len: clamped */
+    PA_DECODE_VIOLATION_ROW = 4,    /* CSR: indptr[b] < 0, indptr[b+1] < indptr[b] or */
+                                    /*   > nnz_pages: the row is clamped into [0, nnz_pages] */
+};
+
 /* Element types of q, the K/V caches and out (all three share one type). */
 enum {
     PA_DTYPE_F32 = 0,
@@ -86,12 +96,16 @@ typedef struct pa_decode_desc {
     int32_t dtype;           /* PA_DTYPE_* of q, k/v cache and out */
     int32_t max_batch;       /* upper bound of args.batch */
     int32_t max_context_len; /* upper bound of args.max_context_len */
-    int32_t device;          /* HIP device ordinal the handle runs on */
+    int32_t device;          /* HIP device ordinal the handle runs on (the handle */
+                             /*   allocates 4 bytes there with debug_checks)    */
     int32_t rotary_mode;     /* 0: none; 1: rotary embedding of q and keys, applied */
                              /*   in the kernel as the keys are read (see above)   */
     float rope_theta;        /* rotary_mode 1: frequency base, finite and > 0     */
     float rope_scale;        /* rotary_mode 1: positions are divided by it, finite */
                              /*   and > 0 (1: no scaling)                           */
+    int32_t debug_checks;    /* 1: keep a device status word that collects          */
+                             /*   PA_DECODE_VIOLATION_* bits (pa_decode_debug_status); */
+                             /*   0: values are clamped all the same, not reported   */
 } pa_decode_desc;
 
 /* Per-call arguments.  Element strides are in elements of the cache dtype. */
@@ -149,7 +163,9 @@ typedef struct pa_decode_plan {
 
 typedef struct pa_decode_handle_s* pa_decode_handle;
 
-/* Validate desc, read the device's properties and return a handle.
+/* Validate desc, read the device's properties and return a handle (with
+ * desc.debug_checks = 1 it also allocates and zeroes the 4-byte status word
+ * on desc.device).
  * Errors: INVALID_ARG (null pointer, non-positive sizes, Hq % Hkv != 0,
  * rotary_mode not 0 or 1, rope_theta or rope_scale not finite and > 0 with
  * rotary_mode 1), UNSUPPORTED (shape or dtype not built), HIP_ERROR (no such
@@ -172,8 +188,16 @@ int pa_decode_workspace_size(pa_decode_handle handle, int32_t batch, int32_t max
  * n_b <= max_context_len.  Keys before lo_b and slots past n_b never reach
  * the result, so they may hold anything (NaN included); page-table entries
  * past ceil(n_b/ps) (within the row's pt_stride entries) may be read but are
- * never used to address K/V. */
+ * never used to address K/V.  A run whose device-side values break the
+ * contract reads no memory outside the caller's buffers (see
+ * PA_DECODE_VIOLATION_*); its out/lse are then unspecified. */
 int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* stream);
+
+/* Violation bits (PA_DECODE_VIOLATION_*) collected by the runs on this
+ * handle since the previous call, then cleared.  Needs desc.debug_checks = 1
+ * (else INVALID_ARG).  Synchronizes the device (hipDeviceSynchronize) before
+ * it reads the word: a debugging aid, not for a timed loop. */
+int pa_decode_debug_status(pa_decode_handle handle, int32_t* status);
 
 /* The plan of the last successful pa_decode_run on this handle. */
 int pa_decode_last_plan(pa_decode_handle handle, pa_decode_plan* plan);

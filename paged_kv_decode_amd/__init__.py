@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     load_library,
     make_desc,
     pa_decode_create,
+    pa_decode_debug_status,
     pa_decode_destroy,
     pa_decode_last_hip_error,
     pa_decode_last_plan,

@@ -36,7 +36,8 @@ EXPORTED = ["pa_decode_create", "pa_decode_destroy", "pa_decode_workspace_size",
             "pa_decode_run", "pa_decode_last_plan", "pa_decode_plan_query",
             "pa_decode_profile_begin", "pa_decode_profile_end",
             "pa_decode_last_hip_error", "pa_decode_status_string",
-            "pa_decode_workspace_size_csr", "pa_decode_run_csr", "pa_decode_plan_query_csr"]
+            "pa_decode_workspace_size_csr", "pa_decode_run_csr", "pa_decode_plan_query_csr",
+            "pa_decode_debug_status"]
 
 
 class PaDecodeDesc(ctypes.Structure):
@@ -45,7 +46,7 @@ class PaDecodeDesc(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("max_context_len", ctypes.c_int32), ("device", ctypes.c_int32),
                 ("rotary_mode", ctypes.c_int32), ("rope_theta", ctypes.c_float),
-                ("rope_scale", ctypes.c_float)]
+                ("rope_scale", ctypes.c_float), ("debug_checks", ctypes.c_int32)]
 
 
 class PaDecodeArgs(ctypes.Structure):
@@ -135,6 +136,7 @@ def load_library(path: Optional[str] = None):
                                                  i32, i32, i32, i32,
                                                  ctypes.POINTER(PaDecodePlan)]
         lib.pa_decode_last_hip_error.argtypes = [vp]
+        lib.pa_decode_debug_status.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
         lib.pa_decode_status_string.argtypes = [ctypes.c_int]
         lib.pa_decode_status_string.restype = ctypes.c_char_p
         for name in EXPORTED:
@@ -242,15 +244,31 @@ def pa_decode_last_hip_error(handle) -> int:
     return int(load_library().pa_decode_last_hip_error(handle))
 
 
+# Violation bits of pa_decode_debug_status (include/pa_decode.h).
+PA_DECODE_VIOLATION_PAGE = 1
+PA_DECODE_VIOLATION_LENGTH = 2
+PA_DECODE_VIOLATION_ROW = 4
+
+
+def pa_decode_debug_status(handle) -> int:
+    """Violation bits collected since the last call (synchronizes the device)."""
+    v = ctypes.c_int32()
+    _check(load_library().pa_decode_debug_status(handle, ctypes.byref(v)),
+           "pa_decode_debug_status")
+    return int(v.value)
+
+
 def make_desc(num_q_heads, num_kv_heads, head_dim, dtype, max_batch, max_context_len,
-              page_size=16, device=0, rope=None, rotary_mode=None) -> PaDecodeDesc:
+              page_size=16, device=0, rope=None, rotary_mode=None,
+              debug_checks=0) -> PaDecodeDesc:
     """rope: None (rotary_mode 0) or (rope_theta, rope_scale) for rotary_mode 1;
-    rotary_mode overrides the mode (to pass invalid values through in tests)."""
+    rotary_mode overrides the mode (to pass invalid values through in tests);
+    debug_checks: 1 keeps the device status word (pa_decode_debug_status)."""
     code = DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     mode = (0 if rope is None else 1) if rotary_mode is None else int(rotary_mode)
     theta, rscale = (0.0, 0.0) if rope is None else (float(rope[0]), float(rope[1]))
     return PaDecodeDesc(num_q_heads, num_kv_heads, head_dim, page_size, code, max_batch,
-                        max_context_len, device, mode, theta, rscale)
+                        max_context_len, device, mode, theta, rscale, int(debug_checks))
 
 
 class PagedDecode:
@@ -261,9 +279,10 @@ class PagedDecode:
     """
 
     def __init__(self, num_q_heads, num_kv_heads, head_dim, dtype, max_batch,
-                 max_context_len, page_size=16, device=0, rope=None):
+                 max_context_len, page_size=16, device=0, rope=None, debug_checks=0):
         self.desc = make_desc(num_q_heads, num_kv_heads, head_dim, dtype, max_batch,
-                              max_context_len, page_size, device, rope=rope)
+                              max_context_len, page_size, device, rope=rope,
+                              debug_checks=debug_checks)
         self.dtype = dtype
         self.device = torch.device("cuda", device)
         self.handle = pa_decode_create(self.desc)

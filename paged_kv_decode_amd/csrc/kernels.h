@@ -33,9 +33,19 @@ struct PartialParams {
     float* ws_l;              // [B, Hq, P], denominators
     void* out;                // [B, Hq, D]
     float* lse;               // [B, Hq] or null
+    // Device-side contract (checked in the kernel, never trusted for an
+    // address): page ids outside [0, num_pages) read page 0; context lengths
+    // are clamped to [0, max_context_len]; CSR rows to [0, nnz_pages].  Each
+    // violation ORs a PA_DECODE_VIOLATION_* bit into *status when status is
+    // not null.
+    int32_t num_pages;
+    int32_t max_context_len;
+    int32_t nnz_pages;
+    int32_t* status;
     int32_t rotary;           // 1: rotary embedding of q and keys (rotary_mode 1)
     double rope_rho;          // rope_theta^(-2/D): theta_i = rope_rho^i / rope_scale
     double rope_f0;           // 1 / (2 pi rope_scale): theta_0 in revolutions
+    float minus_one;          // -1 (a value the compiler cannot fold; see TurnedKey)
 };
 
 // Arguments of the merge kernel (one workgroup per (query head, b)).

@@ -49,6 +49,7 @@ struct pa_decode_handle_s {
     int last_hip_error;
     bool profiling;
     EventRing prof_partial, prof_merge;
+    int32_t* status_word;  // device, with desc.debug_checks: violation bits
 };
 
 namespace {
@@ -153,6 +154,7 @@ struct PageSource {
     const int32_t* context_lens;
     const int32_t* page_indptr;   // null for the dense form
     const int32_t* last_page_len;
+    int32_t nnz_pages;            // CSR: entries of page_indices
 };
 
 // Launches one planned decode step on `stream` (arguments already checked).
@@ -199,10 +201,15 @@ int launch_step(pa_decode_handle handle, const StepArgs& a, const PageSource& sr
     pp.ws_l = plan.split ? reinterpret_cast<float*>(ws + wl.l_off) : nullptr;
     pp.out = a.out;
     pp.lse = a.lse;
+    pp.num_pages = a.num_pages;
+    pp.max_context_len = a.max_context_len;
+    pp.nnz_pages = src.nnz_pages;
+    pp.status = handle->status_word;
     pp.rotary = d.rotary_mode;
     // theta_i = rope_theta^(-2i/D) / rope_scale = rope_rho^i / rope_scale
     pp.rope_rho = d.rotary_mode ? std::pow(double(d.rope_theta), -2.0 / d.head_dim) : 1.0;
     pp.rope_f0 = d.rotary_mode ? 1.0 / (6.283185307179586477 * double(d.rope_scale)) : 0.0;
+    pp.minus_one = -1.0f;
 
     const dim3 grid(plan.grid_partial[0], plan.grid_partial[1], plan.grid_partial[2]);
     const dim3 block(plan.block_partial);
@@ -276,6 +283,20 @@ int pa_decode_create(const pa_decode_desc* desc, pa_decode_handle* handle)
     h->has_plan = false;
     h->last_hip_error = 0;
     h->profiling = false;
+    h->status_word = nullptr;
+    if (desc->debug_checks) {
+        int prev = -1;
+        hipError_t e = hipGetDevice(&prev);
+        if (e == hipSuccess) e = hipSetDevice(desc->device);
+        if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&h->status_word), sizeof(int32_t));
+        if (e == hipSuccess) e = hipMemset(h->status_word, 0, sizeof(int32_t));
+        if (prev >= 0) hipSetDevice(prev);
+        if (e != hipSuccess) {
+            if (h->status_word) hipFree(h->status_word);
+            delete h;
+            return PA_DECODE_HIP_ERROR;
+        }
+    }
     *handle = h;
     return PA_DECODE_OK;
 }
@@ -285,6 +306,7 @@ int pa_decode_destroy(pa_decode_handle handle)
     if (handle) {
         handle->prof_partial.release();
         handle->prof_merge.release();
+        if (handle->status_word) hipFree(handle->status_word);
     }
     delete handle;
     return PA_DECODE_OK;
@@ -386,7 +408,7 @@ int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* str
                        a.sliding_window, a.partition_size, &plan);
     if (st != PA_DECODE_OK)
         return st;
-    PageSource src = {a.page_table, a.pt_stride, a.context_lens, nullptr, nullptr};
+    PageSource src = {a.page_table, a.pt_stride, a.context_lens, nullptr, nullptr, 0};
     return launch_step(handle, common_args(a), src, plan, stream);
 }
 
@@ -434,8 +456,29 @@ int pa_decode_run_csr(pa_decode_handle handle, const pa_decode_csr_args* args, v
         return st;
     StepArgs c = common_args(a);
     c.max_context_len = max_ctx;
-    PageSource src = {a.page_indices, 0, nullptr, a.page_indptr, a.last_page_len};
+    PageSource src = {a.page_indices, 0, nullptr, a.page_indptr, a.last_page_len, a.nnz_pages};
     return launch_step(handle, c, src, plan, stream);
+}
+
+int pa_decode_debug_status(pa_decode_handle handle, int32_t* status)
+{
+    if (!handle || !status || !handle->status_word)
+        return PA_DECODE_INVALID_ARG;
+    int32_t v = 0;
+    const int32_t zero = 0;
+    int prev = -1;
+    hipError_t e = hipGetDevice(&prev);
+    if (e == hipSuccess) e = hipSetDevice(handle->desc.device);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(&v, handle->status_word, sizeof v, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(handle->status_word, &zero, sizeof zero, hipMemcpyHostToDevice);
+    if (prev >= 0) hipSetDevice(prev);
+    if (e != hipSuccess) {
+        handle->last_hip_error = int(e);
+        return PA_DECODE_HIP_ERROR;
+    }
+    *status = v;
+    return PA_DECODE_OK;
 }
 
 int pa_decode_last_plan(pa_decode_handle handle, pa_decode_plan* plan)

@@ -52,6 +52,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -187,21 +188,6 @@ __device__ __forceinline__ void sincos_rev(float x, float* s, float* c)
 // key once would move each score by ~2^-12 (f16) or ~2^-9 (bf16) relative.
 template <int DT> struct TurnedKey;
 
-// f16 pair (x0 - h.lo, x1 - h.hi) for the f16 pair h: two mixed-precision
-// FMAs (f16 source times -1 plus f32 source, rounded to f16 into the low and
-// high halves).  Written out because the compiler turns fma(h, -1, x) into a
-// subtraction, which takes a conversion before and after.
-__device__ __forceinline__ uint32_t minus_f16_pair(uint32_t h, float x0, float x1)
-{
-    // -1 comes from a register: an inline constant in a mixed instruction
-    // is not read as an f32 value.
-    uint32_t r;
-    asm("v_fma_mixlo_f16 %0, %1, %4, %2 op_sel_hi:[1,0,0]\n\t"
-        "v_fma_mixhi_f16 %0, %1, %4, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-        : "=&v"(r)
-        : "v"(h), "v"(x0), "v"(x1), "v"(-1.0f));
-    return r;
-}
 
 template <> struct TurnedKey<PA_DTYPE_F16> {
     static constexpr int EPC = 8;
@@ -225,9 +211,12 @@ template <> struct TurnedKey<PA_DTYPE_F16> {
     // Turn the pair chunks (x, y) (first / second half of head_dim) by the
     // angles (cs, sn) and add both score MFMAs.  The f16 keys enter the
     // mixed-precision FMAs directly; hi is the pair-wise round toward zero of
-    // the turned value and lo = turned - hi (one mixed FMA, rounded to f16).
+    // the turned value and lo = fma(hi, m1, turned) rounded to f16, one mixed
+    // FMA.  m1 is -1 from a kernel argument: with a literal -1 the compiler
+    // rewrites the FMA as a subtraction with conversions around it.
     __device__ static f32x4 turn_mfma(u32x4 xc, u32x4 yc, const float (&cs)[8],
-                                      const float (&sn)[8], u32x4 qx, u32x4 qy, f32x4 acc)
+                                      const float (&sn)[8], u32x4 qx, u32x4 qy, f32x4 acc,
+                                      float m1)
     {
         typedef __fp16 h2 __attribute__((ext_vector_type(2)));
         const f16x8 x = __builtin_bit_cast(f16x8, xc), y = __builtin_bit_cast(f16x8, yc);
@@ -246,8 +235,12 @@ template <> struct TurnedKey<PA_DTYPE_F16> {
             const h2 b = __builtin_amdgcn_cvt_pkrtz(yr[2 * j], yr[2 * j + 1]);
             xh[j] = __builtin_bit_cast(uint32_t, a);
             yh[j] = __builtin_bit_cast(uint32_t, b);
-            xl[j] = minus_f16_pair(xh[j], xr[2 * j], xr[2 * j + 1]);
-            yl[j] = minus_f16_pair(yh[j], yr[2 * j], yr[2 * j + 1]);
+            const f16x2 lx = {(_Float16)__builtin_fmaf((float)a[0], m1, xr[2 * j]),
+                              (_Float16)__builtin_fmaf((float)a[1], m1, xr[2 * j + 1])};
+            const f16x2 ly = {(_Float16)__builtin_fmaf((float)b[0], m1, yr[2 * j]),
+                              (_Float16)__builtin_fmaf((float)b[1], m1, yr[2 * j + 1])};
+            xl[j] = __builtin_bit_cast(uint32_t, lx);
+            yl[j] = __builtin_bit_cast(uint32_t, ly);
         }
         acc = Chunk<PA_DTYPE_F16>::mfma(xh, qx, acc);
         acc = Chunk<PA_DTYPE_F16>::mfma(xl, qx, acc);
@@ -281,7 +274,8 @@ template <> struct TurnedKey<PA_DTYPE_BF16> {
     // (one packed conversion); lo = turned - hi, exact in f32, truncated to
     // bf16 (a byte permute keeps the upper halves): |error| < 2^-16 |turned|.
     __device__ static f32x4 turn_mfma(u32x4 xc, u32x4 yc, const float (&cs)[8],
-                                      const float (&sn)[8], u32x4 qx, u32x4 qy, f32x4 acc)
+                                      const float (&sn)[8], u32x4 qx, u32x4 qy, f32x4 acc,
+                                      float)
     {
         typedef __bf16 b2 __attribute__((ext_vector_type(2)));
         typedef float f2 __attribute__((ext_vector_type(2)));
@@ -498,10 +492,18 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     // Page-table row and context length of sequence b: dense rows of
     // pt_stride entries with context_lens, or CSR rows (page_indptr,
     // last_page_len).  row_len bounds the entries a row may be read at.
+    // Values outside the contract are clamped (and reported), so that no
+    // address ever comes from them.
     const int32_t* pt_row;
     int row_len, n;
+    int violation = 0;
     if (prm.page_indptr) {
-        const int i0 = prm.page_indptr[b], i1 = prm.page_indptr[b + 1];
+        int i0 = prm.page_indptr[b], i1 = prm.page_indptr[b + 1];
+        if (i0 < 0 || i1 < i0 || i1 > prm.nnz_pages) {
+            violation |= PA_DECODE_VIOLATION_ROW;
+            i0 = min(max(i0, 0), prm.nnz_pages);
+            i1 = min(max(i1, i0), prm.nnz_pages);
+        }
         pt_row = prm.page_table + i0;
         row_len = i1 - i0;
         const int last = min(max(prm.last_page_len[b], 0), kPage);
@@ -510,6 +512,10 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         pt_row = prm.page_table + size_t(b) * prm.pt_stride;
         row_len = prm.pt_stride;
         n = prm.context_lens[b];
+    }
+    if (n < 0 || n > prm.max_context_len) {
+        violation |= PA_DECODE_VIOLATION_LENGTH;
+        n = min(max(n, 0), prm.max_context_len);
     }
     const int i16 = lane & 15, grp = lane >> 4;
     // Load map: row and chunk of instruction i's chunk for this lane.
@@ -522,7 +528,10 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     auto load_ids = [&](int pg_first, int pg_end, int it0) {
         const int it = it0 + lane / NB;
         const int pg = pg_first + (wi + wpp * it) * NB + lane % NB;
-        return pg < pg_end ? pt_row[pg] : 0;
+        const int id = pg < pg_end ? pt_row[pg] : 0;
+        const bool ok = uint32_t(id) < uint32_t(prm.num_pages);
+        violation |= ok ? 0 : PA_DECODE_VIOLATION_PAGE;
+        return ok ? id : 0;
     };
     // Without a window the partition's first page does not depend on the
     // context length: fetch the page ids together with the length and q.
@@ -674,7 +683,7 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
                 const u32x4 xc = ktile[tix(row, 4 * fs + grp)];
                 const u32x4 yc = ktile[tix(row, 4 * (fs + KS / 2) + grp)];
                 if constexpr (DT != PA_DTYPE_F32) {
-                    d = TK::turn_mfma(xc, yc, cs, sn, qa[fs], qa[fs + KS / 2], d);
+                    d = TK::turn_mfma(xc, yc, cs, sn, qa[fs], qa[fs + KS / 2], d, prm.minus_one);
                 } else {
                     float x[EPC], y[EPC], xr[EPC], yr[EPC];
                     TK::widen(xc, x);
@@ -915,6 +924,19 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         pin_loads();
         for (int it = it0; it < it1; ++it) step(it, it0, it1);
     }  // chunks of IPV blocks
+
+    // Contract violations seen by any lane: the wave's bits, OR-ed into the
+    // status word by one lane (a device-scope atomic).
+    if (prm.status) {
+        const unsigned long long any = __ballot(violation != 0);
+        if (any) {
+            int v = violation;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) v |= __shfl_xor(v, off);
+            if (lane == __ffsll(any) - 1)
+                __hip_atomic_fetch_or(prm.status, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 
     // Denominator of head i16 over the four lane groups.
     l_run = rows4_sum(l_run);

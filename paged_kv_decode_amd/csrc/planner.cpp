@@ -49,6 +49,8 @@ int check_desc(const pa_decode_desc& d)
         return PA_DECODE_INVALID_ARG;
     if (d.rotary_mode != 0 && d.rotary_mode != 1)
         return PA_DECODE_INVALID_ARG;
+    if (d.debug_checks != 0 && d.debug_checks != 1)
+        return PA_DECODE_INVALID_ARG;
     if (d.rotary_mode == 1 &&
         !(std::isfinite(d.rope_theta) && d.rope_theta > 0.f && std::isfinite(d.rope_scale) &&
           d.rope_scale > 0.f))

@@ -59,6 +59,8 @@ def test_status_strings():
     (dict(rotary_mode=1, rope_theta=-1e4, rope_scale=1.0), B.PA_DECODE_INVALID_ARG),
     (dict(rotary_mode=1, rope_theta=float("inf"), rope_scale=1.0), B.PA_DECODE_INVALID_ARG),
     (dict(rotary_mode=1, rope_theta=1e4, rope_scale=float("nan")), B.PA_DECODE_INVALID_ARG),
+    (dict(debug_checks=2), B.PA_DECODE_INVALID_ARG),
+    (dict(debug_checks=-1), B.PA_DECODE_INVALID_ARG),
 ])
 def test_create_rejects_invalid_descriptions(fields, status):
     base = dict(num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=16,
@@ -71,6 +73,7 @@ def test_create_rejects_invalid_descriptions(fields, status):
 
 
 def test_null_arguments_are_rejected():
+    assert lib().pa_decode_debug_status(None, None) == B.PA_DECODE_INVALID_ARG
     assert lib().pa_decode_create(None, None) == B.PA_DECODE_INVALID_ARG
     assert lib().pa_decode_run(None, None, None) == B.PA_DECODE_INVALID_ARG
     assert lib().pa_decode_last_plan(None, None) == B.PA_DECODE_INVALID_ARG

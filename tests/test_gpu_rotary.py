@@ -154,3 +154,17 @@ def test_rotary_token_major_cache_layout():
         out, lse, _ = run_gpu(p2, partition_size=S)
         compare(out, lse, ref_out, ref_lse, w.dtype, what="rope token-major S=%d" % S)
 
+
+
+@pytest.mark.parametrize("name", ["llama8b_b16_ragged_rope_f16", "llama8b_ctx32k_rope_f16"])
+def test_rotary_runs_are_bitwise_repeatable(name):
+    """The same inputs give the same bits on every run (waves interleave
+    differently from run to run, so a missing wait in the turned-key path
+    would show up here as differing results)."""
+    p = W.generate(W.CONFIGS[name])
+    from helpers import to_device
+    d = to_device(p)
+    first = run_gpu(p, dev=d)
+    for _ in range(6):
+        again = run_gpu(p, dev=d)
+        assert torch.equal(again[0], first[0]) and torch.equal(again[1], first[1])
