@@ -494,16 +494,17 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     // last_page_len).  row_len bounds the entries a row may be read at.
     // Values outside the contract are clamped (and reported), so that no
     // address ever comes from them.
+    // The violation bits (wave-uniform) are reported after the main loop.
+    int violation = 0;
     const int32_t* pt_row;
     int row_len, n;
-    int violation = 0;
+    // Clamps without branches: a branch on a loaded value would hold back
+    // the page-id and q loads until that value arrives.
     if (prm.page_indptr) {
-        int i0 = prm.page_indptr[b], i1 = prm.page_indptr[b + 1];
-        if (i0 < 0 || i1 < i0 || i1 > prm.nnz_pages) {
-            violation |= PA_DECODE_VIOLATION_ROW;
-            i0 = min(max(i0, 0), prm.nnz_pages);
-            i1 = min(max(i1, i0), prm.nnz_pages);
-        }
+        const int r0 = prm.page_indptr[b], r1 = prm.page_indptr[b + 1];
+        const int i0 = min(max(r0, 0), prm.nnz_pages);
+        const int i1 = min(max(r1, i0), prm.nnz_pages);
+        violation |= (i0 != r0 || i1 != r1) ? PA_DECODE_VIOLATION_ROW : 0;
         pt_row = prm.page_table + i0;
         row_len = i1 - i0;
         const int last = min(max(prm.last_page_len[b], 0), kPage);
@@ -513,9 +514,10 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         row_len = prm.pt_stride;
         n = prm.context_lens[b];
     }
-    if (n < 0 || n > prm.max_context_len) {
-        violation |= PA_DECODE_VIOLATION_LENGTH;
-        n = min(max(n, 0), prm.max_context_len);
+    {
+        const int nc = min(max(n, 0), prm.max_context_len);
+        violation |= nc != n ? PA_DECODE_VIOLATION_LENGTH : 0;
+        n = nc;
     }
     const int i16 = lane & 15, grp = lane >> 4;
     // Load map: row and chunk of instruction i's chunk for this lane.
@@ -528,10 +530,7 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     auto load_ids = [&](int pg_first, int pg_end, int it0) {
         const int it = it0 + lane / NB;
         const int pg = pg_first + (wi + wpp * it) * NB + lane % NB;
-        const int id = pg < pg_end ? pt_row[pg] : 0;
-        const bool ok = uint32_t(id) < uint32_t(prm.num_pages);
-        violation |= ok ? 0 : PA_DECODE_VIOLATION_PAGE;
-        return ok ? id : 0;
+        return pg < pg_end ? pt_row[pg] : 0;
     };
     // Without a window the partition's first page does not depend on the
     // context length: fetch the page ids together with the length and q.
@@ -744,7 +743,12 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         const int nbv_ = itn < it1 ? min(NB, pg1 - (pg0 + (wi + wpp * itn) * NB)) : 0;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            page[nb] = __builtin_amdgcn_readlane(ids, (itc - it0) * NB + nb);
+            // A page id outside the pool reads page 0 instead (reported
+            // when it belongs to the block; ids past the block are padding).
+            const int id = __builtin_amdgcn_readlane(ids, (itc - it0) * NB + nb);
+            const bool ok = uint32_t(id) < uint32_t(prm.num_pages);
+            violation |= (ok || nb >= nbv_) ? 0 : PA_DECODE_VIOLATION_PAGE;
+            page[nb] = ok ? id : 0;
             uint32_t m = __builtin_amdgcn_readfirstlane(nb < nbv_ ? ~0u : 0u);
             asm volatile("" : "+s"(m));  // an opaque mask, not a branch condition
             pmask[nb] = m;
@@ -925,18 +929,8 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         for (int it = it0; it < it1; ++it) step(it, it0, it1);
     }  // chunks of IPV blocks
 
-    // Contract violations seen by any lane: the wave's bits, OR-ed into the
-    // status word by one lane (a device-scope atomic).
-    if (prm.status) {
-        const unsigned long long any = __ballot(violation != 0);
-        if (any) {
-            int v = violation;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) v |= __shfl_xor(v, off);
-            if (lane == __ffsll(any) - 1)
-                __hip_atomic_fetch_or(prm.status, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    if (prm.status && violation != 0 && lane == 0)
+        __hip_atomic_fetch_or(prm.status, violation, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // Denominator of head i16 over the four lane groups.
     l_run = rows4_sum(l_run);
