@@ -273,3 +273,26 @@ def test_layer_stacked_step_under_one_graph():
         for l in range(L):
             compare(outs[l].cpu(), lses[l].cpu(), refs[l][0], refs[l][1], base.dtype,
                     "layer %d replay %d" % (l, rep))
+
+
+@pytest.mark.parametrize("rope", [None, (500000.0, 1.0)])
+@pytest.mark.parametrize("window", [300, 0])
+def test_million_token_context(window, rope):
+    """One sequence of 1,000,000 tokens: page ids up to 62,500, 253
+    partitions for the workgroup merge without a window, and, with rotary,
+    angles at positions near 10^6."""
+    n = 1_000_000
+    w = W.custom(batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64, dtype=torch.float16,
+                 context_lens=[n], seed=610, window=window, rope=rope, num_pages=n // 16 + 4)
+    _check(W.generate(w), what="1M tokens, window %d, rope=%s" % (window, rope))
+
+
+def test_batch_of_512_short_ragged_sequences():
+    """A wide grid (512 sequences x 8 KV heads) of short, ragged contexts,
+    empty ones included."""
+    gen = torch.Generator().manual_seed(611)
+    lens = torch.randint(0, 300, (512,), generator=gen).tolist()
+    lens[0], lens[1], lens[2] = 0, 1, 299
+    w = W.custom(batch=512, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype=torch.float16,
+                 context_lens=lens, seed=612)
+    _check(W.generate(w), what="batch 512")
