@@ -108,7 +108,12 @@ typedef struct pa_decode_desc {
                              /*   0: values are clamped all the same, not reported   */
 } pa_decode_desc;
 
-/* Per-call arguments.  Element strides are in elements of the cache dtype. */
+/* Per-call arguments.  Element strides are in elements of the cache dtype.
+ * q, k_cache, v_cache, out and (when the plan splits) workspace must be
+ * 16-byte aligned, each stride times the element size a multiple of 16
+ * bytes, and kv_stride_slot >= D; otherwise pa_decode_run returns
+ * PA_DECODE_INVALID_ARG (PA_DECODE_WORKSPACE_TOO_SMALL for a short
+ * workspace) and launches nothing. */
 typedef struct pa_decode_args {
     const void* q;              /* device, [batch, Hq, D] contiguous */
     const void* k_cache;        /* device, paged keys: element (page, kv, slot, d) at */

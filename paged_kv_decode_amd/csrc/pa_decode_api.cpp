@@ -32,8 +32,8 @@ struct EventRing {
     }
     void release()
     {
-        for (hipEvent_t e : start) hipEventDestroy(e);
-        for (hipEvent_t e : stop) hipEventDestroy(e);
+        for (hipEvent_t e : start) (void)hipEventDestroy(e);
+        for (hipEvent_t e : stop) (void)hipEventDestroy(e);
         start.clear();
         stop.clear();
         used = 0;
@@ -290,9 +290,9 @@ int pa_decode_create(const pa_decode_desc* desc, pa_decode_handle* handle)
         if (e == hipSuccess) e = hipSetDevice(desc->device);
         if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&h->status_word), sizeof(int32_t));
         if (e == hipSuccess) e = hipMemset(h->status_word, 0, sizeof(int32_t));
-        if (prev >= 0) hipSetDevice(prev);
+        if (prev >= 0) (void)hipSetDevice(prev);
         if (e != hipSuccess) {
-            if (h->status_word) hipFree(h->status_word);
+            if (h->status_word) (void)hipFree(h->status_word);
             delete h;
             return PA_DECODE_HIP_ERROR;
         }
@@ -306,7 +306,7 @@ int pa_decode_destroy(pa_decode_handle handle)
     if (handle) {
         handle->prof_partial.release();
         handle->prof_merge.release();
-        if (handle->status_word) hipFree(handle->status_word);
+        if (handle->status_word) (void)hipFree(handle->status_word);
     }
     delete handle;
     return PA_DECODE_OK;
@@ -324,7 +324,7 @@ int pa_decode_profile_begin(pa_decode_handle handle, int32_t max_launches)
             hipError_t e = hipEventCreate(&a);
             if (e == hipSuccess) e = hipEventCreate(&b);
             if (e != hipSuccess) {
-                if (a) hipEventDestroy(a);
+                if (a) (void)hipEventDestroy(a);
                 r->release();
                 handle->last_hip_error = int(e);
                 return PA_DECODE_HIP_ERROR;
@@ -472,7 +472,7 @@ int pa_decode_debug_status(pa_decode_handle handle, int32_t* status)
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e == hipSuccess) e = hipMemcpy(&v, handle->status_word, sizeof v, hipMemcpyDeviceToHost);
     if (e == hipSuccess) e = hipMemcpy(handle->status_word, &zero, sizeof zero, hipMemcpyHostToDevice);
-    if (prev >= 0) hipSetDevice(prev);
+    if (prev >= 0) (void)hipSetDevice(prev);
     if (e != hipSuccess) {
         handle->last_hip_error = int(e);
         return PA_DECODE_HIP_ERROR;

@@ -485,7 +485,8 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     const int nw = blockDim.x / kWave;
     const int wpp = prm.waves_per_partition;
     const int slot = wave / wpp, wi = wave % wpp;
-    const int prel = blockIdx.x * (nw / wpp) + slot;
+    const int nslots = nw / wpp;
+    const int prel = blockIdx.x * nslots + slot;
     const int kvh = blockIdx.y, b = blockIdx.z;
     const int Gact = prm.group;
     const int S = prm.partition_size;
@@ -657,6 +658,7 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     // The score MFMAs of page nb with turned keys.
     auto turned_scores = [&](int nb) {
         using TK = TurnedKey<DT>;
+        static_assert(TK::EPC == EPC, "turned-key chunk width");
         const int row = nb * kPage + i16;
         const float2* bt = rtab + nb * HD;
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
@@ -721,10 +723,12 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     // Software pipeline over the wave's blocks: as soon as block it's K and V
     // rows are in the LDS tiles, the registers take block it+1's loads, so the
     // loads of one block are in flight while the previous block is computed.
-    // Every phase issues exactly 2*NB*KS loads, with no branch around them, so
-    // that each wait leaves the younger loads in flight: a page past the
-    // wave's last block (or past the end of a short block) gets a zero lane
-    // offset, i.e. all lanes read one 16-byte piece of a page.
+    // Every phase issues exactly 2*NB*KS loads, with no branch around the
+    // individual pages, so that each wait leaves the younger loads in flight:
+    // a page past the end of a short block gets a zero lane offset, i.e. all
+    // lanes read one 16-byte piece of a page.  The last step of a chunk
+    // issues nothing (one wave-uniform branch), which shortens the
+    // single-block waves of short contexts.
     u32x4 kr[NB][KS], vr[NB][KS];
     int64_t page[NB];
     uint32_t pmask[NB];
@@ -804,11 +808,15 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         else
             stage(vtile, vr, false, pgb, nbv);
         wave_lds_sync();
-        fetch_ids(it + 1, it0, it1);
-        issue(kbase, kr);
-        pin_loads();
-        issue(vbase, vr);
-        pin_loads();
+        if (it + 1 < it1) {
+            // The next block of this chunk (the loads of a following chunk
+            // are issued once its page ids are in).
+            fetch_ids(it + 1, it0, it1);
+            issue(kbase, kr);
+            pin_loads();
+            issue(vbase, vr);
+            pin_loads();
+        }
 
         // Scores (base 2) of head i16 against token 4*grp + r of each page.
         float s[NB][4];
@@ -998,7 +1006,6 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     }
     __syncthreads();
 
-    const int nslots = nw / wpp;
     for (int sl = 0; sl < nslots; ++sl) {
         const int p_rel = blockIdx.x * nslots + sl;
         if (p_rel >= prm.num_partitions)
@@ -1021,117 +1028,130 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     }
 }
 
-// ---------------------------------------------------------------------------
-// Merge kernel: one workgroup (256 threads) per (query head, sequence).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float block_reduce(float x, float* red, bool is_max)
+// Four consecutive output elements (16-byte aligned for f32, 8-byte for
+// f16/bf16: out is 16-byte aligned and idx a multiple of 4), rounded to the
+// output type as store_out does.
+template <int DT> __device__ __forceinline__ void store_out4(void* out, size_t idx, f32x4 x);
+template <> __device__ __forceinline__ void store_out4<PA_DTYPE_F32>(void* out, size_t idx, f32x4 x)
 {
-    // wave reduce with shuffles, then across the waves through LDS
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const float y = __shfl_xor(x, off);
-        x = is_max ? fmaxf(x, y) : x + y;
-    }
-    const int wave = threadIdx.x / kWave, nwv = blockDim.x / kWave;
-    if ((threadIdx.x & (kWave - 1)) == 0) red[wave] = x;
-    __syncthreads();
-    x = red[0];
-    for (int w = 1; w < nwv; ++w) x = is_max ? fmaxf(x, red[w]) : x + red[w];
-    return x;
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = x;
+}
+template <> __device__ __forceinline__ void store_out4<PA_DTYPE_F16>(void* out, size_t idx, f32x4 x)
+{
+    const f16x4 h = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+    *reinterpret_cast<f16x4*>(static_cast<_Float16*>(out) + idx) = h;
+}
+template <> __device__ __forceinline__ void store_out4<PA_DTYPE_BF16>(void* out, size_t idx, f32x4 x)
+{
+    const bf16x4 h = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out) + idx) = h;
 }
 
-// Merge kernel: one 256-thread workgroup per (query head, sequence, 64-dim
-// slice of head_dim).  16 threads read one partition row slice as float4s,
-// 16 row groups cover 16 partitions per pass; every load of the first 256
-// partitions is issued before the first reduction.  Empty partitions carry
-// max = -inf and denominator 0 and get weight 0.
+// ---------------------------------------------------------------------------
+// Merge kernel for any partition count: one 256-thread workgroup per (query
+// head, sequence, 64-column slice of head_dim).  Every wave finds the global
+// maximum and the rescaled denominator sum itself (lane-strided loads, DPP
+// and lane-swap reductions, no barrier).  For the outputs the 16 row groups
+// (4 per wave, 16 lanes each) take rows rg, rg + 16, ...; lane c4 of a row
+// group reads float4 column c4 of its rows, every load of a 256-row pass
+// issued before the first use.  The row groups of a wave are summed with
+// lane swaps and the four waves through LDS (one barrier).  Empty
+// partitions carry max = -inf and denominator 0 and get weight 0; rows past
+// P re-read row P - 1 with weight 0.
+// ---------------------------------------------------------------------------
 template <int DT, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams prm)
 {
-    constexpr int TPR = 16;               // threads per row slice (64 floats)
-    constexpr int RG = 256 / TPR;         // row groups
-    constexpr int RPT = 16;               // rows per thread held in registers
-    __shared__ float red[2][4];
-    __shared__ f32x4 part[256];
+    constexpr int RPT = 16;               // rows per lane per pass (16 row groups x 16 = 256)
+    __shared__ f32x4 part[4][16];
     const int h = blockIdx.x, b = blockIdx.y, dsl = blockIdx.z;
-    const int rg = threadIdx.x / TPR, c4 = threadIdx.x % TPR;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int rg = 4 * wave + (lane >> 4), c4 = lane & 15;   // row group 0..15, float4 column
     const int P = prm.num_partitions;
     const size_t hrow = size_t(b) * prm.num_q_heads + h;
     const float* m = prm.ws_m + hrow * P;
     const float* l = prm.ws_l + hrow * P;
-    // Columns dsl*64 + 4*c4 .. +3; the last slice of head_dim 96 has 8
-    // float4 columns, so threads past D read column 0 and store nothing.
-    const bool has_col = dsl * 64 + 4 * c4 < D;
-    const f32x4* o = reinterpret_cast<const f32x4*>(prm.ws_o + hrow * P * D) + (has_col ? dsl * TPR + c4 : 0);
+    const int col = dsl * 64 + 4 * c4;
+    const bool has_col = col < D;          // the last slice of head_dim 96 has 32 columns
+    const char* ob = reinterpret_cast<const char*>(prm.ws_o + hrow * P * D);
+    const uint32_t coff = uint32_t(has_col ? col : 0);
 
-    // Rows rg, rg + RG, ... of the first pass, all loads in flight together.
-    float mr[RPT], lr[RPT];
+    // First pass of rows, loaded before anything waits.
     f32x4 orow[RPT];
+    float mr[RPT], lr[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const int p = rg + RG * i;
-        const bool ok = p < P;
-        mr[i] = ok ? m[p] : -INFINITY;
-        lr[i] = ok ? l[p] : 0.f;
-        orow[i] = ok ? o[size_t(p) * (D / 4)] : f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t row = uint32_t(min(rg + 16 * i, P - 1));
+        orow[i] = *reinterpret_cast<const f32x4*>(ob + (row * D + coff) * 4u);
+        mr[i] = m[row];
+        lr[i] = l[row];
     }
-
-    // Phase 1: global max of the partition maxima.
-    float mx = -INFINITY;
+    // Lane-strided maxima and denominators for the wave's own reductions.
+    float ms[4], ls[4];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) mx = fmaxf(mx, mr[i]);
-    for (int p = threadIdx.x + RG * RPT; p < P; p += blockDim.x) mx = fmaxf(mx, m[p]);
-    const float M = block_reduce(mx, red[0], true);
+    for (int k = 0; k < 4; ++k) {
+        const int p = min(lane + kWave * k, P - 1);
+        ms[k] = m[p];
+        ls[k] = l[p];
+    }
+    pin_loads();
+
+    // Phase 1: global max of the partition maxima (entries past P repeat
+    // entry P - 1, which leaves the max unchanged).
+    float mx = fmaxf(fmaxf(ms[0], ms[1]), fmaxf(ms[2], ms[3]));
+    for (int p = lane + 4 * kWave; p < P; p += kWave) mx = fmaxf(mx, m[p]);
+    const float M = rows4_max(row16_max(mx));
     if (M == -INFINITY) {
         // Every partition empty: out = 0, lse = -inf.
-        if (rg == 0 && has_col) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) store_out<DT>(prm.out, hrow * D + dsl * 64 + 4 * c4 + e, 0.f);
-        }
+        if (wave == 0 && rg == 0 && has_col)
+            store_out4<DT>(prm.out, hrow * D + col, f32x4{0.f, 0.f, 0.f, 0.f});
         if (prm.lse && dsl == 0 && threadIdx.x == 0) prm.lse[hrow] = -INFINITY;
         return;
     }
-
-    // Phase 2: rescale each partition's denominator and sum the weighted
-    // outputs (rescale_p = 2^(m_p - M) * l_p).
+    // Phase 2: rescale_p = 2^(m_p - M) * l_p; their sum, and the weighted
+    // outputs.
+    auto weight = [&](float mp, float lp) { return lp > 0.f ? fast_exp2(mp - M) * lp : 0.f; };
     float tl = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        tl += lane + kWave * k < P ? weight(ms[k], ls[k]) : 0.f;
+    for (int p = lane + 4 * kWave; p < P; p += kWave) tl += weight(m[p], l[p]);
+    const float L = rows4_sum(row16_sum(tl));
+
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const float w = lr[i] > 0.f ? fast_exp2(mr[i] - M) * lr[i] : 0.f;
-        tl += w;
-        if (w > 0.f) a += w * orow[i];
+    for (int i = 0; i < RPT; ++i)
+        a += (rg + 16 * i < P ? weight(mr[i], lr[i]) : 0.f) * orow[i];
+    // Further passes (more than 256 partitions).
+    for (int p = rg + 16 * RPT; p < P; p += 16) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(ob + (uint32_t(p) * D + coff) * 4u);
+        a += weight(m[p], l[p]) * o;
     }
-    for (int p = rg + RG * RPT; p < P; p += RG) {
-        const float lp = l[p];
-        const float w = lp > 0.f ? fast_exp2(m[p] - M) * lp : 0.f;
-        tl += w;
-        if (w > 0.f) a += w * o[size_t(p) * (D / 4)];
-    }
-    // Each row's weight is held by all TPR threads of its row group: count it once.
-    const float L = block_reduce(c4 == 0 ? tl : 0.f, red[1], false);
-    part[threadIdx.x] = a;
-    __syncthreads();
-    if (threadIdx.x < TPR && dsl * 64 + 4 * int(threadIdx.x) < D) {
-        f32x4 t = part[threadIdx.x];
-        for (int r = 1; r < RG; ++r) t += part[r * TPR + threadIdx.x];
-        const float inv = 1.f / L;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            store_out<DT>(prm.out, hrow * D + dsl * 64 + 4 * threadIdx.x + e, t[e] * inv);
+    for (int e = 0; e < 4; ++e) a[e] = rows4_sum(a[e]);
+    if ((lane >> 4) == 0) part[wave][c4] = a;
+    __syncthreads();
+    if (threadIdx.x < 16 && has_col) {
+        const f32x4 t = part[0][c4] + part[1][c4] + part[2][c4] + part[3][c4];
+        store_out4<DT>(prm.out, hrow * D + col, t * (1.f / L));
     }
     if (prm.lse && dsl == 0 && threadIdx.x == 0) prm.lse[hrow] = (M + log2f(L)) * kLn2;
 }
 
 // Merge kernel for up to PMAX (<= 64) partitions: one wave per (sequence,
-// query head, 64-dim slice of head_dim).  Lane p holds partition p's max and
-// denominator; both phases reduce across the wave with DPP and permlane
-// swaps (no barrier), and every o row the wave needs is loaded before the
-// first reduction (rows past P re-read row P-1 and get weight 0).
+// query head, 64-column slice of head_dim).  Lane p holds partition p's max
+// and denominator; the global max and the denominator sum reduce across the
+// wave with DPP and lane swaps (no barrier).  For the outputs, lane (rg, c4)
+// = (lane / 16, lane % 16) reads float4 column c4 of rows rg, rg + 4, ...,
+// all before the first reduction, takes each row's weight from the lane that
+// holds it, and the four row groups are summed with lane swaps at the end.
+// Rows past P re-read row P - 1 with weight 0.  Maxima and denominators are
+// loaded first, so that the first reduction waits for them only.
 template <int DT, int D, int PMAX>
 __global__ __launch_bounds__(256) void merge_wave_kernel(const MergeParams prm, int units)
 {
     constexpr int NS = (D + 63) / 64;   // 64-column slices (the last may be partial)
+    constexpr int RPL = PMAX / 4;       // rows per lane
     const int lane = threadIdx.x & (kWave - 1);
     const int unit = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x / kWave) +
                                                     threadIdx.x / kWave);
@@ -1140,20 +1160,31 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(const MergeParams prm, 
     const int P = prm.num_partitions;
     const int slice = unit % NS;
     const size_t hrow = size_t(unit / NS);   // b * Hq + h
-    const int col = slice * 64 + lane;
-    const bool has_col = col < D;
-    const float* o = prm.ws_o + hrow * P * D + (has_col ? col : 0);
-    float orow[PMAX];
+    const int rg = lane >> 4, c4 = lane & 15;
+    const int col = slice * 64 + 4 * c4;
+    const bool has_col = col < D;           // the last slice of head_dim 96 has 32 columns
+    // Branch-free loads (lanes past P re-read entry P - 1), all issued
+    // before the first use.
+    const int pl = min(lane, P - 1);
+    const float mraw = prm.ws_m[hrow * P + pl];
+    const float lraw = prm.ws_l[hrow * P + pl];
+    // Wave-uniform base of this head's rows; per-lane 32-bit byte offsets.
+    const char* ob = reinterpret_cast<const char*>(prm.ws_o + hrow * P * D);
+    f32x4 orow[RPL];
 #pragma unroll
-    for (int p = 0; p < PMAX; ++p) orow[p] = o[size_t(min(p, P - 1)) * D];
-    const float mp = lane < P ? prm.ws_m[hrow * P + lane] : -INFINITY;
-    const float lp = lane < P ? prm.ws_l[hrow * P + lane] : 0.f;
+    for (int i = 0; i < RPL; ++i) {
+        const uint32_t row = uint32_t(min(rg + 4 * i, P - 1));
+        orow[i] = *reinterpret_cast<const f32x4*>(ob + (row * D + uint32_t(has_col ? col : 0)) * 4u);
+    }
+    pin_loads();
+    const float mp = lane < P ? mraw : -INFINITY;
+    const float lp = lane < P ? lraw : 0.f;
 
     // Phase 1: global max of the partition maxima.
     const float M = rows4_max(row16_max(mp));
     if (M == -INFINITY) {
         // Every partition empty: out = 0, lse = -inf.
-        if (has_col) store_out<DT>(prm.out, hrow * D + col, 0.f);
+        if (rg == 0 && has_col) store_out4<DT>(prm.out, hrow * D + col, f32x4{0.f, 0.f, 0.f, 0.f});
         if (prm.lse && slice == 0 && lane == 0) prm.lse[hrow] = -INFINITY;
         return;
     }
@@ -1161,11 +1192,15 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(const MergeParams prm, 
     // 2^(m_p - M) * l_p), sum them, and weight the partition outputs.
     const float w = lp > 0.f ? fast_exp2(mp - M) * lp : 0.f;
     const float L = rows4_sum(row16_sum(w));
-    float a = 0.f;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int p = 0; p < PMAX; ++p)
-        a = __builtin_fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), p)), orow[p], a);
-    if (has_col) store_out<DT>(prm.out, hrow * D + col, a / L);
+    for (int i = 0; i < RPL; ++i) {
+        const float wr = __int_as_float(__builtin_amdgcn_ds_bpermute((rg + 4 * i) * 4, __float_as_int(w)));
+        a += wr * orow[i];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] = rows4_sum(a[e]);
+    if (rg == 0 && has_col) store_out4<DT>(prm.out, hrow * D + col, a * (1.f / L));
     if (prm.lse && slice == 0 && lane == 0) prm.lse[hrow] = (M + log2f(L)) * kLn2;
 }
 
