@@ -90,11 +90,11 @@ enum {
  * (rotary_mode 0) is the plain operation. */
 typedef struct pa_decode_desc {
     int32_t num_q_heads;     /* Hq > 0 */
-    int32_t num_kv_heads;    /* Hkv > 0, divides Hq */
+    int32_t num_kv_heads;    /* Hkv > 0, divides Hq, <= 65535 */
     int32_t head_dim;        /* D */
     int32_t page_size;       /* tokens per page */
     int32_t dtype;           /* PA_DTYPE_* of q, k/v cache and out */
-    int32_t max_batch;       /* upper bound of args.batch */
+    int32_t max_batch;       /* upper bound of args.batch, <= 65535 (UNSUPPORTED above) */
     int32_t max_context_len; /* upper bound of args.max_context_len */
     int32_t device;          /* HIP device ordinal the handle runs on (the handle */
                              /*   allocates 4 bytes there with debug_checks)    */

@@ -66,6 +66,9 @@ int check_desc(const pa_decode_desc& d)
     int G = d.num_q_heads / d.num_kv_heads;
     if (G > kMaxGroup || template_group(G) == 0)
         return PA_DECODE_UNSUPPORTED;
+    // Sequences and KV heads index the y / z dimensions of the launch grids.
+    if (d.max_batch > kMaxGridYZ || d.num_kv_heads > kMaxGridYZ)
+        return PA_DECODE_UNSUPPORTED;
     return PA_DECODE_OK;
 }
 

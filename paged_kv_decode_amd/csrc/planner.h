@@ -25,6 +25,8 @@ constexpr int kMergeThreads = 256;
 // Partition counts up to this use the merge with one wave per (sequence,
 // query head, 64-dim slice); its grid is ceil(B * Hq * D/64 / 4) workgroups.
 constexpr int kMergeWaveMaxPartitions = 64;
+// Largest y / z launch-grid dimension (sequences, KV heads).
+constexpr int kMaxGridYZ = 65535;
 
 // Bytes per element of a PA_DTYPE_* code (0 when unknown).
 int dtype_bytes(int dtype);

@@ -52,6 +52,8 @@ def test_status_strings():
     (dict(dtype=B.PA_DTYPE_F32, head_dim=128), B.PA_DECODE_UNSUPPORTED),
     (dict(num_q_heads=32, num_kv_heads=1), B.PA_DECODE_UNSUPPORTED),
     (dict(max_batch=-1), B.PA_DECODE_INVALID_ARG),
+    (dict(max_batch=65536), B.PA_DECODE_UNSUPPORTED),
+    (dict(num_q_heads=65536 * 2, num_kv_heads=65536), B.PA_DECODE_UNSUPPORTED),
     (dict(rotary_mode=2, rope_theta=1e4, rope_scale=1.0), B.PA_DECODE_INVALID_ARG),
     (dict(rotary_mode=-1), B.PA_DECODE_INVALID_ARG),
     (dict(rotary_mode=1, rope_theta=0.0, rope_scale=1.0), B.PA_DECODE_INVALID_ARG),
