@@ -218,8 +218,11 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
     partial_us = 1e3 * pm / max(pn, 1)
     merge_us = 1e3 * mm / max(mn, 1) if mn else 0.0
 
+    ceiling = same_pages_probe(reps, p, min(steps, 500), sp) if layers == 1 else None
+
     res = {
         "workload": name, "p": p, "plan": plan, "kv_bytes": kv_bytes * L, "replicas": R,
+        "read_ceiling": ceiling,
         "layers": L, "ms_per_step": ms_per_step, "us_per_step": 1e3 * ms_per_step,
         "us_per_layer": 1e3 * ms_per_step / L,
         "gbps": kv_bytes * L / (ms_per_step * 1e-3) / 1e9,
@@ -230,6 +233,90 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
     del reps
     torch.cuda.empty_cache()
     return res
+
+
+def chunk_addresses(p: W.Problem, k: torch.Tensor, v: torch.Tensor, pt: torch.Tensor):
+    """Device addresses of every KV chunk (one KV head's slice of one page) a
+    decode step over `p` reads from caches k, v with page table pt: per
+    (sequence, KV head), its visible pages in order, K then V per page."""
+    eb = k.element_size()
+    B = p.q.shape[0]
+    Hkv = k.shape[1]
+    lens = p.context_lens.tolist()
+    rows = []
+    for b in range(B):
+        n = lens[b]
+        lo = n - p.window if (p.window > 0 and n > p.window) else 0
+        if n <= lo:
+            continue
+        ids = pt[b, lo // W.PAGE_SIZE:(n + W.PAGE_SIZE - 1) // W.PAGE_SIZE].long()
+        for h in range(Hkv):
+            off = (ids * k.stride(0) + h * k.stride(1)) * eb
+            rows.append(torch.stack([k.data_ptr() + off, v.data_ptr() + off], 1).reshape(-1))
+    if not rows:
+        return torch.zeros(0, dtype=torch.int64, device=k.device)
+    return torch.cat(rows).contiguous()
+
+
+def same_pages_probe(reps, p: W.Problem, launches: int, stream_ptr: int):
+    """Read-rate ceiling next to the kernel: pa_decode_read_probe reading
+    exactly the KV chunks a step reads (same replicas, same cold-cache
+    rotation, graph-replayed like the steps), and a plain contiguous read of
+    1 GiB.  Returns None when the chunk size is not one the probe takes."""
+    D = p.q.shape[2]
+    chunk = W.PAGE_SIZE * D * p.k_cache.element_size()
+    if chunk not in (2048, 3072, 4096, 8192) or p.k_cache.stride(2) != D:
+        return None   # a head's page slice must be one contiguous chunk
+    lists = [chunk_addresses(p, k, v, pt) for k, v, pt in reps.caches]
+    n = int(lists[0].numel())
+    if n == 0:
+        return None
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    R = len(lists)
+
+    def probe(i, sp):
+        binding.pa_decode_read_probe(0, lists[i % R].data_ptr(), n, chunk, sink.data_ptr(), sp)
+
+    stream = torch.cuda.current_stream()
+    for i in range(2 * R):
+        probe(i, stream_ptr)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            cs = torch.cuda.current_stream().cuda_stream
+            for i in range(launches):
+                probe(i, cs)
+    stream.wait_stream(cap)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * a.elapsed_time(b) / launches
+    read_bytes = n * chunk
+
+    # Contiguous 1 GiB, 8 KiB chunks.
+    big = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    big.fill_(3)
+    nb = (1 << 30) // 8192
+    for _ in range(3):
+        binding.pa_decode_read_probe(big.data_ptr(), 0, nb, 8192, sink.data_ptr(), stream_ptr)
+    a.record(stream)
+    reps_c = 10
+    for _ in range(reps_c):
+        binding.pa_decode_read_probe(big.data_ptr(), 0, nb, 8192, sink.data_ptr(), stream_ptr)
+    b.record(stream)
+    torch.cuda.synchronize()
+    contig = (1 << 30) * reps_c / (1e-3 * a.elapsed_time(b)) / 1e9
+    del big
+    return {"same_pages_us": round(us, 3), "same_pages_bytes": read_bytes,
+            "same_pages_GBps": round(read_bytes / (us * 1e-6) / 1e9, 1),
+            "contiguous_GBps": round(contig, 1)}
 
 
 def parity(res):
@@ -334,6 +421,7 @@ def main():
             "plan": {k: r["plan"][k] for k in ("partition_size", "num_partitions",
                                                "waves_per_group", "split")},
             "parity": {"out_rel_l2": rel, "lse_max_abs_err": lerr},
+            "read_ceiling": r["read_ceiling"],
         }
         log("%s: %.2f us/step, %.0f GB/s; partial %.2f us (%.0f GB/s), merge %.2f us; "
             "rel_l2 %.2g" % (name, r["us_per_step"], r["gbps"], r["partial_us"],
@@ -379,7 +467,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
                      "traffic": traffic,
                      "kernel": "partial_kernel", "kernel_us": round(main_res["partial_us"], 3),
-                     "merge_us": round(main_res["merge_us"], 3)},
+                     "merge_us": round(main_res["merge_us"], 3),
+                     "read_ceiling": main_res["read_ceiling"]},
         "cpu_baseline": cpu,
         "parity": {"out_rel_l2": rel, "lse_max_abs_err": lerr},
         "also": also,

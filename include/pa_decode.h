@@ -295,6 +295,24 @@ int pa_decode_profile_begin(pa_decode_handle handle, int32_t max_launches);
 int pa_decode_profile_end(pa_decode_handle handle, double* partial_ms, int32_t* partial_launches,
                           double* merge_ms, int32_t* merge_launches);
 
+/* Measurement tool (not part of the decode step): the memory system's read
+ * rate for a set of KV chunks, e.g. the pages a decode step reads.  Reads
+ * num_chunks chunks of chunk_bytes bytes each (2048, 3072, 4096 or 8192:
+ * one KV head's slice of a page, 16 tokens x D x element size) on `stream`
+ * (the current device), with the partial kernel's 16-byte streaming load,
+ * one wave per SIMD with 24-32 KiB in flight each.  Chunk i starts at chunk_addrs[i] (a
+ * device array of device addresses, each 16-byte aligned, whole chunks
+ * inside one allocation), or at base + i * chunk_bytes when chunk_addrs is
+ * NULL (base 16-byte aligned).  *sink (device, 4 bytes) is XORed with the
+ * XOR of every 32-bit word read (one atomic per workgroup), which uses the data
+ * and lets a caller check what was read; clear it first to get that XOR.
+ * Calls that share a sink must not overlap.  Asynchronous; the caller
+ * times it.  Errors: INVALID_ARG (null sink, num_chunks < 0, other chunk
+ * sizes, no base and no chunk_addrs, base misaligned), HIP_ERROR (launch
+ * failed). */
+int pa_decode_read_probe(const void* base, const uint64_t* chunk_addrs, int32_t num_chunks,
+                         int32_t chunk_bytes, uint32_t* sink, void* stream);
+
 /* Last hipError_t recorded on the handle (0 when none). */
 int pa_decode_last_hip_error(pa_decode_handle handle);
 

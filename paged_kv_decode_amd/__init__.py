@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     pa_decode_plan_query,
     pa_decode_profile_begin,
     pa_decode_profile_end,
+    pa_decode_read_probe,
     pa_decode_run,
     pa_decode_status_string,
     pa_decode_workspace_size,

@@ -37,7 +37,7 @@ EXPORTED = ["pa_decode_create", "pa_decode_destroy", "pa_decode_workspace_size",
             "pa_decode_profile_begin", "pa_decode_profile_end",
             "pa_decode_last_hip_error", "pa_decode_status_string",
             "pa_decode_workspace_size_csr", "pa_decode_run_csr", "pa_decode_plan_query_csr",
-            "pa_decode_debug_status"]
+            "pa_decode_debug_status", "pa_decode_read_probe"]
 
 
 class PaDecodeDesc(ctypes.Structure):
@@ -137,6 +137,7 @@ def load_library(path: Optional[str] = None):
                                                  ctypes.POINTER(PaDecodePlan)]
         lib.pa_decode_last_hip_error.argtypes = [vp]
         lib.pa_decode_debug_status.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
+        lib.pa_decode_read_probe.argtypes = [vp, vp, i32, i32, vp, vp]
         lib.pa_decode_status_string.argtypes = [ctypes.c_int]
         lib.pa_decode_status_string.restype = ctypes.c_char_p
         for name in EXPORTED:
@@ -256,6 +257,17 @@ def pa_decode_debug_status(handle) -> int:
     _check(load_library().pa_decode_debug_status(handle, ctypes.byref(v)),
            "pa_decode_debug_status")
     return int(v.value)
+
+
+def pa_decode_read_probe(base: int, chunk_addrs: int, num_chunks: int, chunk_bytes: int,
+                         sink: int, stream: int = 0) -> None:
+    """Measurement tool: read num_chunks chunks (device addresses in the
+    uint64 device array at chunk_addrs, or contiguous from base when
+    chunk_addrs is 0) on `stream`; the device uint32 at sink is XORed with
+    the XOR of every 32-bit word read."""
+    _check(load_library().pa_decode_read_probe(base or None, chunk_addrs or None, num_chunks,
+                                               chunk_bytes, sink or None, stream or None),
+           "pa_decode_read_probe")
 
 
 def make_desc(num_q_heads, num_kv_heads, head_dim, dtype, max_batch, max_context_len,

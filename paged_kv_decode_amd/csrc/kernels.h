@@ -73,6 +73,13 @@ hipError_t launch_partial(int dtype, int head_dim, int group_t, const PartialPar
 hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, dim3 grid, dim3 block,
                         hipStream_t stream, LaunchEvents ev);
 
+// Read probe (measurement): reads num_chunks chunks of kpc * 1024 bytes
+// (kpc in {2, 3, 4, 8}) with the partial kernel's streaming load; chunk i at
+// chunk_addrs[i], or at base + i * chunk bytes when chunk_addrs is null;
+// *sink is XORed with the XOR of every 32-bit word read.
+hipError_t launch_read_probe(const void* base, const uint64_t* chunk_addrs, int32_t num_chunks,
+                             int kpc, uint32_t* sink, hipStream_t stream);
+
 // Waves of the partial kernel (256-thread workgroups with `lds_bytes` of
 // dynamic LDS, with or without rotary) that one compute unit holds at once;
 // 0 when unknown.

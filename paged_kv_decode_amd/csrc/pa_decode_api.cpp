@@ -460,6 +460,20 @@ int pa_decode_run_csr(pa_decode_handle handle, const pa_decode_csr_args* args, v
     return launch_step(handle, c, src, plan, stream);
 }
 
+int pa_decode_read_probe(const void* base, const uint64_t* chunk_addrs, int32_t num_chunks,
+                         int32_t chunk_bytes, uint32_t* sink, void* stream)
+{
+    if (!sink || num_chunks < 0 || (!base && !chunk_addrs && num_chunks > 0))
+        return PA_DECODE_INVALID_ARG;
+    if (chunk_bytes != 2048 && chunk_bytes != 3072 && chunk_bytes != 4096 && chunk_bytes != 8192)
+        return PA_DECODE_INVALID_ARG;
+    if (base && !aligned16(base))
+        return PA_DECODE_INVALID_ARG;
+    const hipError_t e = pa::launch_read_probe(base, chunk_addrs, num_chunks, chunk_bytes / 1024,
+                                               sink, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_DECODE_OK : PA_DECODE_HIP_ERROR;
+}
+
 int pa_decode_debug_status(pa_decode_handle handle, int32_t* status)
 {
     if (!handle || !status || !handle->status_word)

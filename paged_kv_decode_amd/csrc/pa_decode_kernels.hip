@@ -1204,6 +1204,80 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(const MergeParams prm, 
     if (prm.lse && slice == 0 && lane == 0) prm.lse[hrow] = (M + log2f(L)) * kLn2;
 }
 
+// ---------------------------------------------------------------------------
+// Read probe (a measurement tool, not part of the decode step): the rate at
+// which the memory system delivers a given set of KV chunks to the same
+// streaming load the partial kernel uses.  One wave per SIMD (1024 waves;
+// on MI355X more waves measured slower: 8192 waves read a 100k-token page
+// set at 3.5 TB/s against 6.2 TB/s with 1024).  Each wave reads U chunks
+// (24-32 KiB) at a time, all issued before the first use, and folds them
+// into an XOR; at the end each workgroup XORs its result into *sink, so the
+// reads are used and can be checked.
+// ---------------------------------------------------------------------------
+template <int KPC>
+__global__ __launch_bounds__(256) void read_probe_kernel(const char* base,
+                                                         const uint64_t* chunk_addrs,
+                                                         int32_t num_chunks, uint32_t* sink)
+{
+    constexpr int CB = KPC * kWave * 16;   // chunk bytes
+    constexpr int U = KPC >= 8 ? 4 : KPC >= 3 ? 8 : 16;   // chunks in flight per wave (24-32 KiB)
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x / kWave) +
+                                                 threadIdx.x / kWave);
+    const int nwv = gridDim.x * (blockDim.x / kWave);
+    typedef __attribute__((address_space(1))) const u32x4 gvec;   // global memory
+    // Lane u (< U) holds the address of chunk c0 + u (past the end: the
+    // last chunk, re-read but not counted); the next pass's addresses are
+    // loaded while this pass's data is in flight.
+    auto chunk_addr = [&](int c0) -> uint64_t {
+        const int c = min(c0 + (lane & (U - 1)), num_chunks - 1);
+        return chunk_addrs ? chunk_addrs[c] : reinterpret_cast<uint64_t>(base) + uint64_t(c) * CB;
+    };
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    uint64_t av = w * U < num_chunks ? chunk_addr(w * U) : 0;
+    for (int c0 = w * U; c0 < num_chunks; c0 += nwv * U) {
+        uint64_t addr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(av), u);
+            const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(av >> 32), u);
+            addr[u] = (uint64_t(hi) << 32) | lo;
+        }
+        const int cn = c0 + nwv * U;
+        if (cn < num_chunks)
+            av = chunk_addr(cn);
+        u32x4 r[U][KPC];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int k = 0; k < KPC; ++k)
+                r[u][k] = __builtin_nontemporal_load(
+                    reinterpret_cast<gvec*>(addr[u] + uint64_t((k * kWave + lane) * 16)));
+        pin_loads();   // all U * KPC loads in flight before the first use
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const bool counted = c0 + u < num_chunks;
+#pragma unroll
+            for (int k = 0; k < KPC; ++k) acc ^= counted ? r[u][k] : z;
+        }
+    }
+    uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off);
+    // One atomic per workgroup that read anything (atomics on one word
+    // serialise: one per wave cost microseconds on small chunk sets).
+    __shared__ uint32_t red[4];
+    if (lane == 0)
+        red[threadIdx.x / kWave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0 && int(blockIdx.x) * int(blockDim.x / kWave) * U < num_chunks) {
+        uint32_t y = 0;
+        for (int i = 0; i < int(blockDim.x / kWave); ++i) y ^= red[i];
+        __hip_atomic_fetch_xor(sink, y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // Launch through hipExtLaunchKernelGGL so optional start/stop events bracket
 // the kernel itself.
 template <typename K, typename... Args>
@@ -1333,6 +1407,27 @@ hipError_t launch_merge_t(const MergeParams& p, dim3 grid, dim3 block, hipStream
         return launch(merge_wave_kernel<DT, D, 64>, grid, block, 0, stream, ev, p, units);
     }
     return launch(merge_kernel<DT, D>, grid, block, 0, stream, ev, p);
+}
+
+hipError_t launch_read_probe(const void* base, const uint64_t* chunk_addrs, int32_t num_chunks,
+                             int kpc, uint32_t* sink, hipStream_t stream)
+{
+    if (num_chunks <= 0)
+        return hipSuccess;
+    // At most 256 workgroups of 4 waves (one wave per SIMD of 256 compute
+    // units); waves loop over their chunks.
+    const int64_t waves = (int64_t(num_chunks) + 3) / 4;
+    const int64_t groups = (waves + 3) / 4;
+    const dim3 grid(unsigned(groups < 256 ? groups : 256)), block(256);
+    const char* b = static_cast<const char*>(base);
+    switch (kpc) {
+    case 2: hipLaunchKernelGGL(read_probe_kernel<2>, grid, block, 0, stream, b, chunk_addrs, num_chunks, sink); break;
+    case 3: hipLaunchKernelGGL(read_probe_kernel<3>, grid, block, 0, stream, b, chunk_addrs, num_chunks, sink); break;
+    case 4: hipLaunchKernelGGL(read_probe_kernel<4>, grid, block, 0, stream, b, chunk_addrs, num_chunks, sink); break;
+    case 8: hipLaunchKernelGGL(read_probe_kernel<8>, grid, block, 0, stream, b, chunk_addrs, num_chunks, sink); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, dim3 grid, dim3 block,

@@ -74,6 +74,19 @@ def test_create_rejects_invalid_descriptions(fields, status):
     assert not h.value
 
 
+def test_read_probe_rejects_bad_arguments_on_the_host():
+    # Each case fails before anything touches a device.
+    sink = ctypes.c_void_p(256)
+    probe = lib().pa_decode_read_probe
+    assert probe(ctypes.c_void_p(256), None, 4, 2048, None, None) == B.PA_DECODE_INVALID_ARG
+    assert probe(ctypes.c_void_p(256), None, -1, 2048, sink, None) == B.PA_DECODE_INVALID_ARG
+    assert probe(ctypes.c_void_p(256), None, 4, 1024, sink, None) == B.PA_DECODE_INVALID_ARG
+    assert probe(ctypes.c_void_p(256), None, 4, 16384, sink, None) == B.PA_DECODE_INVALID_ARG
+    assert probe(None, None, 4, 2048, sink, None) == B.PA_DECODE_INVALID_ARG
+    assert probe(ctypes.c_void_p(264), None, 4, 2048, sink, None) == B.PA_DECODE_INVALID_ARG
+    assert probe(ctypes.c_void_p(256), None, 0, 2048, sink, None) == B.PA_DECODE_OK
+
+
 def test_null_arguments_are_rejected():
     assert lib().pa_decode_debug_status(None, None) == B.PA_DECODE_INVALID_ARG
     assert lib().pa_decode_create(None, None) == B.PA_DECODE_INVALID_ARG
