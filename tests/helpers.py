@@ -75,8 +75,11 @@ def run_oracle(p: W.Problem):
                          window=p.window, rotary=p.workload.rope)
 
 
-def compare(out, lse, ref_out, ref_lse, dtype, what=""):
-    """Assert the tolerances above; returns (rel_l2, lse_max_abs_err)."""
+def compare(out, lse, ref_out, ref_lse, dtype, what="", lse_rel=0.0):
+    """Assert the tolerances above; returns (rel_l2, lse_max_abs_err).
+    lse_rel > 0 widens the lse bound to LSE_TOL + lse_rel * |lse| per entry
+    (for scores far from order 1, where float32 itself carries an error
+    proportional to the magnitude)."""
     ref_r = torch.from_numpy(ref_out).to(dtype).double()
     g = out.double()
     assert torch.isfinite(g).all(), "%s: non-finite output" % what
@@ -88,5 +91,10 @@ def compare(out, lse, ref_out, ref_lse, dtype, what=""):
     fin = ~inf_ref
     lerr = float(np.abs(lse_d[fin] - ref_lse[fin]).max()) if fin.any() else 0.0
     assert rel <= OUT_TOL[dtype], "%s: out rel-L2 %.3g > %.3g" % (what, rel, OUT_TOL[dtype])
-    assert lerr <= LSE_TOL, "%s: lse abs err %.3g > %.3g" % (what, lerr, LSE_TOL)
+    if lse_rel > 0:
+        bound = LSE_TOL + lse_rel * np.abs(ref_lse[fin])
+        worst = float((np.abs(lse_d[fin] - ref_lse[fin]) / bound).max()) if fin.any() else 0.0
+        assert worst <= 1.0, "%s: lse err %.3g above %.0f%% of its bound" % (what, lerr, 100 * worst)
+    else:
+        assert lerr <= LSE_TOL, "%s: lse abs err %.3g > %.3g" % (what, lerr, LSE_TOL)
     return rel, lerr

@@ -296,3 +296,51 @@ def test_batch_of_512_short_ragged_sequences():
     w = W.custom(batch=512, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype=torch.float16,
                  context_lens=lens, seed=612)
     _check(W.generate(w), what="batch 512")
+
+
+@pytest.mark.parametrize("scale", [0.0, 1e-4, -0.5, 2.0, 8.0])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_extreme_score_scales(scale, dtype):
+    """Score ranges from flat (scale 0: out = mean of V, lse = ln n) to very
+    peaked (scale 8 on N(0,1) data: scores up to ~300 apart, so the softmax
+    reference value jumps many times), negative scale included; several
+    partitions and a ragged tail.  The lse bound grows with |lse| (1e-4 +
+    1e-6 |lse|): at |lse| ~ 400 float32 spacing alone is 3e-5, and a float32
+    q.k over 128 terms of size ~8 carries ~1e-5 absolute error before the
+    scale multiplies it."""
+    w = W.custom(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype=dtype,
+                 context_lens=[3001, 517, 64], seed=620)
+    p = dataclasses.replace(W.generate(w), scale=scale)
+    ref_out, ref_lse = run_oracle(p)
+    for S in (None, 128):
+        out, lse, plan = run_gpu(p, partition_size=S)
+        rel, lerr = compare(out, lse, ref_out, ref_lse, dtype, "scale %g S=%s" % (scale, S),
+                            lse_rel=1e-6)
+        print("scale %g %s S=%s rel_l2=%.3g lse_err=%.3g" % (scale, dtype, S, rel, lerr),
+              flush=True)
+
+
+def test_batch_permutation_permutes_outputs_bitwise():
+    """Sequences are independent: reordering the batch (q rows, page-table
+    rows, lengths) reorders out and lse, bit for bit (the plan depends only
+    on the batch size and the longest context, which do not change)."""
+    p = W.generate(W.CONFIGS["llama8b_b16_ragged_f16"])
+    out, lse, plan = run_gpu(p)
+    perm = torch.randperm(p.q.shape[0], generator=torch.Generator().manual_seed(621))
+    pp = dataclasses.replace(p, q=p.q[perm].contiguous(), page_table=p.page_table[perm].contiguous(),
+                             context_lens=p.context_lens[perm].contiguous())
+    out2, lse2, plan2 = run_gpu(pp)
+    assert plan2 == plan
+    assert torch.equal(out2, out[perm]) and torch.equal(lse2, lse[perm])
+
+
+def test_aliased_pages_in_the_dense_table():
+    """Two sequences whose page-table rows point at the same physical pages
+    (a shared prefix) read them independently; both match the oracle."""
+    w = W.custom(batch=3, num_q_heads=16, num_kv_heads=4, head_dim=64, dtype=torch.float16,
+                 context_lens=[900, 900, 400], seed=622)
+    p = W.generate(w)
+    pt = p.page_table.clone()
+    pt[1, :40] = pt[0, :40]          # 640 shared tokens, then its own pages
+    pt[2, :25] = pt[0, :25]          # the whole of sequence 2 is a prefix of sequence 0
+    _check(dataclasses.replace(p, page_table=pt), what="aliased pages")
