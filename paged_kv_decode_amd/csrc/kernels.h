@@ -80,9 +80,10 @@ hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, dim3 grid
 hipError_t launch_read_probe(const void* base, const uint64_t* chunk_addrs, int32_t num_chunks,
                              int kpc, uint32_t* sink, hipStream_t stream);
 
-// Waves of the partial kernel (256-thread workgroups with `lds_bytes` of
-// dynamic LDS, with or without rotary) that one compute unit holds at once;
-// 0 when unknown.
-int partial_waves_per_cu(int dtype, int head_dim, int group_t, bool rotary, size_t lds_bytes);
+// Waves of the partial kernel (workgroups of `waves` waves with `lds_bytes`
+// of dynamic LDS, with or without rotary) that one compute unit holds at
+// once; 0 when unknown.
+int partial_waves_per_cu(int dtype, int head_dim, int group_t, bool rotary, int waves,
+                         size_t lds_bytes);
 
 }  // namespace pa

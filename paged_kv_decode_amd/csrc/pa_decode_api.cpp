@@ -269,14 +269,14 @@ int pa_decode_create(const pa_decode_desc* desc, pa_decode_handle* handle)
     h->desc = *desc;
     h->num_cus = cus;
     {
-        // Occupancy of the partial kernel this description uses, for a
-        // four-wave workgroup.
+        // Occupancy of the partial kernel this description uses, for the
+        // largest workgroup the planner gives it.
         pa_decode_plan probe = {};
-        probe.waves_per_group = pa::kMaxWavesPerGroup;
+        probe.waves_per_group = pa::workgroup_waves(*desc);
         probe.pages_per_block = pa::pages_per_block(desc->head_dim, desc->dtype);
         const int G = desc->num_q_heads / desc->num_kv_heads;
         int w = pa::partial_waves_per_cu(desc->dtype, desc->head_dim, pa::template_group(G),
-                                         desc->rotary_mode == 1,
+                                         desc->rotary_mode == 1, probe.waves_per_group,
                                          pa::partial_lds_bytes(*desc, probe));
         h->waves_per_cu = w > 0 ? w : 8;
     }

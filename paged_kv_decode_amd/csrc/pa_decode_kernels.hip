@@ -1310,27 +1310,27 @@ hipError_t launch_partial_t(bool rot, const PartialParams& p, dim3 grid, dim3 bl
 }
 
 template <int DT, int D, int G>
-int waves_per_cu_t(bool rot, size_t lds)
+int waves_per_cu_t(bool rot, int waves, size_t lds)
 {
     constexpr int NB = pages_per_block_t<DT, D>();
     const void* k = rot ? reinterpret_cast<const void*>(partial_kernel<DT, D, G, NB, true>)
                         : reinterpret_cast<const void*>(partial_kernel<DT, D, G, NB, false>);
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, 256, lds) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, waves * kWave, lds) != hipSuccess)
         return 0;
-    return blocks * 4;
+    return blocks * waves;
 }
 
 template <int DT, int D>
-int waves_per_cu_g(int group_t, bool rot, size_t lds)
+int waves_per_cu_g(int group_t, bool rot, int waves, size_t lds)
 {
     switch (group_t) {
-    case 1: return waves_per_cu_t<DT, D, 1>(rot, lds);
-    case 2: return waves_per_cu_t<DT, D, 2>(rot, lds);
-    case 4: return waves_per_cu_t<DT, D, 4>(rot, lds);
-    case 6: return waves_per_cu_t<DT, D, 6>(rot, lds);
-    case 8: return waves_per_cu_t<DT, D, 8>(rot, lds);
-    case 16: return waves_per_cu_t<DT, D, 16>(rot, lds);
+    case 1: return waves_per_cu_t<DT, D, 1>(rot, waves, lds);
+    case 2: return waves_per_cu_t<DT, D, 2>(rot, waves, lds);
+    case 4: return waves_per_cu_t<DT, D, 4>(rot, waves, lds);
+    case 6: return waves_per_cu_t<DT, D, 6>(rot, waves, lds);
+    case 8: return waves_per_cu_t<DT, D, 8>(rot, waves, lds);
+    case 16: return waves_per_cu_t<DT, D, 16>(rot, waves, lds);
     default: return 0;
     }
 }
@@ -1374,9 +1374,10 @@ hipError_t launch_partial(int dtype, int head_dim, int group_t, const PartialPar
     return hipErrorInvalidValue;
 }
 
-int partial_waves_per_cu(int dtype, int head_dim, int group_t, bool rotary, size_t lds)
+int partial_waves_per_cu(int dtype, int head_dim, int group_t, bool rotary, int waves,
+                         size_t lds)
 {
-#define PA_OCC(DT, D) return waves_per_cu_g<DT, D>(group_t, rotary, lds);
+#define PA_OCC(DT, D) return waves_per_cu_g<DT, D>(group_t, rotary, waves, lds);
     if (dtype == PA_DTYPE_F32 && head_dim == 64) { PA_OCC(PA_DTYPE_F32, 64) }
     if (dtype == PA_DTYPE_F16) {
         if (head_dim == 64) { PA_OCC(PA_DTYPE_F16, 64) }

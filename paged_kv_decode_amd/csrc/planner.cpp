@@ -74,6 +74,29 @@ int check_desc(const pa_decode_desc& d)
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Waves per workgroup of the partial kernel: four, fewer when the K/V tiles
+// or the combine buffer would pass 64 KiB of LDS, or (rotary) when the
+// workgroup's tiles and tables would pass 80 KiB.
+int workgroup_waves(const pa_decode_desc& d)
+{
+    const int ps = d.page_size;
+    const int nb = pages_per_block(d.head_dim, d.dtype);
+    const int G = d.num_q_heads / d.num_kv_heads;
+    int nw = kMaxWavesPerGroup;
+    const int Gt = template_group(G);
+    const int gp4 = (Gt + 3) / 4 * 4;
+    const int64_t comb = int64_t(2 * gp4 + Gt * d.head_dim) * 4;
+    const int64_t tiles = int64_t(2) * nb * ps * 16 * tile_row_slots(d.head_dim, d.dtype);
+    const int64_t per_wave = std::max(comb, tiles);
+    while (nw > 1 && nw * per_wave > 65536) nw /= 2;
+    // With rotary, also keep the workgroup (tiles, base tables, offset
+    // table) within half of the compute unit's 160 KiB, so that two
+    // workgroups share a compute unit.
+    while (nw > 1 && nw * (tiles + rotary_table_bytes(d)) + rotary_offset_table_bytes(d) > 81920)
+        nw /= 2;
+    return nw;
+}
+
 WorkspaceLayout workspace_layout(const pa_decode_desc& d, int batch, int num_partitions)
 {
     auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
@@ -103,7 +126,6 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
 
     const int ps = d.page_size;
     const int nb = pages_per_block(d.head_dim, d.dtype);
-    const int G = d.num_q_heads / d.num_kv_heads;
     const int64_t units = int64_t(std::max(batch, 1)) * d.num_kv_heads;
     const bool windowed = sliding_window > 0 && sliding_window < max_context_len;
     const int64_t visible = windowed ? sliding_window : max_context_len;
@@ -122,15 +144,18 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
     const int per_cu = (d.rotary_mode == 1 && batch > 1) ? 8 : 4;
     const int64_t target = std::min<int64_t>(capacity, int64_t(num_cus) * per_cu);
 
+    int nw = workgroup_waves(d);
     int64_t S;
     if (partition_size > 0) {
         S = partition_size;
     } else {
-        // Pages per wave so that `target` waves cover the work, four waves
-        // sharing a partition; at least one page per wave and at most 64.
+        // Pages per wave so that `target` waves cover the work, a
+        // workgroup's waves (nw, fewer than four only for head_dim-256
+        // rotary) sharing a partition; at least one page per wave and at
+        // most 64.
         int64_t ppw = std::max<int64_t>(1, ceil_div(units * vis_pages, target));
         ppw = std::min<int64_t>(ppw, 64);
-        S = int64_t(kMaxWavesPerGroup) * ppw * ps;
+        S = int64_t(nw) * ppw * ps;
     }
     int64_t P;
     if (max_context_len == 0) {
@@ -149,23 +174,6 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
         S = ceil_div(max_context_len, ps) * ps;
     }
 
-    // Waves per workgroup: four, fewer when the K/V tiles or the combine
-    // buffer would pass 64 KiB of LDS.
-    int nw = kMaxWavesPerGroup;
-    {
-        const int Gt = template_group(G);
-        const int gp4 = (Gt + 3) / 4 * 4;
-        const int64_t comb = int64_t(2 * gp4 + Gt * d.head_dim) * 4;
-        const int64_t tiles = int64_t(2) * nb * ps * 16 * tile_row_slots(d.head_dim, d.dtype);
-        const int64_t per_wave = std::max(comb, tiles);
-        while (nw > 1 && nw * per_wave > 65536) nw /= 2;
-        // With rotary, also keep the workgroup (tiles, base tables, offset
-        // table) within half of the compute unit's 160 KiB, so that two
-        // workgroups share a compute unit.
-        while (nw > 1 &&
-               nw * (tiles + rotary_table_bytes(d)) + rotary_offset_table_bytes(d) > 81920)
-            nw /= 2;
-    }
     // Waves sharing one partition: the count (1, 2 or 4, at most one per
     // block of the partition) whose grid total is closest to `target` and
     // fits in one round of resident waves.

@@ -64,6 +64,9 @@ int make_plan_csr(const pa_decode_desc& d, int num_cus, int waves_per_cu, int ba
 
 // LDS bytes of one wave's rotary base table (0 without rotary): the (cos,
 // sin) of every frequency at each page of a block.
+// Waves per workgroup of the partial kernel for this description (1, 2 or 4;
+// LDS-limited).
+int workgroup_waves(const pa_decode_desc& d);
 int64_t rotary_table_bytes(const pa_decode_desc& d);
 
 // LDS bytes of a workgroup's rotary offset table (0 without rotary): the
