@@ -3,7 +3,10 @@
 // Host side of one decode step: validate the arguments (no HIP call before
 // that), plan the partitioning for the device's compute units, launch the
 // partial kernel and, when the context is split, the merge kernel, all on the
-// caller's stream.  Nothing here synchronises or allocates device memory.
+// caller's stream.  pa_decode_run / pa_decode_run_csr neither synchronise nor
+// allocate; device memory is allocated only at create (the 4-byte status
+// word, with desc.debug_checks), and only pa_decode_debug_status and
+// pa_decode_profile_end wait for the device.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
