@@ -319,3 +319,21 @@ def test_rotary_descriptions_are_planned(dtype, head_dim):
         if p1.split:
             assert p1.workspace_bytes >= batch * 32 * p1.num_partitions * (head_dim + 2) * 4
 
+
+
+@pytest.mark.parametrize("dtype", [B.PA_DTYPE_F16, B.PA_DTYPE_BF16])
+@pytest.mark.parametrize("waves_per_cu", [4, 6, 8])
+def test_plans_fill_their_wave_target_with_two_wave_workgroups(dtype, waves_per_cu):
+    """head_dim-256 rotary workgroups hold two waves (LDS); partitions are
+    sized for those two waves, so a long batch launches the targeted wave
+    count (one per resident slot, at most eight per compute unit), not half
+    of it."""
+    d = B.PaDecodeDesc(num_q_heads=16, num_kv_heads=4, head_dim=256, page_size=16, dtype=dtype,
+                       max_batch=64, max_context_len=1 << 17, device=0, rotary_mode=1,
+                       rope_theta=500000.0, rope_scale=1.0)
+    p = B.pa_decode_plan_query(d, 256, waves_per_cu, 8, 8192, 0, 0)
+    assert p.waves_per_group == 2
+    waves = p.grid_partial[0] * p.grid_partial[1] * p.grid_partial[2] * p.waves_per_group
+    target = 256 * min(waves_per_cu, 8)
+    assert target * 0.9 <= waves <= target
+    assert covered(p, 8192, 0)
