@@ -1054,10 +1054,11 @@ template <> __device__ __forceinline__ void store_out4<PA_DTYPE_BF16>(void* out,
 // and lane-swap reductions, no barrier).  For the outputs the 16 row groups
 // (4 per wave, 16 lanes each) take rows rg, rg + 16, ...; lane c4 of a row
 // group reads float4 column c4 of its rows, every load of a 256-row pass
-// issued before the first use.  The row groups of a wave are summed with
-// lane swaps and the four waves through LDS (one barrier).  Empty
-// partitions carry max = -inf and denominator 0 and get weight 0; rows past
-// P re-read row P - 1 with weight 0.
+// issued before the first use; a row's weight comes from the lane of the
+// same wave that holds its maximum and denominator.  The row groups of a
+// wave are summed with lane swaps and the four waves through LDS (one
+// barrier).  Empty partitions carry max = -inf and denominator 0 and get
+// weight 0; rows past P re-read row P - 1 with weight 0.
 // ---------------------------------------------------------------------------
 template <int DT, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams prm)
@@ -1078,15 +1079,13 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams prm)
 
     // First pass of rows, loaded before anything waits.
     f32x4 orow[RPT];
-    float mr[RPT], lr[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const uint32_t row = uint32_t(min(rg + 16 * i, P - 1));
         orow[i] = *reinterpret_cast<const f32x4*>(ob + (row * D + coff) * 4u);
-        mr[i] = m[row];
-        lr[i] = l[row];
     }
-    // Lane-strided maxima and denominators for the wave's own reductions.
+    // Lane-strided maxima and denominators (partition lane + 64 k) for the
+    // wave's own reductions and, by lane permutes, the first pass's weights.
     float ms[4], ls[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -1111,17 +1110,24 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams prm)
     // Phase 2: rescale_p = 2^(m_p - M) * l_p; their sum, and the weighted
     // outputs.
     auto weight = [&](float mp, float lp) { return lp > 0.f ? fast_exp2(mp - M) * lp : 0.f; };
-    float tl = 0.f;
+    float wk[4], tl = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        tl += lane + kWave * k < P ? weight(ms[k], ls[k]) : 0.f;
+    for (int k = 0; k < 4; ++k) {
+        wk[k] = lane + kWave * k < P ? weight(ms[k], ls[k]) : 0.f;
+        tl += wk[k];
+    }
     for (int p = lane + 4 * kWave; p < P; p += kWave) tl += weight(m[p], l[p]);
     const float L = rows4_sum(row16_sum(tl));
 
+    // Row rg + 16 i (< 256) is partition lane + 64 k of this wave with
+    // k = i / 4 and lane = rg + 16 (i % 4); rows past P carry weight 0 there.
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-        a += (rg + 16 * i < P ? weight(mr[i], lr[i]) : 0.f) * orow[i];
+    for (int i = 0; i < RPT; ++i) {
+        const float wr = __int_as_float(
+            __builtin_amdgcn_ds_bpermute((rg + 16 * (i & 3)) * 4, __float_as_int(wk[i >> 2])));
+        a += wr * orow[i];
+    }
     // Further passes (more than 256 partitions).
     for (int p = rg + 16 * RPT; p < P; p += 16) {
         const f32x4 o = *reinterpret_cast<const f32x4*>(ob + (uint32_t(p) * D + coff) * 4u);
