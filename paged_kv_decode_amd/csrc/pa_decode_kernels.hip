@@ -1049,13 +1049,16 @@ template <> __device__ __forceinline__ void store_out4<PA_DTYPE_BF16>(void* out,
 
 // ---------------------------------------------------------------------------
 // Merge kernel for any partition count: one 256-thread workgroup per (query
-// head, sequence, 64-column slice of head_dim).  Every wave finds the global
-// maximum and the rescaled denominator sum itself (lane-strided loads, DPP
-// and lane-swap reductions, no barrier).  For the outputs the 16 row groups
-// (4 per wave, 16 lanes each) take rows rg, rg + 16, ...; lane c4 of a row
-// group reads float4 column c4 of its rows, every load of a 256-row pass
-// issued before the first use; a row's weight comes from the lane of the
-// same wave that holds its maximum and denominator.  The row groups of a
+// head, sequence, 16-column slice of head_dim), so that even one sequence
+// spreads its reads over many compute units (the 100k workload: 24 heads x
+// 16 slices = 384 workgroups).  Every wave finds the global maximum and the
+// rescaled denominator sum itself (lane-strided loads, DPP and lane-swap
+// reductions, no barrier).  For the outputs the 64 row groups (16 per wave,
+// 4 lanes each) take rows rg, rg + 64, ...; lane c4 of a row group reads
+// float4 column c4 of the slice, every load of a 256-row pass issued before
+// the first use, and a row's weight comes by lane permute from the lane of
+// the same wave that holds its maximum and denominator (row rg + 64 i is
+// partition lane rg, k = i of the strided layout).  The row groups of a
 // wave are summed with lane swaps and the four waves through LDS (one
 // barrier).  Empty partitions carry max = -inf and denominator 0 and get
 // weight 0; rows past P re-read row P - 1 with weight 0.
@@ -1063,26 +1066,24 @@ template <> __device__ __forceinline__ void store_out4<PA_DTYPE_BF16>(void* out,
 template <int DT, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams prm)
 {
-    constexpr int RPT = 16;               // rows per lane per pass (16 row groups x 16 = 256)
-    __shared__ f32x4 part[4][16];
+    constexpr int RPT = 4;                // rows per lane per pass (64 row groups x 4 = 256)
+    __shared__ f32x4 part[4][4];
     const int h = blockIdx.x, b = blockIdx.y, dsl = blockIdx.z;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-    const int rg = 4 * wave + (lane >> 4), c4 = lane & 15;   // row group 0..15, float4 column
+    const int rg = 16 * wave + (lane >> 2), c4 = lane & 3;   // row group 0..63, float4 column
     const int P = prm.num_partitions;
     const size_t hrow = size_t(b) * prm.num_q_heads + h;
     const float* m = prm.ws_m + hrow * P;
     const float* l = prm.ws_l + hrow * P;
-    const int col = dsl * 64 + 4 * c4;
-    const bool has_col = col < D;          // the last slice of head_dim 96 has 32 columns
+    const int col = dsl * 16 + 4 * c4;
     const char* ob = reinterpret_cast<const char*>(prm.ws_o + hrow * P * D);
-    const uint32_t coff = uint32_t(has_col ? col : 0);
 
     // First pass of rows, loaded before anything waits.
     f32x4 orow[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const uint32_t row = uint32_t(min(rg + 16 * i, P - 1));
-        orow[i] = *reinterpret_cast<const f32x4*>(ob + (row * D + coff) * 4u);
+        const uint32_t row = uint32_t(min(rg + 64 * i, P - 1));
+        orow[i] = *reinterpret_cast<const f32x4*>(ob + (row * D + uint32_t(col)) * 4u);
     }
     // Lane-strided maxima and denominators (partition lane + 64 k) for the
     // wave's own reductions and, by lane permutes, the first pass's weights.
@@ -1102,7 +1103,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams prm)
     const float M = rows4_max(row16_max(mx));
     if (M == -INFINITY) {
         // Every partition empty: out = 0, lse = -inf.
-        if (wave == 0 && rg == 0 && has_col)
+        if (threadIdx.x < 4)
             store_out4<DT>(prm.out, hrow * D + col, f32x4{0.f, 0.f, 0.f, 0.f});
         if (prm.lse && dsl == 0 && threadIdx.x == 0) prm.lse[hrow] = -INFINITY;
         return;
@@ -1119,25 +1120,29 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams prm)
     for (int p = lane + 4 * kWave; p < P; p += kWave) tl += weight(m[p], l[p]);
     const float L = rows4_sum(row16_sum(tl));
 
-    // Row rg + 16 i (< 256) is partition lane + 64 k of this wave with
-    // k = i / 4 and lane = rg + 16 (i % 4); rows past P carry weight 0 there.
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const float wr = __int_as_float(
-            __builtin_amdgcn_ds_bpermute((rg + 16 * (i & 3)) * 4, __float_as_int(wk[i >> 2])));
+        const float wr =
+            __int_as_float(__builtin_amdgcn_ds_bpermute(rg * 4, __float_as_int(wk[i])));
         a += wr * orow[i];
     }
     // Further passes (more than 256 partitions).
-    for (int p = rg + 16 * RPT; p < P; p += 16) {
-        const f32x4 o = *reinterpret_cast<const f32x4*>(ob + (uint32_t(p) * D + coff) * 4u);
+    for (int p = rg + 64 * RPT; p < P; p += 64) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(ob + (uint32_t(p) * D + uint32_t(col)) * 4u);
         a += weight(m[p], l[p]) * o;
     }
+    // Sum the 16 row groups of the wave (lanes c4, c4 + 4, ..., c4 + 60).
 #pragma unroll
-    for (int e = 0; e < 4; ++e) a[e] = rows4_sum(a[e]);
-    if ((lane >> 4) == 0) part[wave][c4] = a;
+    for (int e = 0; e < 4; ++e) {
+        float x = a[e];
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 8);
+        a[e] = rows4_sum(x);
+    }
+    if (lane < 4) part[wave][c4] = a;
     __syncthreads();
-    if (threadIdx.x < 16 && has_col) {
+    if (threadIdx.x < 4) {
         const f32x4 t = part[0][c4] + part[1][c4] + part[2][c4] + part[3][c4];
         store_out4<DT>(prm.out, hrow * D + col, t * (1.f / L));
     }

@@ -234,7 +234,7 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
         } else {
             p.grid_merge[0] = d.num_q_heads;
             p.grid_merge[1] = batch;
-            p.grid_merge[2] = int32_t(ceil_div(d.head_dim, 64));
+            p.grid_merge[2] = d.head_dim / 16;   // 16-column slices
         }
         p.block_merge = kMergeThreads;
         p.workspace_bytes = int64_t(workspace_layout(d, batch, int(P)).total);

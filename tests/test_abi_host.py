@@ -138,8 +138,8 @@ def test_plan_covers_every_context(name):
             if p.split and p.num_partitions <= 64:
                 units = w.batch * w.num_q_heads * (w.head_dim // 64)   # one wave each
                 assert list(p.grid_merge) == [-(-units // 4), 1, 1]
-            elif p.split:
-                assert list(p.grid_merge) == [w.num_q_heads, w.batch, w.head_dim // 64]
+            elif p.split:   # one workgroup per 16-column slice
+                assert list(p.grid_merge) == [w.num_q_heads, w.batch, w.head_dim // 16]
             if p.split:
                 rows = w.batch * w.num_q_heads * p.num_partitions
                 assert p.workspace_bytes >= rows * (w.head_dim + 2) * 4
@@ -283,7 +283,7 @@ def test_head_dim_96_is_planned(dtype):
         if P <= 64:
             assert list(p.grid_merge) == [-(-2 * 32 * 2 // 4), 1, 1]
         else:
-            assert list(p.grid_merge) == [32, 2, 2]
+            assert list(p.grid_merge) == [32, 2, 96 // 16]
         rows = 2 * 32 * P
         assert p.workspace_bytes >= rows * (96 + 2) * 4
 
