@@ -1150,19 +1150,23 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams prm)
 }
 
 // Merge kernel for up to PMAX (<= 64) partitions: one wave per (sequence,
-// query head, 64-column slice of head_dim).  Lane p holds partition p's max
-// and denominator; the global max and the denominator sum reduce across the
-// wave with DPP and lane swaps (no barrier).  For the outputs, lane (rg, c4)
-// = (lane / 16, lane % 16) reads float4 column c4 of rows rg, rg + 4, ...,
-// all before the first reduction, takes each row's weight from the lane that
-// holds it, and the four row groups are summed with lane swaps at the end.
-// Rows past P re-read row P - 1 with weight 0.  Maxima and denominators are
-// loaded first, so that the first reduction waits for them only.
-template <int DT, int D, int PMAX>
+// query head, CW-column slice of head_dim; CW = 64, or 16 when the batch
+// and heads give few waves).  Lane p holds partition p's max and
+// denominator; the global max and the denominator sum reduce across the
+// wave with DPP and lane swaps (no barrier).  For the outputs the lanes form
+// 64 / (CW / 4) row groups of CW / 4 lanes; lane c4 of row group rg reads
+// float4 column c4 of rows rg, rg + NRG, ..., all before the first
+// reduction, takes each row's weight from the lane that holds it, and the
+// row groups are summed with lane swaps at the end.  Rows past P re-read
+// row P - 1 with weight 0.
+template <int DT, int D, int PMAX, int CW>
 __global__ __launch_bounds__(256) void merge_wave_kernel(const MergeParams prm, int units)
 {
-    constexpr int NS = (D + 63) / 64;   // 64-column slices (the last may be partial)
-    constexpr int RPL = PMAX / 4;       // rows per lane
+    constexpr int NS = (D + CW - 1) / CW;   // slices (the last may be partial for CW = 64)
+    constexpr int LPR = CW / 4;             // lanes per row group
+    constexpr int NRG = kWave / LPR;        // row groups
+    constexpr int RPL = PMAX / NRG;         // rows per lane
+    static_assert(RPL * NRG == PMAX && PMAX <= kWave, "rows");
     const int lane = threadIdx.x & (kWave - 1);
     const int unit = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x / kWave) +
                                                     threadIdx.x / kWave);
@@ -1171,9 +1175,9 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(const MergeParams prm, 
     const int P = prm.num_partitions;
     const int slice = unit % NS;
     const size_t hrow = size_t(unit / NS);   // b * Hq + h
-    const int rg = lane >> 4, c4 = lane & 15;
-    const int col = slice * 64 + 4 * c4;
-    const bool has_col = col < D;           // the last slice of head_dim 96 has 32 columns
+    const int rg = lane / LPR, c4 = lane % LPR;
+    const int col = slice * CW + 4 * c4;
+    const bool has_col = col < D;           // head_dim 96, CW 64: the last slice has 32 columns
     // Branch-free loads (lanes past P re-read entry P - 1), all issued
     // before the first use.
     const int pl = min(lane, P - 1);
@@ -1184,7 +1188,7 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(const MergeParams prm, 
     f32x4 orow[RPL];
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-        const uint32_t row = uint32_t(min(rg + 4 * i, P - 1));
+        const uint32_t row = uint32_t(min(rg + NRG * i, P - 1));
         orow[i] = *reinterpret_cast<const f32x4*>(ob + (row * D + uint32_t(has_col ? col : 0)) * 4u);
     }
     pin_loads();
@@ -1206,11 +1210,20 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(const MergeParams prm, 
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-        const float wr = __int_as_float(__builtin_amdgcn_ds_bpermute((rg + 4 * i) * 4, __float_as_int(w)));
+        const float wr = __int_as_float(__builtin_amdgcn_ds_bpermute((rg + NRG * i) * 4, __float_as_int(w)));
         a += wr * orow[i];
     }
+    // Sum the row groups: within each 16-lane row first (CW 16: lanes c4,
+    // c4 + 4, c4 + 8, c4 + 12), then across the four rows.
 #pragma unroll
-    for (int e = 0; e < 4; ++e) a[e] = rows4_sum(a[e]);
+    for (int e = 0; e < 4; ++e) {
+        float x = a[e];
+        if constexpr (LPR == 4) {
+            x += __shfl_xor(x, 4);
+            x += __shfl_xor(x, 8);
+        }
+        a[e] = rows4_sum(x);
+    }
     if (rg == 0 && has_col) store_out4<DT>(prm.out, hrow * D + col, a * (1.f / L));
     if (prm.lse && slice == 0 && lane == 0) prm.lse[hrow] = (M + log2f(L)) * kLn2;
 }
@@ -1411,12 +1424,20 @@ hipError_t launch_merge_t(const MergeParams& p, dim3 grid, dim3 block, hipStream
                           LaunchEvents ev)
 {
     if (p.num_partitions <= kMergeWaveMaxPartitions) {
-        const int units = p.batch * p.num_q_heads * ((D + 63) / 64);
+        const int cw = merge_slice_width(p.batch, p.num_q_heads, D);
+        const int units = p.batch * p.num_q_heads * ((D + cw - 1) / cw);
+        if (cw == 16) {
+            if (p.num_partitions <= 16)
+                return launch(merge_wave_kernel<DT, D, 16, 16>, grid, block, 0, stream, ev, p, units);
+            if (p.num_partitions <= 32)
+                return launch(merge_wave_kernel<DT, D, 32, 16>, grid, block, 0, stream, ev, p, units);
+            return launch(merge_wave_kernel<DT, D, 64, 16>, grid, block, 0, stream, ev, p, units);
+        }
         if (p.num_partitions <= 16)
-            return launch(merge_wave_kernel<DT, D, 16>, grid, block, 0, stream, ev, p, units);
+            return launch(merge_wave_kernel<DT, D, 16, 64>, grid, block, 0, stream, ev, p, units);
         if (p.num_partitions <= 32)
-            return launch(merge_wave_kernel<DT, D, 32>, grid, block, 0, stream, ev, p, units);
-        return launch(merge_wave_kernel<DT, D, 64>, grid, block, 0, stream, ev, p, units);
+            return launch(merge_wave_kernel<DT, D, 32, 64>, grid, block, 0, stream, ev, p, units);
+        return launch(merge_wave_kernel<DT, D, 64, 64>, grid, block, 0, stream, ev, p, units);
     }
     return launch(merge_kernel<DT, D>, grid, block, 0, stream, ev, p);
 }

@@ -227,7 +227,8 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
     if (split) {
         if (P <= kMergeWaveMaxPartitions) {
             // one wave per (sequence, query head, 64-dim slice), four per workgroup
-            const int64_t units = int64_t(batch) * d.num_q_heads * ceil_div(d.head_dim, 64);
+            const int cw = merge_slice_width(batch, d.num_q_heads, d.head_dim);
+            const int64_t units = int64_t(batch) * d.num_q_heads * ceil_div(d.head_dim, cw);
             p.grid_merge[0] = int32_t(ceil_div(units, 4));
             p.grid_merge[1] = 1;
             p.grid_merge[2] = 1;

@@ -25,6 +25,13 @@ constexpr int kMergeThreads = 256;
 // Partition counts up to this use the merge with one wave per (sequence,
 // query head, 64-dim slice); its grid is ceil(B * Hq * D/64 / 4) workgroups.
 constexpr int kMergeWaveMaxPartitions = 64;
+// Columns of head_dim per wave of the merge for up to 64 partitions: 64,
+// or 16 when that leaves fewer than 256 waves (one sequence, few heads),
+// which spreads the merge's reads over four times the waves.
+inline int merge_slice_width(int batch, int num_q_heads, int head_dim)
+{
+    return int64_t(batch) * num_q_heads * ((head_dim + 63) / 64) < 256 ? 16 : 64;
+}
 // Largest y / z launch-grid dimension (sequences, KV heads).
 constexpr int kMaxGridYZ = 65535;
 

@@ -136,7 +136,11 @@ def test_plan_covers_every_context(name):
             assert p.grid_partial[1] == w.num_kv_heads
             assert 64 <= p.block_partial <= 256 and p.block_partial == 64 * p.waves_per_group
             if p.split and p.num_partitions <= 64:
-                units = w.batch * w.num_q_heads * (w.head_dim // 64)   # one wave each
+                # one wave per 64-column slice, or per 16-column slice when
+                # 64-column slices give fewer than 256 waves
+                slices = -(-w.head_dim // 64)
+                cw = 16 if w.batch * w.num_q_heads * slices < 256 else 64
+                units = w.batch * w.num_q_heads * -(-w.head_dim // cw)
                 assert list(p.grid_merge) == [-(-units // 4), 1, 1]
             elif p.split:   # one workgroup per 16-column slice
                 assert list(p.grid_merge) == [w.num_q_heads, w.batch, w.head_dim // 16]
@@ -280,8 +284,8 @@ def test_head_dim_96_is_planned(dtype):
     for S, P in ((16, 256), (512, 8)):
         p = B.pa_decode_plan_query(d, 256, 8, 2, 4096, 0, S)
         assert p.pages_per_block == 2 and p.num_partitions == P
-        if P <= 64:
-            assert list(p.grid_merge) == [-(-2 * 32 * 2 // 4), 1, 1]
+        if P <= 64:   # 2 x 32 x 2 = 128 waves at 64 columns: 16-column slices
+            assert list(p.grid_merge) == [-(-2 * 32 * (96 // 16) // 4), 1, 1]
         else:
             assert list(p.grid_merge) == [32, 2, 96 // 16]
         rows = 2 * 32 * P
