@@ -209,6 +209,41 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
     ms_total = start.elapsed_time(stop)
     ms_per_step = ms_total / steps
 
+    # Spread and warm-cache figures (after the timed region; not part of it):
+    # the same graph replayed five more times (µs/step of each replay), and,
+    # for graph mode, K steps on one replica only, so that its K/V stays in
+    # the L2 and the 256 MB MALL where it fits.
+    spread = None
+    warm = None
+    if mode == "graph":
+        per = []
+        for _ in range(5):
+            start.record(stream)
+            g.replay()
+            stop.record(stream)
+            torch.cuda.synchronize()
+            per.append(1e3 * start.elapsed_time(stop) / steps)
+        per.sort()
+        spread = {"min": round(per[0], 3), "median": round(per[2], 3), "max": round(per[-1], 3),
+                  "replays": 5}
+        if layers == 1:
+            gw = torch.cuda.CUDAGraph()
+            cap.wait_stream(stream)
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(gw, stream=cap):
+                    cs = torch.cuda.current_stream().cuda_stream
+                    for i in range(steps):
+                        reps.run(reps.args[0], cs)
+            stream.wait_stream(cap)
+            gw.replay()
+            torch.cuda.synchronize()
+            start.record(stream)
+            gw.replay()
+            stop.record(stream)
+            torch.cuda.synchronize()
+            warm = round(1e3 * start.elapsed_time(stop) / steps, 3)
+            del gw
+
     # Kernel durations: start/stop events recorded around each launch.
     nprof = min(steps, 2000)
     binding.pa_decode_profile_begin(eng.handle, nprof)
@@ -222,7 +257,7 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
 
     res = {
         "workload": name, "p": p, "plan": plan, "kv_bytes": kv_bytes * L, "replicas": R,
-        "read_ceiling": ceiling,
+        "read_ceiling": ceiling, "spread": spread, "warm_us_per_step": warm,
         "layers": L, "ms_per_step": ms_per_step, "us_per_step": 1e3 * ms_per_step,
         "us_per_layer": 1e3 * ms_per_step / L,
         "gbps": kv_bytes * L / (ms_per_step * 1e-3) / 1e9,
@@ -466,6 +501,8 @@ def main():
                    "replicas": main_res["replicas"], "mode": args.mode,
                    "page_table": args.page_table, "layers": args.layers,
                    "us_per_layer": round(main_res["us_per_layer"], 3),
+                   "us_per_step_replays": main_res["spread"],
+                   "warm_us_per_step": main_res["warm_us_per_step"],
                    "plan": main_res["plan"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
