@@ -158,9 +158,13 @@ typedef struct pa_decode_plan {
     int32_t grid_partial[3];    /* partial kernel grid (x = group of partitions,    */
                                 /*   y = KV head, z = b)                            */
     int32_t block_partial;      /* threads per workgroup of the partial kernel */
-    int32_t grid_merge[3];      /* merge kernel grid (x = query head, y = b, z = 64-dim */
-                                /*   slice of head_dim; 0s when split == 0)           */
-    int32_t block_merge;
+    int32_t grid_merge[3];      /* merge kernel grid; 0s when split == 0.  Up to 64  */
+                                /*   partitions: (ceil(waves / 4), 1, 1) with one wave  */
+                                /*   per (b, query head, slice of 64 columns, or of 16  */
+                                /*   when 64 would give fewer than 256 waves); beyond:  */
+                                /*   (query head, b, head_dim / 16), one workgroup per  */
+                                /*   16-column slice                                    */
+    int32_t block_merge;        /* threads per merge workgroup (256) */
     int32_t num_cus;            /* compute units the plan was made for */
     int32_t waves_per_cu;       /* partial-kernel waves one compute unit holds     */
     int64_t workspace_bytes;    /* bytes of workspace the plan needs */
