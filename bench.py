@@ -51,6 +51,8 @@ METRIC = "decode-attention µs/step + achieved KV HBM GB/s (% of peak) at ctx 3k
 PEAK_GBPS = 8000.0
 CACHE_BYTES = 288 << 20          # 256 MiB MALL + 8 x 4 MiB L2
 KERNEL_SOURCES = ["paged_kv_decode_amd/csrc/pa_decode_kernels.hip",
+                  "paged_kv_decode_amd/csrc/partial_kernel.h",
+                  "paged_kv_decode_amd/csrc/pa_decode_balanced.hip",
                   "paged_kv_decode_amd/csrc/planner.cpp"]
 
 

@@ -76,6 +76,19 @@ enum {
                                     /*   > nnz_pages: the row is clamped into [0, nnz_pages] */
 };
 
+/* partition_size value that asks for the length-balanced schedule: the
+ * visible pages of the whole batch (window start to last page of each
+ * sequence, in sequence order) are split into equal contiguous ranges, one
+ * per wave of each KV head, from the context lengths the kernel reads, so
+ * that a few long sequences in a ragged batch do not set the step time.  A
+ * wave's range is cut at sequence ends; each piece is one partition state,
+ * and the merge combines a sequence's pieces.  This is the split-context
+ * method of the paged_attention_v2 commit page (partition states merged by
+ * log-sum-exp, "Phase 2") with partition bounds that follow the lengths
+ * instead of fixed S-token blocks.  Needs batch <= 64 and
+ * batch * (max_context_len / page_size + 66) < 2^31; UNSUPPORTED otherwise. */
+#define PA_DECODE_PARTITION_BALANCED (-1)
+
 /* Element types of q, the K/V caches and out (all three share one type). */
 enum {
     PA_DTYPE_F32 = 0,
@@ -135,7 +148,8 @@ typedef struct pa_decode_args {
     float scale;                /* multiplies q.k */
     int32_t sliding_window;     /* <= 0: no window; else keys [n_b - W, n_b) */
     int32_t partition_size;     /* 0: planner's choice; else tokens per partition, */
-                                /*   a positive multiple of page_size */
+                                /*   a positive multiple of page_size; or          */
+                                /*   PA_DECODE_PARTITION_BALANCED                  */
     void* out;                  /* device, [batch, Hq, D] contiguous, desc.dtype */
     float* lse;                 /* device, float32 [batch, Hq], may be NULL */
     void* workspace;            /* device scratch of >= workspace_bytes needed by the */
@@ -168,6 +182,12 @@ typedef struct pa_decode_plan {
     int32_t num_cus;            /* compute units the plan was made for */
     int32_t waves_per_cu;       /* partial-kernel waves one compute unit holds     */
     int64_t workspace_bytes;    /* bytes of workspace the plan needs */
+    int32_t balanced_waves;     /* > 0: the length-balanced schedule with this many */
+                                /*   waves per KV head (grid x = balanced_waves /   */
+                                /*   waves_per_group, y = KV head, z = 1); then      */
+                                /*   partition_size is 0 and num_partitions is the  */
+                                /*   most states one (sequence, head) can have.     */
+                                /*   0: fixed partitions of partition_size tokens.  */
 } pa_decode_plan;
 
 typedef struct pa_decode_handle_s* pa_decode_handle;
@@ -259,7 +279,8 @@ typedef struct pa_decode_csr_args {
     int32_t partition_size;       /* 0: the host switch above -- one partition per    */
                                   /*   (sequence, KV head) when nnz_pages <=          */
                                   /*   B * 256 / page_size, else the planner's split; */
-                                  /*   > 0: tokens per partition, as in pa_decode_args */
+                                  /*   > 0: tokens per partition, as in pa_decode_args; */
+                                  /*   PA_DECODE_PARTITION_BALANCED as there          */
     void* out;                    /* device, [batch, Hq, D] contiguous, desc.dtype */
     float* lse;                   /* device, float32 [batch, Hq], may be NULL */
     void* workspace;              /* device scratch, pa_decode_workspace_size_csr bytes */

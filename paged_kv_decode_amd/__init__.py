@@ -5,6 +5,7 @@ C ABI of include/pa_decode.h); ``binding`` is its ctypes front end and
 ``workloads`` draws seeded synthetic inputs.
 """
 from .binding import (  # noqa: F401
+    PA_DECODE_PARTITION_BALANCED,
     PagedDecode,
     PaDecodeArgs,
     PaDecodeDesc,

@@ -24,6 +24,9 @@ PA_DECODE_UNSUPPORTED = -2
 PA_DECODE_WORKSPACE_TOO_SMALL = -3
 PA_DECODE_HIP_ERROR = -4
 
+# partition_size value for the length-balanced schedule (batch <= 64).
+PA_DECODE_PARTITION_BALANCED = -1
+
 PA_DTYPE_F32 = 0
 PA_DTYPE_F16 = 1
 PA_DTYPE_BF16 = 2
@@ -82,7 +85,7 @@ class PaDecodePlan(ctypes.Structure):
                 ("block_partial", ctypes.c_int32), ("grid_merge", ctypes.c_int32 * 3),
                 ("block_merge", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("waves_per_cu", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_int64)]
+                ("workspace_bytes", ctypes.c_int64), ("balanced_waves", ctypes.c_int32)]
 
     def as_dict(self):
         return {"split": self.split, "partition_size": self.partition_size,
@@ -92,7 +95,7 @@ class PaDecodePlan(ctypes.Structure):
                 "grid_partial": list(self.grid_partial), "block_partial": self.block_partial,
                 "grid_merge": list(self.grid_merge), "block_merge": self.block_merge,
                 "num_cus": self.num_cus, "waves_per_cu": self.waves_per_cu,
-                "workspace_bytes": self.workspace_bytes}
+                "workspace_bytes": self.workspace_bytes, "balanced_waves": self.balanced_waves}
 
 
 class PaDecodeError(RuntimeError):

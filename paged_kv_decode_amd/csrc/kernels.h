@@ -46,6 +46,17 @@ struct PartialParams {
     double rope_rho;          // rope_theta^(-2/D): theta_i = rope_rho^i / rope_scale
     double rope_f0;           // 1 / (2 pi rope_scale): theta_0 in revolutions
     float minus_one;          // -1 (a value the compiler cannot fold; see TurnedKey)
+    // Length-balanced schedule (launch_partial_balanced only): the visible
+    // pages of the batch's `batch` (<= 64) sequences, in sequence order, are
+    // split into bal_waves contiguous ranges, one per wave of the KV head
+    // (grid x * waves per workgroup = bal_waves).  ws_cnt[b * Hq + h]
+    // receives the number of state rows of (sequence b, query head h): rows
+    // of ws_o / ws_m / ws_l at partition index 0 .. count - 1,
+    // num_partitions being their pitch.
+    int32_t batch;
+    int32_t bal_waves;
+    int32_t bal_start;        // pages charged for each sequence's start (>= 0)
+    int32_t* ws_cnt;
 };
 
 // Arguments of the merge kernel (one workgroup per (query head, b)).
@@ -58,6 +69,11 @@ struct MergeParams {
     const float* ws_l;
     void* out;
     float* lse;
+    // Null: every (sequence, head) has num_partitions state rows.  Otherwise
+    // (length-balanced schedule) (sequence b, query head h) has
+    // ws_cnt[b * Hq + h] rows (at most the pitch num_partitions); the rows
+    // past it hold no state and are never used.
+    const int32_t* ws_cnt;
 };
 
 // Optional start/stop events recorded around one launch (both null: none).
@@ -70,6 +86,11 @@ struct LaunchEvents {
 hipError_t launch_partial(int dtype, int head_dim, int group_t, const PartialParams& p,
                           dim3 grid, dim3 block, size_t lds_bytes, hipStream_t stream,
                           LaunchEvents ev);
+// The partial kernel with the length-balanced schedule (p.bal_waves > 0,
+// p.batch <= 64, one wave per partition slot).
+hipError_t launch_partial_balanced(int dtype, int head_dim, int group_t, const PartialParams& p,
+                                   dim3 grid, dim3 block, size_t lds_bytes, hipStream_t stream,
+                                   LaunchEvents ev);
 hipError_t launch_merge(int dtype, int head_dim, const MergeParams& p, dim3 grid, dim3 block,
                         hipStream_t stream, LaunchEvents ev);
 
@@ -85,5 +106,7 @@ hipError_t launch_read_probe(const void* base, const uint64_t* chunk_addrs, int3
 // once; 0 when unknown.
 int partial_waves_per_cu(int dtype, int head_dim, int group_t, bool rotary, int waves,
                          size_t lds_bytes);
+int partial_balanced_waves_per_cu(int dtype, int head_dim, int group_t, bool rotary, int waves,
+                                  size_t lds_bytes);
 
 }  // namespace pa

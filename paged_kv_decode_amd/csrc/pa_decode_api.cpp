@@ -103,7 +103,8 @@ StepArgs common_args(const A& a)
 int check_common(const pa_decode_desc& d, const StepArgs& a)
 {
     if (a.batch < 0 || a.batch > d.max_batch || a.max_context_len < 0 ||
-        a.max_context_len > d.max_context_len || a.partition_size < 0)
+        a.max_context_len > d.max_context_len ||
+        (a.partition_size < 0 && a.partition_size != PA_DECODE_PARTITION_BALANCED))
         return PA_DECODE_INVALID_ARG;
     if (a.partition_size > 0 && a.partition_size % d.page_size != 0)
         return PA_DECODE_INVALID_ARG;
@@ -176,7 +177,9 @@ int launch_step(pa_decode_handle handle, const StepArgs& a, const PageSource& sr
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int G = d.num_q_heads / d.num_kv_heads;
-    const pa::WorkspaceLayout wl = pa::workspace_layout(d, a.batch, plan.num_partitions);
+    const bool balanced = plan.balanced_waves > 0;
+    const pa::WorkspaceLayout wl =
+        pa::workspace_layout(d, a.batch, plan.num_partitions, balanced);
     char* ws = static_cast<char*>(a.workspace);
 
     pa::PartialParams pp;
@@ -213,13 +216,21 @@ int launch_step(pa_decode_handle handle, const StepArgs& a, const PageSource& sr
     pp.rope_rho = d.rotary_mode ? std::pow(double(d.rope_theta), -2.0 / d.head_dim) : 1.0;
     pp.rope_f0 = d.rotary_mode ? 1.0 / (6.283185307179586477 * double(d.rope_scale)) : 0.0;
     pp.minus_one = -1.0f;
+    pp.batch = a.batch;
+    pp.bal_waves = plan.balanced_waves;
+    pp.bal_start = balanced ? pa::balanced_start_pages(d) : 0;
+    pp.ws_cnt = balanced ? reinterpret_cast<int32_t*>(ws + wl.c_off) : nullptr;
 
     const dim3 grid(plan.grid_partial[0], plan.grid_partial[1], plan.grid_partial[2]);
     const dim3 block(plan.block_partial);
     const pa::LaunchEvents ev_partial =
         handle->profiling ? handle->prof_partial.next() : pa::LaunchEvents();
-    hipError_t e = pa::launch_partial(d.dtype, d.head_dim, pa::template_group(G), pp, grid, block,
-                                      pa::partial_lds_bytes(d, plan), s, ev_partial);
+    const size_t lds = pa::partial_lds_bytes(d, plan);
+    hipError_t e =
+        balanced ? pa::launch_partial_balanced(d.dtype, d.head_dim, pa::template_group(G), pp,
+                                               grid, block, lds, s, ev_partial)
+                 : pa::launch_partial(d.dtype, d.head_dim, pa::template_group(G), pp, grid,
+                                      block, lds, s, ev_partial);
     if (e != hipSuccess) {
         handle->last_hip_error = int(e);
         return PA_DECODE_HIP_ERROR;
@@ -234,6 +245,7 @@ int launch_step(pa_decode_handle handle, const StepArgs& a, const PageSource& sr
         mp.ws_l = pp.ws_l;
         mp.out = a.out;
         mp.lse = a.lse;
+        mp.ws_cnt = pp.ws_cnt;
         const dim3 mgrid(plan.grid_merge[0], plan.grid_merge[1], plan.grid_merge[2]);
         const pa::LaunchEvents ev_merge =
             handle->profiling ? handle->prof_merge.next() : pa::LaunchEvents();

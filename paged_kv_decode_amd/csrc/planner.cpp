@@ -97,7 +97,8 @@ int workgroup_waves(const pa_decode_desc& d)
     return nw;
 }
 
-WorkspaceLayout workspace_layout(const pa_decode_desc& d, int batch, int num_partitions)
+WorkspaceLayout workspace_layout(const pa_decode_desc& d, int batch, int num_partitions,
+                                 bool counts)
 {
     auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
     size_t rows = size_t(batch) * size_t(d.num_q_heads) * size_t(num_partitions);
@@ -105,8 +106,84 @@ WorkspaceLayout workspace_layout(const pa_decode_desc& d, int batch, int num_par
     w.o_off = 0;
     w.m_off = w.o_off + align(rows * size_t(d.head_dim) * sizeof(float));
     w.l_off = w.m_off + align(rows * sizeof(float));
-    w.total = w.l_off + align(rows * sizeof(float));
+    w.c_off = w.l_off + align(rows * sizeof(float));
+    w.total = w.c_off +
+              (counts ? align(size_t(batch) * size_t(d.num_q_heads) * sizeof(int32_t)) : 0);
     return w;
+}
+
+// Merge grid and block of a split plan with P state rows per (sequence,
+// head); `counts` (balanced schedule): the per-wave merge whatever P.
+static void set_merge_grid(const pa_decode_desc& d, int batch, int64_t P, pa_decode_plan* p,
+                           bool counts = false)
+{
+    if (P <= kMergeWaveMaxPartitions || counts) {
+        // one wave per (sequence, query head, 64-dim slice), four per workgroup
+        const int cw = merge_slice_width(batch, d.num_q_heads, d.head_dim);
+        const int64_t units = int64_t(batch) * d.num_q_heads * ((d.head_dim + cw - 1) / cw);
+        p->grid_merge[0] = int32_t((units + 3) / 4);
+        p->grid_merge[1] = 1;
+        p->grid_merge[2] = 1;
+    } else {
+        p->grid_merge[0] = d.num_q_heads;
+        p->grid_merge[1] = batch;
+        p->grid_merge[2] = d.head_dim / 16;   // 16-column slices
+    }
+    p->block_merge = kMergeThreads;
+}
+
+int balanced_start_pages(const pa_decode_desc& d)
+{
+    // Four blocks' worth: measured on MI355X over 2 .. 32 pages for head_dim
+    // 96 and 128 batches of 16 with lengths up to 4096 (with and without
+    // rotary), the best charges were 6 - 8 pages at two pages per block.
+    int c = 4 * pages_per_block(d.head_dim, d.dtype);
+    // Experiments only: PA_DECODE_BALANCED_START overrides the charge.
+    if (const char* env = std::getenv("PA_DECODE_BALANCED_START")) c = std::atoi(env);
+    return std::max(0, std::min(64, c));
+}
+
+// The length-balanced schedule (partition_size PA_DECODE_PARTITION_BALANCED):
+// every KV head gets W waves (about four per compute unit over all heads, a
+// multiple of the workgroup size), which split the batch's visible pages
+// evenly in the kernel.  A (sequence, head) then has at most min(W, its
+// visible pages) states.
+static int make_balanced_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
+                              int64_t vis_pages, pa_decode_plan* plan)
+{
+    if (batch > kBalancedMaxBatch)
+        return PA_DECODE_UNSUPPORTED;
+    if (int64_t(batch) * (vis_pages + 64) >= (int64_t(1) << 31))   // charged pages fit in int32
+        return PA_DECODE_UNSUPPORTED;
+    const int nw = workgroup_waves(d);
+    const int64_t capacity = int64_t(num_cus) * waves_per_cu;
+    const int64_t target = std::min<int64_t>(capacity, int64_t(num_cus) * 4);
+    // Waves per KV head: the target shared by the heads, no more than the
+    // batch's pages, a whole number of workgroups.
+    int64_t W = std::min<int64_t>(target / d.num_kv_heads, int64_t(batch) * vis_pages);
+    W = std::max<int64_t>(nw, W / nw * nw);
+    if (W / nw > 65535)
+        return PA_DECODE_UNSUPPORTED;
+    const int64_t P = std::min<int64_t>(W, vis_pages);
+
+    pa_decode_plan p = {};
+    p.split = 1;
+    p.partition_size = 0;
+    p.num_partitions = int32_t(P);
+    p.waves_per_group = nw;
+    p.waves_per_partition = 1;
+    p.pages_per_block = pages_per_block(d.head_dim, d.dtype);
+    p.grid_partial[0] = int32_t(W / nw);
+    p.grid_partial[1] = d.num_kv_heads;
+    p.grid_partial[2] = 1;
+    p.block_partial = nw * 64;
+    set_merge_grid(d, batch, P, &p, true);
+    p.workspace_bytes = int64_t(workspace_layout(d, batch, int(P), true).total);
+    p.num_cus = num_cus;
+    p.waves_per_cu = waves_per_cu;
+    p.balanced_waves = int32_t(W);
+    *plan = p;
+    return PA_DECODE_OK;
 }
 
 int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
@@ -118,8 +195,10 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
     int st = check_desc(d);
     if (st != PA_DECODE_OK)
         return st;
+    const bool balanced = partition_size == PA_DECODE_PARTITION_BALANCED;
     if (num_cus <= 0 || waves_per_cu <= 0 || batch < 0 || batch > d.max_batch ||
-        max_context_len < 0 || max_context_len > d.max_context_len || partition_size < 0)
+        max_context_len < 0 || max_context_len > d.max_context_len ||
+        (partition_size < 0 && !balanced))
         return PA_DECODE_INVALID_ARG;
     if (partition_size > 0 && partition_size % d.page_size != 0)
         return PA_DECODE_INVALID_ARG;
@@ -132,6 +211,8 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
     // Pages a visible range can touch (one more when the window edge is not
     // page aligned).
     const int64_t vis_pages = ceil_div(std::max<int64_t>(visible, 1), ps) + (windowed ? 1 : 0);
+    if (balanced && batch > 0)   // (an empty batch launches nothing either way)
+        return make_balanced_plan(d, num_cus, waves_per_cu, batch, vis_pages, plan);
     // Waves the grid aims for: about four per compute unit (one per SIMD),
     // never more than the device holds at once.  Measured on MI355X, fewer
     // waves with more pages each stream KV faster than more, shorter waves.
@@ -225,19 +306,7 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
     p.grid_partial[2] = batch;
     p.block_partial = nw * 64;
     if (split) {
-        if (P <= kMergeWaveMaxPartitions) {
-            // one wave per (sequence, query head, 64-dim slice), four per workgroup
-            const int cw = merge_slice_width(batch, d.num_q_heads, d.head_dim);
-            const int64_t units = int64_t(batch) * d.num_q_heads * ceil_div(d.head_dim, cw);
-            p.grid_merge[0] = int32_t(ceil_div(units, 4));
-            p.grid_merge[1] = 1;
-            p.grid_merge[2] = 1;
-        } else {
-            p.grid_merge[0] = d.num_q_heads;
-            p.grid_merge[1] = batch;
-            p.grid_merge[2] = d.head_dim / 16;   // 16-column slices
-        }
-        p.block_merge = kMergeThreads;
+        set_merge_grid(d, batch, P, &p);
         p.workspace_bytes = int64_t(workspace_layout(d, batch, int(P)).total);
     }
     p.num_cus = num_cus;
@@ -250,7 +319,8 @@ int make_plan_csr(const pa_decode_desc& d, int num_cus, int waves_per_cu, int ba
                   int nnz_pages, int max_context_len, int sliding_window, int partition_size,
                   pa_decode_plan* plan, int* max_ctx_used)
 {
-    if (!plan || nnz_pages < 0 || batch < 0 || max_context_len < 0 || partition_size < 0)
+    if (!plan || nnz_pages < 0 || batch < 0 || max_context_len < 0 ||
+        (partition_size < 0 && partition_size != PA_DECODE_PARTITION_BALANCED))
         return PA_DECODE_INVALID_ARG;
     if (batch == 0 && nnz_pages != 0)
         return PA_DECODE_INVALID_ARG;

@@ -86,9 +86,19 @@ size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan);
 // Workspace layout of a split plan: partition outputs o[B][Hq][P][D] (f32),
 // maxima m[B][Hq][P] and denominators l[B][Hq][P] (f32), each region
 // 256-byte aligned.
+// The balanced schedule adds the state-row counts c[B][Hq] (int32).
 struct WorkspaceLayout {
-    size_t o_off, m_off, l_off, total;
+    size_t o_off, m_off, l_off, c_off, total;
 };
-WorkspaceLayout workspace_layout(const pa_decode_desc& d, int batch, int num_partitions);
+WorkspaceLayout workspace_layout(const pa_decode_desc& d, int batch, int num_partitions,
+                                 bool counts = false);
+
+// Largest batch of the length-balanced schedule (one sequence per lane of a
+// wave's prefix sum).
+constexpr int kBalancedMaxBatch = 64;
+// Pages the balanced schedule charges for each sequence's start (0 .. 64):
+// four blocks' worth (a segment's start waits for its page ids and q before
+// the first block's loads go out, and its pipeline starts empty).
+int balanced_start_pages(const pa_decode_desc& d);
 
 }  // namespace pa

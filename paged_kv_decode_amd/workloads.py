@@ -52,7 +52,8 @@ class Workload:
     num_pages: int                      # size of the physical page pool
     seed: int
     window: int = 0                     # <= 0: no sliding window
-    partition_size: int = 0             # 0: the library chooses
+    partition_size: int = 0             # 0: the library chooses; BALANCED: the
+                                        # length-balanced schedule
     page_size: int = PAGE_SIZE
     random_lens: Optional[tuple] = None  # (lo, hi, forced{index: len}) for drawn lengths
     rope: Optional[tuple] = None        # (rope_theta, rope_scale): rotary_mode 1; None: off
@@ -67,6 +68,12 @@ class Workload:
         return float(np.float32(1.0 / math.sqrt(self.head_dim)))
 
 
+# partition_size of the length-balanced schedule (PA_DECODE_PARTITION_BALANCED):
+# the ragged batches below run with it, as a caller who knows its batch is
+# ragged would (the planner's automatic choice keeps fixed partitions, which
+# suit batches of equal lengths better).
+BALANCED = -1
+
 CONFIGS = {
     "tiny_gqa4_f32": Workload(
         name="tiny_gqa4_f32", batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64,
@@ -77,7 +84,7 @@ CONFIGS = {
     "llama8b_b16_ragged_f16": Workload(
         name="llama8b_b16_ragged_f16", batch=16, num_q_heads=32, num_kv_heads=8,
         head_dim=128, dtype=torch.float16, context_lens=None, num_pages=4096, seed=3,
-        random_lens=(1, 4096, {0: 1, 1: 4096, 2: 17})),
+        random_lens=(1, 4096, {0: 1, 1: 4096, 2: 17}), partition_size=BALANCED),
     "d256_window4096_bf16": Workload(
         name="d256_window4096_bf16", batch=4, num_q_heads=8, num_kv_heads=4, head_dim=256,
         dtype=torch.bfloat16, context_lens=[8192] * 4, num_pages=2048, seed=4,
@@ -90,7 +97,7 @@ CONFIGS = {
     "d96_b16_ragged_f16": Workload(
         name="d96_b16_ragged_f16", batch=16, num_q_heads=32, num_kv_heads=8, head_dim=96,
         dtype=torch.float16, context_lens=None, num_pages=4096, seed=6,
-        random_lens=(1, 4096, {0: 1, 1: 4096, 2: 17})),
+        random_lens=(1, 4096, {0: 1, 1: 4096, 2: 17}), partition_size=BALANCED),
     "d96_ctx32k_f16": Workload(
         name="d96_ctx32k_f16", batch=1, num_q_heads=32, num_kv_heads=8, head_dim=96,
         dtype=torch.float16, context_lens=[32768], num_pages=2048, seed=7),

@@ -162,7 +162,7 @@ def test_waves_per_partition_target_one_round(name, waves_per_cu):
     """The waves sharing a partition bring the grid's wave count closest to
     four per compute unit without exceeding what the device holds at once."""
     w = W.CONFIGS[name]
-    p = plan(w, waves_per_cu=waves_per_cu)
+    p = plan(w, waves_per_cu=waves_per_cu, S=max(w.partition_size, 0))   # fixed partitions
     if not p.split:
         return
     units = w.batch * w.num_kv_heads * p.num_partitions

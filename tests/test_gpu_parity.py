@@ -13,6 +13,8 @@ lse (absolute error) with the tolerances in helpers.py.  Covered:
     nine lengths in that range with a shuffled table; its "Tests" lay out
     D = 96 too);
   * forced partition sizes (16 ... 1024 tokens) and the unsplit path;
+  * the ragged batches with fixed partitions too (their workloads use the
+    length-balanced schedule, covered in test_gpu_balanced.py);
   * every built group size G in 1..16;
   * NaN in every slot the method must not read (tail slots, keys before the
     window, unused pages, page-table padding);
@@ -50,6 +52,15 @@ def _check(p, S=None, what=""):
 def test_workload_full_size(name):
     p = W.generate(W.CONFIGS[name])
     _check(p, what=name)
+
+
+@pytest.mark.parametrize("name", ["llama8b_b16_ragged_f16", "d96_b16_ragged_f16",
+                                  "llama8b_b16_ragged_rope_f16"])
+def test_ragged_workloads_with_fixed_partitions(name):
+    """The ragged batches run with the balanced schedule by default; here
+    with the planner's fixed partitions."""
+    p = W.generate(W.CONFIGS[name])
+    _check(p, S=0, what=name + " fixed")
 
 
 @pytest.mark.parametrize("D,dtype", [(64, torch.float16), (96, torch.float16), (128, torch.float16),
@@ -322,14 +333,16 @@ def test_extreme_score_scales(scale, dtype):
 
 def test_batch_permutation_permutes_outputs_bitwise():
     """Sequences are independent: reordering the batch (q rows, page-table
-    rows, lengths) reorders out and lse, bit for bit (the plan depends only
-    on the batch size and the longest context, which do not change)."""
+    rows, lengths) reorders out and lse, bit for bit, under fixed partitions
+    (whose plan depends only on the batch size and the longest context,
+    which do not change; the balanced schedule's split points follow the
+    order of the lengths, so there the rounding may differ)."""
     p = W.generate(W.CONFIGS["llama8b_b16_ragged_f16"])
-    out, lse, plan = run_gpu(p)
+    out, lse, plan = run_gpu(p, partition_size=0)
     perm = torch.randperm(p.q.shape[0], generator=torch.Generator().manual_seed(621))
     pp = dataclasses.replace(p, q=p.q[perm].contiguous(), page_table=p.page_table[perm].contiguous(),
                              context_lens=p.context_lens[perm].contiguous())
-    out2, lse2, plan2 = run_gpu(pp)
+    out2, lse2, plan2 = run_gpu(pp, partition_size=0)
     assert plan2 == plan
     assert torch.equal(out2, out[perm]) and torch.equal(lse2, lse[perm])
 
