@@ -580,11 +580,11 @@ def _csv_rows(path):
 
 
 def _short(name):
-    """Kernel family of a trace or counter row (both merge kernels count as
-    the merge)."""
+    """Kernel family of a trace or counter row (the three merge kernels count
+    as the merge)."""
     if "partial_kernel" in name:
         return "partial_kernel"
-    if "merge_kernel" in name or "merge_wave_kernel" in name:
+    if "merge_kernel" in name or "merge_wave_kernel" in name or "merge_count_kernel" in name:
         return "merge_kernel"
     if "copyBuffer" in name:
         return "copyBuffer"

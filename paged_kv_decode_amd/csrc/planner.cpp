@@ -134,10 +134,11 @@ static void set_merge_grid(const pa_decode_desc& d, int batch, int64_t P, pa_dec
 
 int balanced_start_pages(const pa_decode_desc& d)
 {
-    // Four blocks' worth: measured on MI355X over 2 .. 32 pages for head_dim
-    // 96 and 128 batches of 16 with lengths up to 4096 (with and without
-    // rotary), the best charges were 6 - 8 pages at two pages per block.
-    int c = 4 * pages_per_block(d.head_dim, d.dtype);
+    // Four blocks' worth, three with rotary: measured on MI355X over 2 .. 32
+    // pages for batches of 16 with lengths up to 4096 at two pages per
+    // block, the best charges were 8 (head_dim 128), 8 - 10 (head_dim 96)
+    // and 6 - 7 (head_dim 128 with rotary, whose blocks take longer).
+    int c = (d.rotary_mode == 1 ? 3 : 4) * pages_per_block(d.head_dim, d.dtype);
     // Experiments only: PA_DECODE_BALANCED_START overrides the charge.
     if (const char* env = std::getenv("PA_DECODE_BALANCED_START")) c = std::atoi(env);
     return std::max(0, std::min(64, c));
@@ -157,7 +158,11 @@ static int make_balanced_plan(const pa_decode_desc& d, int num_cus, int waves_pe
         return PA_DECODE_UNSUPPORTED;
     const int nw = workgroup_waves(d);
     const int64_t capacity = int64_t(num_cus) * waves_per_cu;
-    const int64_t target = std::min<int64_t>(capacity, int64_t(num_cus) * 4);
+    int per_cu = 4;
+    // Experiments only: PA_DECODE_BALANCED_WAVES_PER_CU overrides the target.
+    if (const char* env = std::getenv("PA_DECODE_BALANCED_WAVES_PER_CU"))
+        per_cu = std::max(1, std::min(16, std::atoi(env)));
+    const int64_t target = std::min<int64_t>(capacity, int64_t(num_cus) * per_cu);
     // Waves per KV head: the target shared by the heads, no more than the
     // batch's pages, a whole number of workgroups.
     int64_t W = std::min<int64_t>(target / d.num_kv_heads, int64_t(batch) * vis_pages);

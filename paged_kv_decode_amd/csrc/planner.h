@@ -97,8 +97,9 @@ WorkspaceLayout workspace_layout(const pa_decode_desc& d, int batch, int num_par
 // wave's prefix sum).
 constexpr int kBalancedMaxBatch = 64;
 // Pages the balanced schedule charges for each sequence's start (0 .. 64):
-// four blocks' worth (a segment's start waits for its page ids and q before
-// the first block's loads go out, and its pipeline starts empty).
+// four blocks' worth, three with rotary (a segment's start waits for its
+// page ids and q before the first block's loads go out, and its pipeline
+// starts empty).
 int balanced_start_pages(const pa_decode_desc& d);
 
 }  // namespace pa
