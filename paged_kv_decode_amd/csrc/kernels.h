@@ -9,7 +9,9 @@
 
 namespace pa {
 
-// Arguments of the partial kernel (one workgroup per (partition, KV head, b)).
+// Arguments of the partial kernel (fixed schedule: one workgroup per
+// (group of partitions, KV head, b); balanced schedule: bal_waves waves per
+// KV head).
 struct PartialParams {
     const void* q;            // [B, Hq, D]
     const void* k;            // paged K, element strides below (D contiguous)

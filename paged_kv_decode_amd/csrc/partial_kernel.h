@@ -451,10 +451,15 @@ template <> struct PV<PA_DTYPE_BF16> {
 // ---------------------------------------------------------------------------
 // Partial kernel.
 //   DT: element type; D: head_dim; G: instantiated group size (>= actual);
-//   NB: pages per block; ROT: rotary embedding of q and keys (rotary_mode 1).
-// Workgroup: blockDim.x / 64 waves split into partition slots of
-// prm.waves_per_partition waves; slot j of workgroup x handles partition
-// x * slots + j of KV head blockIdx.y of sequence blockIdx.z.
+//   NB: pages per block; ROT: rotary embedding of q and keys (rotary_mode 1);
+//   BAL: the length-balanced schedule.
+// Workgroup (fixed schedule): blockDim.x / 64 waves split into partition
+// slots of prm.waves_per_partition waves; slot j of workgroup x handles
+// partition x * slots + j of KV head blockIdx.y of sequence blockIdx.z.
+// Balanced schedule: wave j of workgroup x is wave x * waves + j of KV head
+// blockIdx.y; it finds its range of the batch's visible pages from the
+// lengths (see the prologue) and computes one partition state per sequence
+// piece of that range.
 // Lane maps (lane = 0..63, i16 = lane % 16, grp = lane / 16):
 //   loads:   K and V alike: load instruction i of a page reads chunks
 //            64*i .. 64*i + 63 of the page's 16 x CH chunk grid, lane l chunk
