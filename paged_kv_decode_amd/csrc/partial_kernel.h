@@ -579,12 +579,48 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     // visible pages of the wave's range, cut at sequence ends, are its
     // segments; the segment of sequence b in wave w is that sequence's state
     // row w - w0(b), w0(b) being the wave of its first visible page.
-    int sb = 0;                       // next sequence to look at
+    int sb = 0;                       // first sequence of the range
     int vincl = 0, vpages = 0, vv = 0, vn = 0, vlo = 0, vi0 = 0, vrl = 0;
     const int C = prm.bal_start;
     int T = 0, Weff = 0;
     int64_t rA = 0, rE = 0;           // the wave's page range
     uint64_t nonempty = 0;
+    // The next segment (sequence nx_b, pages [nx_pg0, nx_pg1)) and its page
+    // ids, fetched one segment ahead.
+    bool nx = false;
+    int nx_b = 0, nx_pg0 = 0, nx_pg1 = 0, nx_ids = 0;
+    auto seq_row = [&](int j) {
+        return prm.page_table + (prm.page_indptr ? size_t(__builtin_amdgcn_readlane(vi0, j))
+                                                 : size_t(j) * prm.pt_stride);
+    };
+    // From sequence s on, the first sequence with visible pages in the
+    // range: sets nx_b, nx_pg0, nx_pg1 and issues the load of its first
+    // page ids; false when none is left (or the next starts past the range).
+    auto find_seg = [&](int s) -> bool {
+        for (;;) {
+            const uint64_t rest = s < kWave ? nonempty & (~0ull << s) : 0ull;
+            if (rest == 0)
+                return false;
+            s = __builtin_amdgcn_readfirstlane(int(__builtin_ctzll(rest)));
+            const int in = __builtin_amdgcn_readlane(vincl, s);
+            const int ex = in - __builtin_amdgcn_readlane(vv, s);
+            if (ex >= rE)
+                return false;
+            // The visible part of the range in sequence s (empty when the
+            // range holds only its start charge).
+            const int64_t r0 = max(rA, int64_t(ex) + C), r1 = min(rE, int64_t(in));
+            if (r0 < r1) {
+                const int fp = __builtin_amdgcn_readlane(vlo, s) / kPage;
+                nx_b = s;
+                nx_pg0 = fp + int(r0 - ex - C);
+                nx_pg1 = fp + int(r1 - ex - C);
+                const int32_t* row = seq_row(s);
+                nx_ids = nx_pg0 + lane < nx_pg1 ? row[nx_pg0 + lane] : 0;
+                return true;
+            }
+            ++s;
+        }
+    };
     if constexpr (BAL) {
         const int B = min(prm.batch, kWave);
         if (lane < B) {
@@ -619,6 +655,7 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
             int32_t* cr = prm.ws_cnt + size_t(lane) * prm.num_q_heads + size_t(kvh) * Gact;
             for (int g = 0; g < Gact; ++g) cr[g] = c;
         }
+        nx = find_seg(sb);
     } else {
         // Sequence blockIdx.z, read as seq_view does, but with the row
         // address formed in each branch: a scalar wait for the row stride
@@ -705,37 +742,25 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     int t0, t1, pg0, pg1, srow;   // srow: the segment's partition (state row) index
     bool active;
     if constexpr (BAL) {
-        // The next sequence with visible pages; done when none is left or
-        // it starts past the range.
-        const uint64_t rest = sb < kWave ? nonempty & (~0ull << sb) : 0ull;
-        if (rest == 0)
+        // The segment whose page ids were fetched ahead; then the ids of the
+        // one after it go out, so that they are in by the time its blocks
+        // start.
+        if (!nx)
             break;
-        sb = __builtin_amdgcn_readfirstlane(int(__builtin_ctzll(rest)));
-        const int in = __builtin_amdgcn_readlane(vincl, sb);
-        const int ex = in - __builtin_amdgcn_readlane(vv, sb);
-        if (ex >= rE)
-            break;
-        // The visible part of the range in sequence sb (empty when the
-        // range holds only its start charge).
-        const int64_t r0 = max(rA, int64_t(ex) + C), r1 = min(rE, int64_t(in));
-        if (r0 >= r1) {
-            ++sb;
-            continue;
-        }
-        b = sb;
-        n = __builtin_amdgcn_readlane(vn, sb);
-        row_len = __builtin_amdgcn_readlane(vrl, sb);
-        pt_row = prm.page_table + (prm.page_indptr ? size_t(__builtin_amdgcn_readlane(vi0, sb))
-                                                   : size_t(b) * prm.pt_stride);
-        const int lo = __builtin_amdgcn_readlane(vlo, sb);
-        const int fp = lo / kPage;
-        pg0 = fp + int(r0 - ex - C);
-        pg1 = fp + int(r1 - ex - C);
+        b = nx_b;
+        pg0 = nx_pg0;
+        pg1 = nx_pg1;
+        ids = nx_ids;
+        n = __builtin_amdgcn_readlane(vn, b);
+        row_len = __builtin_amdgcn_readlane(vrl, b);
+        pt_row = seq_row(b);
+        const int lo = __builtin_amdgcn_readlane(vlo, b);
         t0 = max(pg0 * kPage, lo);
         t1 = min(pg1 * kPage, n);
         active = true;
+        const int ex = __builtin_amdgcn_readlane(vincl, b) - __builtin_amdgcn_readlane(vv, b);
         srow = prel - floor_div((int64_t(ex) + C + 1) * Weff - 1, T);
-        ids = load_ids(pg0, pg1, 0);
+        nx = find_seg(b + 1);
     }
     // q as the MFMA B operand, held in VGPRs: column i16 = query head
     // kvh*G + i16 (zero past G), chunk 4*ks + grp of head_dim.
@@ -1134,10 +1159,8 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
                 }
             }
         }
-        if constexpr (BAL) {
-            ++sb;
+        if constexpr (BAL)
             continue;
-        }
         return;
     }
 
