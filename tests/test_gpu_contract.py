@@ -13,6 +13,8 @@ With desc.debug_checks = 1 the handle also collects a violation bit per kind
     that run backwards or past nnz_pages are reported; the run finishes and
     reads nothing outside the caller's buffers; the next valid run reports
     nothing.
+Each case runs under both schedules: fixed partitions and the
+length-balanced one (whose waves read every sequence's length and row).
 """
 import dataclasses
 
@@ -32,25 +34,29 @@ def _engine(w, debug):
                          max_context_len=1 << 16, rope=w.rope, debug_checks=debug)
 
 
-def _run(eng, p, page_table=None, lens=None, max_ctx=None):
+SCHEDULES = [0, B.PA_DECODE_PARTITION_BALANCED]
+
+
+def _run(eng, p, page_table=None, lens=None, max_ctx=None, S=0):
     d = lambda t: t.cuda()  # noqa: E731
     pt = d(p.page_table if page_table is None else page_table)
     cl = d(p.context_lens if lens is None else lens)
     out, lse = eng(d(p.q), d(p.k_cache), d(p.v_cache), pt, cl, p.scale,
                    max_context_len=p.max_context_len if max_ctx is None else max_ctx,
-                   sliding_window=p.window, partition_size=p.workload.partition_size)
+                   sliding_window=p.window, partition_size=S)
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu()
 
 
+@pytest.mark.parametrize("S", SCHEDULES)
 @pytest.mark.parametrize("rope", [None, (500000.0, 1.0)])
-def test_valid_runs_report_nothing_and_match(rope):
+def test_valid_runs_report_nothing_and_match(rope, S):
     w = W.custom(batch=3, num_q_heads=16, num_kv_heads=4, head_dim=128, dtype=torch.float16,
                  context_lens=[1, 700, 3060], seed=700, rope=rope)
     p = W.generate(w)
     plain, checked = _engine(w, 0), _engine(w, 1)
-    a = _run(plain, p)
-    b = _run(checked, p)
+    a = _run(plain, p, S=S)
+    b = _run(checked, p, S=S)
     assert B.pa_decode_debug_status(checked.handle) == 0
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     with pytest.raises(B.PaDecodeError):
@@ -59,9 +65,10 @@ def test_valid_runs_report_nothing_and_match(rope):
     compare(b[0], b[1], ref[0], ref[1], w.dtype, what="checked run")
 
 
+@pytest.mark.parametrize("S", SCHEDULES)
 @pytest.mark.parametrize("window", [0, 500])
 @pytest.mark.parametrize("bad_id", ["past_pool", "negative"])
-def test_out_of_range_page_ids_are_reported(window, bad_id):
+def test_out_of_range_page_ids_are_reported(window, bad_id, S):
     w = W.custom(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=64, dtype=torch.float16,
                  context_lens=[900, 2000], seed=701, window=window)
     p = W.generate(w)
@@ -69,16 +76,17 @@ def test_out_of_range_page_ids_are_reported(window, bad_id):
     pt = p.page_table.clone()
     num_pages = p.k_cache.shape[0]
     pt[1, 100] = num_pages + 7 if bad_id == "past_pool" else -1   # a page of tokens 1600..1615
-    out, lse = _run(eng, p, page_table=pt)
+    out, lse = _run(eng, p, page_table=pt, S=S)
     assert B.pa_decode_debug_status(eng.handle) & B.PA_DECODE_VIOLATION_PAGE
     # Sequence 0 is untouched by the bad entry of row 1.
     ref = run_oracle(p)
     compare(out[:1], lse[:1], ref[0][:1], ref[1][:1], w.dtype, what="row 0 beside a bad row")
-    _run(eng, p)
+    _run(eng, p, S=S)
     assert B.pa_decode_debug_status(eng.handle) == 0
 
 
-def test_lengths_outside_the_contract_are_reported():
+@pytest.mark.parametrize("S", SCHEDULES)
+def test_lengths_outside_the_contract_are_reported(S):
     w = W.custom(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype=torch.bfloat16,
                  context_lens=[300, 1000, 64], seed=702)
     p = W.generate(w)
@@ -86,14 +94,15 @@ def test_lengths_outside_the_contract_are_reported():
     for bad in (1001, 5000, -5):
         lens = p.context_lens.clone()
         lens[1] = bad
-        out, lse = _run(eng, p, lens=lens, max_ctx=1000)
+        out, lse = _run(eng, p, lens=lens, max_ctx=1000, S=S)
         assert B.pa_decode_debug_status(eng.handle) & B.PA_DECODE_VIOLATION_LENGTH, bad
         assert torch.isfinite(out).all()
-    _run(eng, p)
+    _run(eng, p, S=S)
     assert B.pa_decode_debug_status(eng.handle) == 0
 
 
-def test_csr_rows_outside_the_contract_are_reported():
+@pytest.mark.parametrize("S", SCHEDULES)
+def test_csr_rows_outside_the_contract_are_reported(S):
     w = W.custom(batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64, dtype=torch.float16,
                  context_lens=[50, 700, 333], seed=703)
     p = W.generate(w)
@@ -106,7 +115,7 @@ def test_csr_rows_outside_the_contract_are_reported():
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
         args = eng.make_csr_args(q, k, v, indptr.cuda(), indices.cuda(),
                                  csr.last_page_len.cuda(), csr.nnz_pages, p.scale, out, lse,
-                                 max_context_len=p.max_context_len)
+                                 max_context_len=p.max_context_len, partition_size=S)
         eng.run_csr_args(args)
         torch.cuda.synchronize()
         return B.pa_decode_debug_status(eng.handle)
@@ -124,12 +133,13 @@ def test_csr_rows_outside_the_contract_are_reported():
     assert run(csr.indptr, csr.indices) == 0
 
 
-def test_rotary_kernel_reports_bad_page_ids():
+@pytest.mark.parametrize("S", SCHEDULES)
+def test_rotary_kernel_reports_bad_page_ids(S):
     w = W.custom(batch=1, num_q_heads=16, num_kv_heads=4, head_dim=128, dtype=torch.float16,
                  context_lens=[1500], seed=704, rope=(10000.0, 1.0))
     p = W.generate(w)
     eng = _engine(w, 1)
     pt = p.page_table.clone()
     pt[0, 10] = 1 << 30
-    _run(eng, p, page_table=pt)
+    _run(eng, p, page_table=pt, S=S)
     assert B.pa_decode_debug_status(eng.handle) & B.PA_DECODE_VIOLATION_PAGE
