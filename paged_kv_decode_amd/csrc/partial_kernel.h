@@ -739,474 +739,474 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
 
     // One segment per pass; the fixed schedule makes exactly one pass.
     for (;;) {
-    int t0, t1, pg0, pg1, srow;   // srow: the segment's partition (state row) index
-    bool active;
-    if constexpr (BAL) {
-        // The segment whose page ids were fetched ahead; then the ids of the
-        // one after it go out, so that they are in by the time its blocks
-        // start.
-        if (!nx)
-            break;
-        b = nx_b;
-        pg0 = nx_pg0;
-        pg1 = nx_pg1;
-        ids = nx_ids;
-        n = __builtin_amdgcn_readlane(vn, b);
-        row_len = __builtin_amdgcn_readlane(vrl, b);
-        pt_row = seq_row(b);
-        const int lo = __builtin_amdgcn_readlane(vlo, b);
-        t0 = max(pg0 * kPage, lo);
-        t1 = min(pg1 * kPage, n);
-        active = true;
-        const int ex = __builtin_amdgcn_readlane(vincl, b) - __builtin_amdgcn_readlane(vv, b);
-        srow = prel - floor_div((int64_t(ex) + C + 1) * Weff - 1, T);
-        nx = find_seg(b + 1);
-    }
-    // q as the MFMA B operand, held in VGPRs: column i16 = query head
-    // kvh*G + i16 (zero past G), chunk 4*ks + grp of head_dim.
-    u32x4 qa[KS];
-    {
-        const bool real = i16 < Gact;
-        const char* qrow = static_cast<const char*>(prm.q) +
-                           (size_t(b) * prm.num_q_heads + size_t(kvh) * Gact + (real ? i16 : 0)) * D * EB;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 z = {0u, 0u, 0u, 0u};
-            qa[ks] = real ? load16(qrow + (4 * ks + grp) * 16) : z;
+        int t0, t1, pg0, pg1, srow;   // srow: the segment's partition (state row) index
+        bool active;
+        if constexpr (BAL) {
+            // The segment whose page ids were fetched ahead; then the ids of the
+            // one after it go out, so that they are in by the time its blocks
+            // start.
+            if (!nx)
+                break;
+            b = nx_b;
+            pg0 = nx_pg0;
+            pg1 = nx_pg1;
+            ids = nx_ids;
+            n = __builtin_amdgcn_readlane(vn, b);
+            row_len = __builtin_amdgcn_readlane(vrl, b);
+            pt_row = seq_row(b);
+            const int lo = __builtin_amdgcn_readlane(vlo, b);
+            t0 = max(pg0 * kPage, lo);
+            t1 = min(pg1 * kPage, n);
+            active = true;
+            const int ex = __builtin_amdgcn_readlane(vincl, b) - __builtin_amdgcn_readlane(vv, b);
+            srow = prel - floor_div((int64_t(ex) + C + 1) * Weff - 1, T);
+            nx = find_seg(b + 1);
         }
-    }
-
-    if constexpr (!BAL) {
-        const int lo = (prm.window > 0 && n > prm.window) ? n - prm.window : 0;
-        const int pabs = lo / S + prel;
-        t0 = max(pabs * S, lo);
-        t1 = min(pabs * S + S, n);
-        active = prel < prm.num_partitions && t0 < t1;
-        pg0 = t0 / kPage;
-        pg1 = (t1 + kPage - 1) / kPage;
-        srow = prel;
-        if (prm.window > 0 && active)
-            ids = load_ids(pg0, pg1, 0);
-    }
-
-    const int64_t ss = prm.stride_slot;
-    const char* kbase = static_cast<const char*>(prm.k) + int64_t(kvh) * prm.stride_head * EB;
-    const char* vbase = static_cast<const char*>(prm.v) + int64_t(kvh) * prm.stride_head * EB;
-
-    // Online-softmax state of head i16 (the same in the four lane groups;
-    // the denominator holds the lane's own tokens until the end).
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 acc[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    u32x4* ktile = reinterpret_cast<u32x4*>(smem + wave * WS);
-    u32x4* vtile = ktile + KT;
-    float2* rtab = reinterpret_cast<float2*>(vtile + KT);   // ROT: [NB][HD] (cos, sin)
-    // Tile layout (K and V alike): chunk j of tile row r (page r / 16, token
-    // r % 16) sits at slot tix(r, j).  Power-of-two rows: r * CH + (j ^
-    // swz(r)), where swz permutes within aligned groups of 8 chunks, so a
-    // 128-byte line still lands whole, and the 16 rows one read touches fall
-    // in distinct 16-byte bank groups.  12-chunk rows (head_dim 96): rows
-    // padded to an odd 13 slots, which spreads 16 consecutive rows over all
-    // 16 bank groups without a swizzle.
-    auto swz = [](int r) { return CH >= 16 ? (r & 15) : ((r >> 1) & 7); };
-    auto tix = [&](int r, int j) {
-        if constexpr (POW2) return r * CH + (j ^ swz(r));
-        else return r * CHP + j;
-    };
-
-    // Bases of the block's pages: entry nb * HD + i of rtab.
-    auto fill_bases = [&](int pgb) {
-#pragma unroll
-        for (int k = 0; k < NE; ++k) {
-            const int e = lane + kWave * k;
-            if (NE * kWave == NB * HD || e < NB * HD) {
-                const int pos = (pgb + e / HD) * kPage - (n - 1);
-                double x = double(pos) * ftab[e % HD];
-                x -= rint(x);
-                float sn, c;
-                sincos_rev(float(x), &sn, &c);
-                rtab[e] = make_float2(c, sn);
-            }
-        }
-    };
-    // The score MFMAs of page nb with turned keys.
-    auto turned_scores = [&](int nb) {
-        using TK = TurnedKey<DT>;
-        static_assert(TK::EPC == EPC, "turned-key chunk width");
-        const int row = nb * kPage + i16;
-        const float2* bt = rtab + nb * HD;
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
-        const float2* ot = reinterpret_cast<const float2*>(otab + i16 * TS);
-        auto angle = [&](int i0, float (&cs)[EPC], float (&sn)[EPC]) {
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                const float2 bb = bt[i0 + e], oo = ot[i0 + e];
-                cs[e] = bb.x * oo.x - bb.y * oo.y;
-                sn[e] = bb.y * oo.x + bb.x * oo.y;
-            }
-        };
-        if constexpr (KS % 2 == 0) {
-            // Chunk fs (first half) and fs + KS/2 (second half) of the lane.
-#pragma unroll
-            for (int fs = 0; fs < KS / 2; ++fs) {
-                if constexpr (KS >= 8) {
-                    if (fs > 0)
-                        pin_loads();   // head_dim 256: one chunk pair at a time
-                }
-                float cs[EPC], sn[EPC];
-                angle(EPC * (4 * fs + grp), cs, sn);
-                const u32x4 xc = ktile[tix(row, 4 * fs + grp)];
-                const u32x4 yc = ktile[tix(row, 4 * (fs + KS / 2) + grp)];
-                if constexpr (DT != PA_DTYPE_F32) {
-                    d = TK::turn_mfma(xc, yc, cs, sn, qa[fs], qa[fs + KS / 2], d, prm.minus_one);
-                } else {
-                    float x[EPC], y[EPC], xr[EPC], yr[EPC];
-                    TK::widen(xc, x);
-                    TK::widen(yc, y);
-#pragma unroll
-                    for (int e = 0; e < EPC; ++e) {
-                        xr[e] = x[e] * cs[e] - y[e] * sn[e];
-                        yr[e] = y[e] * cs[e] + x[e] * sn[e];
-                    }
-                    d = TK::mfma(xr, qa[fs], d);
-                    d = TK::mfma(yr, qa[fs + KS / 2], d);
-                }
-            }
-        } else {
-            // Odd chunk count (head_dim 96): the partner chunk of the other
-            // half is a second LDS read.
+        // q as the MFMA B operand, held in VGPRs: column i16 = query head
+        // kvh*G + i16 (zero past G), chunk 4*ks + grp of head_dim.
+        u32x4 qa[KS];
+        {
+            const bool real = i16 < Gact;
+            const char* qrow = static_cast<const char*>(prm.q) +
+                               (size_t(b) * prm.num_q_heads + size_t(kvh) * Gact + (real ? i16 : 0)) * D * EB;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int c = 4 * ks + grp;
-                const bool first = c < CH / 2;
-                float cs[EPC], sn[EPC], x[EPC], y[EPC], xr[EPC];
-                angle(EPC * (first ? c : c - CH / 2), cs, sn);
-                TK::widen(ktile[tix(row, c)], x);
-                TK::widen(ktile[tix(row, first ? c + CH / 2 : c - CH / 2)], y);
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) xr[e] = x[e] * cs[e] + (first ? -y[e] : y[e]) * sn[e];
-                d = TK::mfma(xr, qa[ks], d);
+                u32x4 z = {0u, 0u, 0u, 0u};
+                qa[ks] = real ? load16(qrow + (4 * ks + grp) * 16) : z;
             }
         }
-        return d;
-    };
 
-    const int nblk = active ? (pg1 - pg0 + NB - 1) / NB : 0;
-    const int nit = nblk > wi ? (nblk - wi + wpp - 1) / wpp : 0;
+        if constexpr (!BAL) {
+            const int lo = (prm.window > 0 && n > prm.window) ? n - prm.window : 0;
+            const int pabs = lo / S + prel;
+            t0 = max(pabs * S, lo);
+            t1 = min(pabs * S + S, n);
+            active = prel < prm.num_partitions && t0 < t1;
+            pg0 = t0 / kPage;
+            pg1 = (t1 + kPage - 1) / kPage;
+            srow = prel;
+            if (prm.window > 0 && active)
+                ids = load_ids(pg0, pg1, 0);
+        }
 
-    // Software pipeline over the wave's blocks: as soon as block it's K and V
-    // rows are in the LDS tiles, the registers take block it+1's loads, so the
-    // loads of one block are in flight while the previous block is computed.
-    // Every phase issues exactly 2*NB*KS loads, with no branch around the
-    // individual pages, so that each wait leaves the younger loads in flight:
-    // a page past the end of a short block gets a zero lane offset, i.e. all
-    // lanes read one 16-byte piece of a page.  The last step of a chunk
-    // issues nothing (one wave-uniform branch), which shortens the
-    // single-block waves of short contexts.
-    u32x4 kr[NB][KS], vr[NB][KS];
-    int64_t page[NB];
-    uint32_t pmask[NB];
-    // Byte offset of this lane's chunk of load instruction i in a page.  For
-    // power-of-two rows it is loff[0] + i * lstep, with a wave-uniform step
-    // (instruction i reads rows R*i + lane/CH), so one VGPR holds them all.
-    uint32_t loff[POW2 ? 1 : KS];
+        const int64_t ss = prm.stride_slot;
+        const char* kbase = static_cast<const char*>(prm.k) + int64_t(kvh) * prm.stride_head * EB;
+        const char* vbase = static_cast<const char*>(prm.v) + int64_t(kvh) * prm.stride_head * EB;
+
+        // Online-softmax state of head i16 (the same in the four lane groups;
+        // the denominator holds the lane's own tokens until the end).
+        float m_run = -INFINITY, l_run = 0.f;
+        f32x4 acc[NDB];
 #pragma unroll
-    for (int i = 0; i < (POW2 ? 1 : KS); ++i)
-        loff[i] = uint32_t((int64_t(lrow(i)) * ss + int64_t(lchk(i)) * EPC) * EB);
-    const uint32_t lstep = uint32_t(int64_t(R) * ss * EB);
-    auto fetch_ids = [&](int itn, int it0, int it1) {
-        // Page ids of block `itn` into scalar registers (ids holds the blocks
-        // it0 .. it0 + IPV - 1).
-        const int itc = min(itn, it1 - 1);
-        const int nbv_ = itn < it1 ? min(NB, pg1 - (pg0 + (wi + wpp * itn) * NB)) : 0;
+        for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        u32x4* ktile = reinterpret_cast<u32x4*>(smem + wave * WS);
+        u32x4* vtile = ktile + KT;
+        float2* rtab = reinterpret_cast<float2*>(vtile + KT);   // ROT: [NB][HD] (cos, sin)
+        // Tile layout (K and V alike): chunk j of tile row r (page r / 16, token
+        // r % 16) sits at slot tix(r, j).  Power-of-two rows: r * CH + (j ^
+        // swz(r)), where swz permutes within aligned groups of 8 chunks, so a
+        // 128-byte line still lands whole, and the 16 rows one read touches fall
+        // in distinct 16-byte bank groups.  12-chunk rows (head_dim 96): rows
+        // padded to an odd 13 slots, which spreads 16 consecutive rows over all
+        // 16 bank groups without a swizzle.
+        auto swz = [](int r) { return CH >= 16 ? (r & 15) : ((r >> 1) & 7); };
+        auto tix = [&](int r, int j) {
+            if constexpr (POW2) return r * CH + (j ^ swz(r));
+            else return r * CHP + j;
+        };
+
+        // Bases of the block's pages: entry nb * HD + i of rtab.
+        auto fill_bases = [&](int pgb) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            // A page id outside the pool reads page 0 instead (reported
-            // when it belongs to the block; ids past the block are padding).
-            const int id = __builtin_amdgcn_readlane(ids, (itc - it0) * NB + nb);
-            const bool ok = uint32_t(id) < uint32_t(prm.num_pages);
-            violation |= (ok || nb >= nbv_) ? 0 : PA_DECODE_VIOLATION_PAGE;
-            page[nb] = ok ? id : 0;
-            uint32_t m = __builtin_amdgcn_readfirstlane(nb < nbv_ ? ~0u : 0u);
-            asm volatile("" : "+s"(m));  // an opaque mask, not a branch condition
-            pmask[nb] = m;
-        }
-    };
-    auto issue = [&](const char* base, u32x4 (&r)[NB][KS]) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const char* pb = base + page[nb] * prm.stride_page * EB;
-#pragma unroll
-            for (int i = 0; i < KS; ++i) {
-                if constexpr (POW2)
-                    r[nb][i] = load16_stream(pb + ((uint32_t(i) * lstep) & pmask[nb]) +
-                                             (loff[0] & pmask[nb]));
-                else
-                    r[nb][i] = load16_stream(pb + (loff[i] & pmask[nb]));
-            }
-        }
-    };
-    // Registers -> swizzled tile; V rows of tokens outside [t0, t1) (or of
-    // pages past the block's end) become zero, so that slots the method must
-    // not read never reach the output (their probabilities are already 0).
-    auto stage = [&](u32x4* tile, const u32x4 (&r)[NB][KS], bool zero_invalid, int pgb, int nbv) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int i = 0; i < KS; ++i) {
-                const int row = nb * kPage + lrow(i);
-                u32x4 x = r[nb][i];
-                if (zero_invalid) {
-                    const int tok = (pgb + nb) * kPage + lrow(i);
-                    const u32x4 z = {0u, 0u, 0u, 0u};
-                    x = (nb < nbv && tok >= t0 && tok < t1) ? x : z;
+            for (int k = 0; k < NE; ++k) {
+                const int e = lane + kWave * k;
+                if (NE * kWave == NB * HD || e < NB * HD) {
+                    const int pos = (pgb + e / HD) * kPage - (n - 1);
+                    double x = double(pos) * ftab[e % HD];
+                    x -= rint(x);
+                    float sn, c;
+                    sincos_rev(float(x), &sn, &c);
+                    rtab[e] = make_float2(c, sn);
                 }
-                tile[tix(row, lchk(i))] = x;
             }
-    };
+        };
+        // The score MFMAs of page nb with turned keys.
+        auto turned_scores = [&](int nb) {
+            using TK = TurnedKey<DT>;
+            static_assert(TK::EPC == EPC, "turned-key chunk width");
+            const int row = nb * kPage + i16;
+            const float2* bt = rtab + nb * HD;
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+            const float2* ot = reinterpret_cast<const float2*>(otab + i16 * TS);
+            auto angle = [&](int i0, float (&cs)[EPC], float (&sn)[EPC]) {
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) {
+                    const float2 bb = bt[i0 + e], oo = ot[i0 + e];
+                    cs[e] = bb.x * oo.x - bb.y * oo.y;
+                    sn[e] = bb.y * oo.x + bb.x * oo.y;
+                }
+            };
+            if constexpr (KS % 2 == 0) {
+                // Chunk fs (first half) and fs + KS/2 (second half) of the lane.
+#pragma unroll
+                for (int fs = 0; fs < KS / 2; ++fs) {
+                    if constexpr (KS >= 8) {
+                        if (fs > 0)
+                            pin_loads();   // head_dim 256: one chunk pair at a time
+                    }
+                    float cs[EPC], sn[EPC];
+                    angle(EPC * (4 * fs + grp), cs, sn);
+                    const u32x4 xc = ktile[tix(row, 4 * fs + grp)];
+                    const u32x4 yc = ktile[tix(row, 4 * (fs + KS / 2) + grp)];
+                    if constexpr (DT != PA_DTYPE_F32) {
+                        d = TK::turn_mfma(xc, yc, cs, sn, qa[fs], qa[fs + KS / 2], d, prm.minus_one);
+                    } else {
+                        float x[EPC], y[EPC], xr[EPC], yr[EPC];
+                        TK::widen(xc, x);
+                        TK::widen(yc, y);
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e) {
+                            xr[e] = x[e] * cs[e] - y[e] * sn[e];
+                            yr[e] = y[e] * cs[e] + x[e] * sn[e];
+                        }
+                        d = TK::mfma(xr, qa[fs], d);
+                        d = TK::mfma(yr, qa[fs + KS / 2], d);
+                    }
+                }
+            } else {
+                // Odd chunk count (head_dim 96): the partner chunk of the other
+                // half is a second LDS read.
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int c = 4 * ks + grp;
+                    const bool first = c < CH / 2;
+                    float cs[EPC], sn[EPC], x[EPC], y[EPC], xr[EPC];
+                    angle(EPC * (first ? c : c - CH / 2), cs, sn);
+                    TK::widen(ktile[tix(row, c)], x);
+                    TK::widen(ktile[tix(row, first ? c + CH / 2 : c - CH / 2)], y);
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) xr[e] = x[e] * cs[e] + (first ? -y[e] : y[e]) * sn[e];
+                    d = TK::mfma(xr, qa[ks], d);
+                }
+            }
+            return d;
+        };
 
-    // One pipeline step: block it's rows go from the registers to the tiles,
-    // the registers take block it+1's loads, then block it is computed.
-    auto step = [&](int it, int it0, int it1) {
-        const int pgb = pg0 + (wi + wpp * it) * NB;
-        const int nbv = min(NB, pg1 - pgb);
-        // Edge blocks only (partition or window ends, short blocks) need
-        // the V mask (wave-uniform).
-        const bool edge = nbv < NB || pgb * kPage < t0 || (pgb + NB) * kPage > t1;
+        const int nblk = active ? (pg1 - pg0 + NB - 1) / NB : 0;
+        const int nit = nblk > wi ? (nblk - wi + wpp - 1) / wpp : 0;
 
-        if constexpr (ROT)
-            fill_bases(pgb);
-        stage(ktile, kr, false, pgb, nbv);
-        if (edge)
-            stage(vtile, vr, true, pgb, nbv);
-        else
-            stage(vtile, vr, false, pgb, nbv);
-        wave_lds_sync();
-        if (it + 1 < it1) {
-            // The next block of this chunk (the loads of a following chunk
-            // are issued once its page ids are in).
-            fetch_ids(it + 1, it0, it1);
+        // Software pipeline over the wave's blocks: as soon as block it's K and V
+        // rows are in the LDS tiles, the registers take block it+1's loads, so the
+        // loads of one block are in flight while the previous block is computed.
+        // Every phase issues exactly 2*NB*KS loads, with no branch around the
+        // individual pages, so that each wait leaves the younger loads in flight:
+        // a page past the end of a short block gets a zero lane offset, i.e. all
+        // lanes read one 16-byte piece of a page.  The last step of a chunk
+        // issues nothing (one wave-uniform branch), which shortens the
+        // single-block waves of short contexts.
+        u32x4 kr[NB][KS], vr[NB][KS];
+        int64_t page[NB];
+        uint32_t pmask[NB];
+        // Byte offset of this lane's chunk of load instruction i in a page.  For
+        // power-of-two rows it is loff[0] + i * lstep, with a wave-uniform step
+        // (instruction i reads rows R*i + lane/CH), so one VGPR holds them all.
+        uint32_t loff[POW2 ? 1 : KS];
+#pragma unroll
+        for (int i = 0; i < (POW2 ? 1 : KS); ++i)
+            loff[i] = uint32_t((int64_t(lrow(i)) * ss + int64_t(lchk(i)) * EPC) * EB);
+        const uint32_t lstep = uint32_t(int64_t(R) * ss * EB);
+        auto fetch_ids = [&](int itn, int it0, int it1) {
+            // Page ids of block `itn` into scalar registers (ids holds the blocks
+            // it0 .. it0 + IPV - 1).
+            const int itc = min(itn, it1 - 1);
+            const int nbv_ = itn < it1 ? min(NB, pg1 - (pg0 + (wi + wpp * itn) * NB)) : 0;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                // A page id outside the pool reads page 0 instead (reported
+                // when it belongs to the block; ids past the block are padding).
+                const int id = __builtin_amdgcn_readlane(ids, (itc - it0) * NB + nb);
+                const bool ok = uint32_t(id) < uint32_t(prm.num_pages);
+                violation |= (ok || nb >= nbv_) ? 0 : PA_DECODE_VIOLATION_PAGE;
+                page[nb] = ok ? id : 0;
+                uint32_t m = __builtin_amdgcn_readfirstlane(nb < nbv_ ? ~0u : 0u);
+                asm volatile("" : "+s"(m));  // an opaque mask, not a branch condition
+                pmask[nb] = m;
+            }
+        };
+        auto issue = [&](const char* base, u32x4 (&r)[NB][KS]) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const char* pb = base + page[nb] * prm.stride_page * EB;
+#pragma unroll
+                for (int i = 0; i < KS; ++i) {
+                    if constexpr (POW2)
+                        r[nb][i] = load16_stream(pb + ((uint32_t(i) * lstep) & pmask[nb]) +
+                                                 (loff[0] & pmask[nb]));
+                    else
+                        r[nb][i] = load16_stream(pb + (loff[i] & pmask[nb]));
+                }
+            }
+        };
+        // Registers -> swizzled tile; V rows of tokens outside [t0, t1) (or of
+        // pages past the block's end) become zero, so that slots the method must
+        // not read never reach the output (their probabilities are already 0).
+        auto stage = [&](u32x4* tile, const u32x4 (&r)[NB][KS], bool zero_invalid, int pgb, int nbv) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int i = 0; i < KS; ++i) {
+                    const int row = nb * kPage + lrow(i);
+                    u32x4 x = r[nb][i];
+                    if (zero_invalid) {
+                        const int tok = (pgb + nb) * kPage + lrow(i);
+                        const u32x4 z = {0u, 0u, 0u, 0u};
+                        x = (nb < nbv && tok >= t0 && tok < t1) ? x : z;
+                    }
+                    tile[tix(row, lchk(i))] = x;
+                }
+        };
+
+        // One pipeline step: block it's rows go from the registers to the tiles,
+        // the registers take block it+1's loads, then block it is computed.
+        auto step = [&](int it, int it0, int it1) {
+            const int pgb = pg0 + (wi + wpp * it) * NB;
+            const int nbv = min(NB, pg1 - pgb);
+            // Edge blocks only (partition or window ends, short blocks) need
+            // the V mask (wave-uniform).
+            const bool edge = nbv < NB || pgb * kPage < t0 || (pgb + NB) * kPage > t1;
+
+            if constexpr (ROT)
+                fill_bases(pgb);
+            stage(ktile, kr, false, pgb, nbv);
+            if (edge)
+                stage(vtile, vr, true, pgb, nbv);
+            else
+                stage(vtile, vr, false, pgb, nbv);
+            wave_lds_sync();
+            if (it + 1 < it1) {
+                // The next block of this chunk (the loads of a following chunk
+                // are issued once its page ids are in).
+                fetch_ids(it + 1, it0, it1);
+                issue(kbase, kr);
+                pin_loads();
+                issue(vbase, vr);
+                pin_loads();
+            }
+
+            // Scores (base 2) of head i16 against token 4*grp + r of each page.
+            float s[NB][4];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                f32x4 d = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (ROT) {
+                    // One page at a time: the turned keys of a page take ~90
+                    // VGPRs while they are formed.
+                    pin_loads();
+                    d = turned_scores(nb);
+                } else {
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        d = Chunk<DT>::mfma(ktile[tix(nb * kPage + i16, 4 * ks + grp)], qa[ks], d);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tok = (pgb + nb) * kPage + 4 * grp + r;
+                    const bool ok = nb < nbv && tok >= t0 && tok < t1;
+                    s[nb][r] = ok ? d[r] * prm.scale_log2 : -INFINITY;
+                }
+            }
+
+            // Block maximum of head i16: the lane's own 4*NB scores, then the
+            // four lane groups.
+            float bm = s[0][0];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bm = fmaxf(bm, s[nb][r]);
+            bm = rows4_max(bm);
+            // The reference value m_run the exponentials are taken against
+            // moves only when the block maximum passes it by more than
+            // kSlack (so p <= 2^kSlack, exact in f16 / bf16 hi+lo and f32);
+            // the state (m, l, acc) is exact for any reference, since the
+            // result is acc / l and m + log2(l).  The output accumulators
+            // then need rescaling only on those rare moves (wave-uniform
+            // decision).
+            const bool grow = bm > m_run + kSlack;
+            const float mnew = grow ? bm : m_run;
+            const float alpha = grow ? fast_exp2(m_run - bm) : 1.f;
+            const bool any_rescale = __any(grow && i16 < G);
+            float ps = 0.f;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    s[nb][r] = fast_exp2(s[nb][r] - mnew);
+                    ps += s[nb][r];
+                }
+            l_run = alpha * l_run + ps;
+            m_run = mnew;
+
+            if (any_rescale) {
+                // Row 4*grp + r of the output blocks is head 4*grp + r, whose
+                // alpha sits in lane 4*grp + r.
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float a = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) acc[db][r] *= a;
+                }
+            }
+
+            // P.V: V rows 4*grp + i16/4 of each page, columns 16*db +
+            // 4*(i16%4) .. +3 for the transpose read.
+            auto tr_read = [&](int nb, int db) -> s16x4 {
+                const int vrow = nb * kPage + 4 * grp + (i16 >> 2);
+                const int j = 2 * db + ((i16 & 3) >> 1);
+                const char* addr = reinterpret_cast<const char*>(vtile + tix(vrow, j)) + (i16 & 1) * 8;
+                return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(addr));
+            };
+            if constexpr (DT == PA_DTYPE_F32) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    // 16x16x4 f32 steps: step r takes token 4*grp + r of every
+                    // lane group (k index grp).
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = nb * kPage + 4 * grp + r;
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db) {
+                            const int col = 16 * db + i16;
+                            const float v = reinterpret_cast<const float*>(vtile + tix(row, col >> 2))[col & 3];
+                            acc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(s[nb][r], v, acc[db], 0, 0, 0);
+                        }
+                    }
+                }
+            } else if constexpr (NB % 2 == 0) {
+                // Pages in pairs: 32 tokens per MFMA (the same issue cost as 16).
+#pragma unroll
+                for (int nb = 0; nb < NB; nb += 2) {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        acc[db] = PV2<DT>::mma(s[nb], s[nb + 1], tr_read(nb, db), tr_read(nb + 1, db), acc[db]);
+                }
+            } else {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) acc[db] = PV<DT>::mma(s[nb], tr_read(nb, db), acc[db]);
+                }
+            }
+        };
+
+        // Outer loop over chunks of IPV blocks (one page-id vector each); the
+        // pipelined inner loop itself issues no load but K/V.
+        for (int it0 = 0; it0 < nit; it0 += IPV) {
+            const int it1 = min(nit, it0 + IPV);
+            if (it0 > 0)
+                ids = load_ids(pg0, pg1, it0);
+            fetch_ids(it0, it0, it1);
             issue(kbase, kr);
             pin_loads();
             issue(vbase, vr);
             pin_loads();
+            for (int it = it0; it < it1; ++it) step(it, it0, it1);
+        }  // chunks of IPV blocks
+
+        if constexpr (!BAL) {
+            if (prm.status && violation != 0 && lane == 0)
+                __hip_atomic_fetch_or(prm.status, violation, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 
-        // Scores (base 2) of head i16 against token 4*grp + r of each page.
-        float s[NB][4];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            f32x4 d = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (ROT) {
-                // One page at a time: the turned keys of a page take ~90
-                // VGPRs while they are formed.
-                pin_loads();
-                d = turned_scores(nb);
+        // Denominator of head i16 over the four lane groups.
+        l_run = rows4_sum(l_run);
+
+        // Result of (query head g of the group, partition p_rel): the partition
+        // state (o normalised, max, denominator) for the merge, or, when one
+        // partition covers the context, out and lse (an empty context gives
+        // out = 0, lse = -inf).
+        auto emit = [&](int g, int p_rel, int dd, float o, float M, float L, bool head_lane) {
+            const size_t h = size_t(b) * prm.num_q_heads + size_t(kvh) * Gact + g;
+            if (prm.split) {
+                const size_t row = h * prm.num_partitions + p_rel;
+                prm.ws_o[row * D + dd] = o;
+                if (head_lane) {
+                    prm.ws_m[row] = M;
+                    prm.ws_l[row] = L;
+                }
             } else {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    d = Chunk<DT>::mfma(ktile[tix(nb * kPage + i16, 4 * ks + grp)], qa[ks], d);
+                store_out<DT>(prm.out, h * D + dd, o);
+                if (head_lane && prm.lse) prm.lse[h] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tok = (pgb + nb) * kPage + 4 * grp + r;
-                const bool ok = nb < nbv && tok >= t0 && tok < t1;
-                s[nb][r] = ok ? d[r] * prm.scale_log2 : -INFINITY;
-            }
-        }
-
-        // Block maximum of head i16: the lane's own 4*NB scores, then the
-        // four lane groups.
-        float bm = s[0][0];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) bm = fmaxf(bm, s[nb][r]);
-        bm = rows4_max(bm);
-        // The reference value m_run the exponentials are taken against
-        // moves only when the block maximum passes it by more than
-        // kSlack (so p <= 2^kSlack, exact in f16 / bf16 hi+lo and f32);
-        // the state (m, l, acc) is exact for any reference, since the
-        // result is acc / l and m + log2(l).  The output accumulators
-        // then need rescaling only on those rare moves (wave-uniform
-        // decision).
-        const bool grow = bm > m_run + kSlack;
-        const float mnew = grow ? bm : m_run;
-        const float alpha = grow ? fast_exp2(m_run - bm) : 1.f;
-        const bool any_rescale = __any(grow && i16 < G);
-        float ps = 0.f;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                s[nb][r] = fast_exp2(s[nb][r] - mnew);
-                ps += s[nb][r];
-            }
-        l_run = alpha * l_run + ps;
-        m_run = mnew;
-
-        if (any_rescale) {
-            // Row 4*grp + r of the output blocks is head 4*grp + r, whose
-            // alpha sits in lane 4*grp + r.
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float a = __shfl(alpha, 4 * grp + r);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) acc[db][r] *= a;
-            }
-        }
-
-        // P.V: V rows 4*grp + i16/4 of each page, columns 16*db +
-        // 4*(i16%4) .. +3 for the transpose read.
-        auto tr_read = [&](int nb, int db) -> s16x4 {
-            const int vrow = nb * kPage + 4 * grp + (i16 >> 2);
-            const int j = 2 * db + ((i16 & 3) >> 1);
-            const char* addr = reinterpret_cast<const char*>(vtile + tix(vrow, j)) + (i16 & 1) * 8;
-            return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(addr));
         };
-        if constexpr (DT == PA_DTYPE_F32) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                // 16x16x4 f32 steps: step r takes token 4*grp + r of every
-                // lane group (k index grp).
+
+        if (wpp == 1) {
+            // Every wave owns its partition: write straight from the output
+            // blocks (row 4*grp + r of block db is head 4*grp + r, column
+            // 16*db + i16); the max and denominator of head 4*grp + r sit in
+            // lane 4*grp + r.  No LDS, no barrier.
+            if (uint32_t(srow) < uint32_t(prm.num_partitions)) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = nb * kPage + 4 * grp + r;
+                    const int g = 4 * grp + r;
+                    const float M = __shfl(m_run, g);
+                    const float L = __shfl(l_run, g);
+                    if (g < Gact) {
+                        const float inv = M == -INFINITY ? 0.f : 1.f / L;
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const int col = 16 * db + i16;
-                        const float v = reinterpret_cast<const float*>(vtile + tix(row, col >> 2))[col & 3];
-                        acc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(s[nb][r], v, acc[db], 0, 0, 0);
+                        for (int db = 0; db < NDB; ++db)
+                            emit(g, srow, 16 * db + i16, acc[db][r] * inv, M, L, db == 0 && i16 == 0);
                     }
                 }
             }
-        } else if constexpr (NB % 2 == 0) {
-            // Pages in pairs: 32 tokens per MFMA (the same issue cost as 16).
+            if constexpr (BAL)
+                continue;
+            return;
+        }
+
+        // Several waves share each partition: combine them in LDS, maximum
+        // first, then the rescaled denominators and outputs.  A wave without
+        // blocks holds max = -inf, denominator 0 and contributes nothing; a slot
+        // whose partition is empty ends with max = -inf.
+        __syncthreads();
+        float* cm = smem;               // [nw][GP4]
+        float* cl = cm + nw * GP4;      // [nw][GP4]
+        float* ca = cl + nw * GP4;      // [nw][G][D]
+        if (grp == 0 && i16 < G) {
+            cm[wave * GP4 + i16] = m_run;
+            cl[wave * GP4 + i16] = l_run;
+        }
 #pragma unroll
-            for (int nb = 0; nb < NB; nb += 2) {
+        for (int r = 0; r < 4; ++r) {
+            const int g = 4 * grp + r;
+            if (g < G) {
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    acc[db] = PV2<DT>::mma(s[nb], s[nb + 1], tr_read(nb, db), tr_read(nb + 1, db), acc[db]);
-            }
-        } else {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) acc[db] = PV<DT>::mma(s[nb], tr_read(nb, db), acc[db]);
+                for (int db = 0; db < NDB; ++db) ca[(wave * G + g) * D + 16 * db + i16] = acc[db][r];
             }
         }
-    };
+        __syncthreads();
 
-    // Outer loop over chunks of IPV blocks (one page-id vector each); the
-    // pipelined inner loop itself issues no load but K/V.
-    for (int it0 = 0; it0 < nit; it0 += IPV) {
-        const int it1 = min(nit, it0 + IPV);
-        if (it0 > 0)
-            ids = load_ids(pg0, pg1, it0);
-        fetch_ids(it0, it0, it1);
-        issue(kbase, kr);
-        pin_loads();
-        issue(vbase, vr);
-        pin_loads();
-        for (int it = it0; it < it1; ++it) step(it, it0, it1);
-    }  // chunks of IPV blocks
-
-    if constexpr (!BAL) {
-        if (prm.status && violation != 0 && lane == 0)
-            __hip_atomic_fetch_or(prm.status, violation, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-
-    // Denominator of head i16 over the four lane groups.
-    l_run = rows4_sum(l_run);
-
-    // Result of (query head g of the group, partition p_rel): the partition
-    // state (o normalised, max, denominator) for the merge, or, when one
-    // partition covers the context, out and lse (an empty context gives
-    // out = 0, lse = -inf).
-    auto emit = [&](int g, int p_rel, int dd, float o, float M, float L, bool head_lane) {
-        const size_t h = size_t(b) * prm.num_q_heads + size_t(kvh) * Gact + g;
-        if (prm.split) {
-            const size_t row = h * prm.num_partitions + p_rel;
-            prm.ws_o[row * D + dd] = o;
-            if (head_lane) {
-                prm.ws_m[row] = M;
-                prm.ws_l[row] = L;
-            }
-        } else {
-            store_out<DT>(prm.out, h * D + dd, o);
-            if (head_lane && prm.lse) prm.lse[h] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
-        }
-    };
-
-    if (wpp == 1) {
-        // Every wave owns its partition: write straight from the output
-        // blocks (row 4*grp + r of block db is head 4*grp + r, column
-        // 16*db + i16); the max and denominator of head 4*grp + r sit in
-        // lane 4*grp + r.  No LDS, no barrier.
-        if (uint32_t(srow) < uint32_t(prm.num_partitions)) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int g = 4 * grp + r;
-                const float M = __shfl(m_run, g);
-                const float L = __shfl(l_run, g);
-                if (g < Gact) {
-                    const float inv = M == -INFINITY ? 0.f : 1.f / L;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-                        emit(g, srow, 16 * db + i16, acc[db][r] * inv, M, L, db == 0 && i16 == 0);
+        for (int sl = 0; sl < nslots; ++sl) {
+            const int p_rel = blockIdx.x * nslots + sl;
+            if (p_rel >= prm.num_partitions)
+                break;
+            for (int e = threadIdx.x; e < Gact * D; e += blockDim.x) {
+                const int g = e / D, dd = e % D;   // D is a power of two
+                float M = -INFINITY;
+                for (int w = sl * wpp; w < sl * wpp + wpp; ++w) M = fmaxf(M, cm[w * GP4 + g]);
+                float L = 0.f, o = 0.f;
+                if (M != -INFINITY) {
+                    for (int w = sl * wpp; w < sl * wpp + wpp; ++w) {
+                        const float sc = fast_exp2(cm[w * GP4 + g] - M);
+                        L += sc * cl[w * GP4 + g];
+                        o += sc * ca[(w * G + g) * D + dd];
+                    }
+                    o = o / L;
                 }
+                emit(g, p_rel, dd, o, M, L, dd == 0);
             }
         }
-        if constexpr (BAL)
-            continue;
         return;
-    }
-
-    // Several waves share each partition: combine them in LDS, maximum
-    // first, then the rescaled denominators and outputs.  A wave without
-    // blocks holds max = -inf, denominator 0 and contributes nothing; a slot
-    // whose partition is empty ends with max = -inf.
-    __syncthreads();
-    float* cm = smem;               // [nw][GP4]
-    float* cl = cm + nw * GP4;      // [nw][GP4]
-    float* ca = cl + nw * GP4;      // [nw][G][D]
-    if (grp == 0 && i16 < G) {
-        cm[wave * GP4 + i16] = m_run;
-        cl[wave * GP4 + i16] = l_run;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int g = 4 * grp + r;
-        if (g < G) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) ca[(wave * G + g) * D + 16 * db + i16] = acc[db][r];
-        }
-    }
-    __syncthreads();
-
-    for (int sl = 0; sl < nslots; ++sl) {
-        const int p_rel = blockIdx.x * nslots + sl;
-        if (p_rel >= prm.num_partitions)
-            break;
-        for (int e = threadIdx.x; e < Gact * D; e += blockDim.x) {
-            const int g = e / D, dd = e % D;   // D is a power of two
-            float M = -INFINITY;
-            for (int w = sl * wpp; w < sl * wpp + wpp; ++w) M = fmaxf(M, cm[w * GP4 + g]);
-            float L = 0.f, o = 0.f;
-            if (M != -INFINITY) {
-                for (int w = sl * wpp; w < sl * wpp + wpp; ++w) {
-                    const float sc = fast_exp2(cm[w * GP4 + g] - M);
-                    L += sc * cl[w * GP4 + g];
-                    o += sc * ca[(w * G + g) * D + dd];
-                }
-                o = o / L;
-            }
-            emit(g, p_rel, dd, o, M, L, dd == 0);
-        }
-    }
-    return;
     }  // segments
 
     if (prm.status && violation != 0 && lane == 0)
