@@ -10,7 +10,7 @@ sequence ends, and the merge combines each sequence's pieces.  Covered:
     mixing empty, one-token, page-multiple and long contexts, windows that
     cut pages;
   * NaN in every slot the method must not read;
-  * the CSR page table;
+  * the CSR page table and a token-major cache layout;
   * a workspace filled with garbage, then a second call with a smaller batch
     into the same workspace (state counts of the first call must not leak);
   * graph replays;
@@ -95,6 +95,18 @@ def test_balanced_csr(name):
     out, lse, plan = run_gpu_csr(p, csr, partition_size=BAL)
     assert plan["balanced_waves"] > 0
     compare(out, lse, ref_out, ref_lse, p.workload.dtype, "csr balanced %s" % name)
+
+
+def test_balanced_token_major_cache():
+    """[num_pages, page_size, Hkv, D] storage viewed as [num_pages, Hkv,
+    page_size, D]: only the strides differ."""
+    p = W.generate(W.CONFIGS["llama8b_b16_ragged_f16"])
+    k = p.k_cache.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    v = p.v_cache.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    ref_out, ref_lse = run_oracle(p)
+    out, lse, plan = run_gpu(dataclasses.replace(p, k_cache=k, v_cache=v), partition_size=BAL)
+    assert plan["balanced_waves"] > 0
+    compare(out, lse, ref_out, ref_lse, p.workload.dtype, "token-major balanced")
 
 
 def test_balanced_garbage_workspace_then_smaller_batch():
