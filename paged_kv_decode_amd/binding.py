@@ -385,6 +385,10 @@ class PagedDecode:
     def __call__(self, q, k_cache, v_cache, page_table, context_lens, scale,
                  max_context_len=None, sliding_window=0, partition_size=0, out=None,
                  lse=None):
+        """One decode step; returns (out, lse).  partition_size: 0 for the
+        planner's fixed partitions, a multiple of 16 to force their size, or
+        PA_DECODE_PARTITION_BALANCED for the length-balanced schedule (ragged
+        batches of up to 64 sequences)."""
         B, Hq, D = q.shape
         if out is None:
             out = torch.empty((B, Hq, D), dtype=self.dtype, device=q.device)
