@@ -288,18 +288,30 @@ __global__ __launch_bounds__(256) void merge_count_kernel(const MergeParams prm,
         const float wr = __int_as_float(__builtin_amdgcn_ds_bpermute(row * 4, __float_as_int(w)));
         a = row < cnt ? a + wr * orow[i] : a;
     }
-    // Rows from RS on (a wave-uniform loop, so that every lane takes part
-    // in the lane permutes).
-    for (int base = RS; base < cnt; base += NRG) {
-        const int row = base + rg;
-        const uint32_t rc = uint32_t(min(row, cnt - 1));
-        const f32x4 o = *reinterpret_cast<const f32x4*>(ob + (rc * D + cb) * 4u);
-        float wr = __int_as_float(__builtin_amdgcn_ds_bpermute((row & (kWave - 1)) * 4, __float_as_int(w)));
-        if (base + NRG > kWave) {
-            const float wm = weight(m[rc], l[rc]);
-            wr = row < kWave ? wr : wm;
+    // Rows from RS on, four per lane per pass with every load of a pass
+    // issued before the first use (a wave-uniform loop, so that every lane
+    // takes part in the lane permutes).
+    constexpr int UR = 4;
+    for (int base = RS; base < cnt; base += UR * NRG) {
+        f32x4 o[UR];
+        float mq[UR], lq[UR];
+        const bool far = base + UR * NRG > kWave;   // rows past 64: weights from memory
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const uint32_t rc = uint32_t(min(base + u * NRG + rg, cnt - 1));
+            o[u] = *reinterpret_cast<const f32x4*>(ob + (rc * D + cb) * 4u);
+            mq[u] = far ? m[rc] : 0.f;
+            lq[u] = far ? l[rc] : 0.f;
         }
-        a = row < cnt ? a + wr * o : a;
+        pin_loads();
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+            const int row = base + u * NRG + rg;
+            float wr = __int_as_float(
+                __builtin_amdgcn_ds_bpermute((row & (kWave - 1)) * 4, __float_as_int(w)));
+            wr = row < kWave ? wr : weight(mq[u], lq[u]);
+            a = row < cnt ? a + wr * o[u] : a;
+        }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
