@@ -7,7 +7,8 @@ D, partition sizes, batch and max_context_len against the description, the
 page-table row stride, a non-finite scale, and (CSR) nnz_pages.  Each
 rejected call returns PA_DECODE_INVALID_ARG, launches nothing (out keeps a
 sentinel) and leaves the handle usable: a valid call afterwards is right.
-A zero batch is a valid no-op.
+A zero batch is a valid no-op; the balanced schedule refuses more than 64
+sequences (PA_DECODE_UNSUPPORTED).
 """
 import pytest
 import torch
@@ -144,3 +145,32 @@ def test_csr_run_rejects_bad_arguments_and_launches_nothing():
     torch.cuda.synchronize()
     ref = run_oracle(p)
     compare(out.cpu(), lse.cpu(), ref[0], ref[1], p.workload.dtype, "csr after rejected calls")
+
+
+def test_balanced_schedule_above_64_sequences_is_unsupported():
+    """The length-balanced schedule takes at most 64 sequences: a call with
+    65 returns PA_DECODE_UNSUPPORTED and launches nothing; 64 runs."""
+    for batch, ok in ((65, False), (64, True)):
+        w = W.custom(batch=batch, num_q_heads=8, num_kv_heads=2, head_dim=64, dtype=torch.float16,
+                     context_lens=[1 + 37 * i for i in range(batch)], seed=batch)
+        p = W.generate(w)
+        d = to_device(p)
+        eng = engine(p)
+        out = torch.full_like(d.q, SENTINEL)
+        lse = torch.full(d.q.shape[:2], SENTINEL, dtype=torch.float32, device="cuda")
+        if not ok:
+            with pytest.raises(B.PaDecodeError) as e:
+                eng.make_args(d.q, d.k_cache, d.v_cache, d.page_table, d.context_lens, p.scale,
+                              out, lse, max_context_len=p.max_context_len,
+                              partition_size=B.PA_DECODE_PARTITION_BALANCED)
+            assert e.value.status == B.PA_DECODE_UNSUPPORTED
+            torch.cuda.synchronize()
+            assert torch.all(out == SENTINEL)
+            continue
+        args = eng.make_args(d.q, d.k_cache, d.v_cache, d.page_table, d.context_lens, p.scale,
+                             out, lse, max_context_len=p.max_context_len,
+                             partition_size=B.PA_DECODE_PARTITION_BALANCED)
+        eng.run_args(args)
+        torch.cuda.synchronize()
+        ref = run_oracle(p)
+        compare(out.cpu(), lse.cpu(), ref[0], ref[1], torch.float16, "balanced batch 64")
