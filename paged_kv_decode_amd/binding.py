@@ -286,6 +286,91 @@ def make_desc(num_q_heads, num_kv_heads, head_dim, dtype, max_batch, max_context
                         max_context_len, device, mode, theta, rscale, int(debug_checks))
 
 
+
+def _storage_elems(t: torch.Tensor) -> int:
+    """Elements of t's storage from t's first element on."""
+    return t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+
+
+def _check_step_shapes(desc: PaDecodeDesc, dtype, q, k_cache, v_cache, out, lse):
+    """Shapes the C ABI cannot see (it takes raw pointers): q and out
+    [B, Hq, D], caches [num_pages, Hkv, page_size, D] with D contiguous, lse
+    [B, Hq].  Raises TypeError / ValueError before anything launches."""
+    Hq, Hkv, D, ps = desc.num_q_heads, desc.num_kv_heads, desc.head_dim, desc.page_size
+    if q.dtype != dtype or k_cache.dtype != dtype or v_cache.dtype != dtype or \
+            out.dtype != dtype:
+        raise TypeError("q, k/v caches and out must be %s" % dtype)
+    if q.dim() != 3 or q.shape[1] != Hq or q.shape[2] != D:
+        raise ValueError("q must be [B, %d, %d], got %s" % (Hq, D, tuple(q.shape)))
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape %s, got %s" % (tuple(q.shape), tuple(out.shape)))
+    if not q.is_contiguous() or not out.is_contiguous():
+        raise ValueError("q and out must be contiguous")
+    if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (Hkv, ps, D) or k_cache.stride(3) != 1:
+        raise ValueError("caches must be [num_pages, %d, %d, %d] with D contiguous, got %s"
+                         % (Hkv, ps, D, tuple(k_cache.shape)))
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if k_cache.shape[0] < 1:
+        raise ValueError("the caches hold no page")
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise TypeError("lse must be contiguous float32")
+        if tuple(lse.shape) != tuple(q.shape[:2]):
+            raise ValueError("lse must be [B, Hq] = %s, got %s" % (tuple(q.shape[:2]),
+                                                                  tuple(lse.shape)))
+
+
+def check_dense_shapes(desc: PaDecodeDesc, dtype, q, k_cache, v_cache, page_table, context_lens,
+                       out, lse, max_context_len: int) -> None:
+    """Every shape of a pa_decode_run call checked against the descriptor and
+    the batch (B = q.shape[0]): page_table int32 [>= B, >= ceil(max_context_len
+    / page_size)] with unit inner stride, and storage behind each of its first
+    B rows for a whole row stride (the kernel may read a row's entries up to
+    the stride); context_lens int32 with >= B entries."""
+    _check_step_shapes(desc, dtype, q, k_cache, v_cache, out, lse)
+    B = q.shape[0]
+    if page_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("page_table and context_lens must be int32")
+    if page_table.dim() != 2 or page_table.stride(1) != 1:
+        raise ValueError("page_table must be [B, pt_stride] with unit inner stride")
+    if not context_lens.is_contiguous() or context_lens.dim() != 1:
+        raise ValueError("context_lens must be a contiguous 1-D tensor")
+    if B == 0:
+        return
+    ps = desc.page_size
+    if page_table.shape[0] < B:
+        raise ValueError("page_table has %d rows for a batch of %d" % (page_table.shape[0], B))
+    if page_table.shape[1] * ps < max_context_len:
+        raise ValueError("page_table rows of %d pages cannot hold %d tokens"
+                         % (page_table.shape[1], max_context_len))
+    if page_table.stride(0) < page_table.shape[1] or \
+            _storage_elems(page_table) < B * page_table.stride(0):
+        raise ValueError("page_table storage must hold %d rows of stride %d"
+                         % (B, page_table.stride(0)))
+    if context_lens.numel() < B:
+        raise ValueError("context_lens has %d entries for a batch of %d"
+                         % (context_lens.numel(), B))
+
+
+def check_csr_shapes(desc: PaDecodeDesc, dtype, q, k_cache, v_cache, page_indptr, page_indices,
+                     last_page_len, nnz_pages: int, out, lse) -> None:
+    """Every shape of a pa_decode_run_csr call: page_indptr >= B + 1 entries,
+    last_page_len >= B, page_indices >= nnz_pages (all contiguous int32)."""
+    _check_step_shapes(desc, dtype, q, k_cache, v_cache, out, lse)
+    B = q.shape[0]
+    for name, t in (("page_indptr", page_indptr), ("page_indices", page_indices),
+                    ("last_page_len", last_page_len)):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.dim() != 1:
+            raise TypeError("%s must be a contiguous 1-D int32 tensor" % name)
+    if nnz_pages < 0 or page_indices.numel() < nnz_pages:
+        raise ValueError("page_indices has %d entries for nnz_pages %d"
+                         % (page_indices.numel(), nnz_pages))
+    if B > 0 and (page_indptr.numel() < B + 1 or last_page_len.numel() < B):
+        raise ValueError("page_indptr needs %d entries and last_page_len %d (batch %d)"
+                         % (B + 1, B, B))
+
+
 class PagedDecode:
     """Handle-owning front end for torch tensors on one GPU.
 
@@ -330,27 +415,14 @@ class PagedDecode:
                   workspace=None) -> PaDecodeArgs:
         for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                         ("page_table", page_table), ("context_lens", context_lens),
-                        ("out", out)):
+                        ("out", out)) + ((("lse", lse),) if lse is not None else ()):
             if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
                 raise TypeError("%s must be a device tensor" % name)
-        if q.dtype != self.dtype or k_cache.dtype != self.dtype or \
-                v_cache.dtype != self.dtype or out.dtype != self.dtype:
-            raise TypeError("q, k/v caches and out must be %s" % self.dtype)
-        if not q.is_contiguous() or not out.is_contiguous():
-            raise ValueError("q and out must be contiguous")
-        if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
-            raise ValueError("k_cache and v_cache must share shape and strides")
-        if k_cache.dim() != 4 or k_cache.stride(3) != 1:
-            raise ValueError("caches must be [num_pages, Hkv, page_size, D] with D contiguous")
-        if page_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
-            raise TypeError("page_table and context_lens must be int32")
-        if page_table.dim() != 2 or page_table.stride(1) != 1:
-            raise ValueError("page_table must be [B, pt_stride] with unit inner stride")
-        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-            raise TypeError("lse must be contiguous float32")
-        B = q.shape[0]
+        B = q.shape[0] if q.dim() > 0 else 0
         if max_context_len is None:
-            max_context_len = int(context_lens.max().item()) if B else 0
+            max_context_len = int(context_lens[:B].max().item()) if B else 0
+        check_dense_shapes(self.desc, self.dtype, q, k_cache, v_cache, page_table, context_lens,
+                           out, lse, max_context_len)
         ws_bytes = self.workspace_size(B, max_context_len, sliding_window, partition_size)
         if workspace is None:
             workspace = self.workspace(ws_bytes)
@@ -406,24 +478,12 @@ class PagedDecode:
         page_indptr[-1]."""
         for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                         ("page_indptr", page_indptr), ("page_indices", page_indices),
-                        ("last_page_len", last_page_len), ("out", out)):
+                        ("last_page_len", last_page_len), ("out", out)) + \
+                ((("lse", lse),) if lse is not None else ()):
             if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
                 raise TypeError("%s must be a device tensor" % name)
-        if q.dtype != self.dtype or k_cache.dtype != self.dtype or \
-                v_cache.dtype != self.dtype or out.dtype != self.dtype:
-            raise TypeError("q, k/v caches and out must be %s" % self.dtype)
-        if not q.is_contiguous() or not out.is_contiguous():
-            raise ValueError("q and out must be contiguous")
-        if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
-            raise ValueError("k_cache and v_cache must share shape and strides")
-        if k_cache.dim() != 4 or k_cache.stride(3) != 1:
-            raise ValueError("caches must be [num_pages, Hkv, page_size, D] with D contiguous")
-        for name, t in (("page_indptr", page_indptr), ("page_indices", page_indices),
-                        ("last_page_len", last_page_len)):
-            if t.dtype != torch.int32 or not t.is_contiguous():
-                raise TypeError("%s must be contiguous int32" % name)
-        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-            raise TypeError("lse must be contiguous float32")
+        check_csr_shapes(self.desc, self.dtype, q, k_cache, v_cache, page_indptr, page_indices,
+                         last_page_len, int(nnz_pages), out, lse)
         B = q.shape[0]
         ws_bytes = pa_decode_workspace_size_csr(self.handle, B, nnz_pages, max_context_len,
                                                 sliding_window, partition_size)
