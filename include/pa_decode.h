@@ -123,8 +123,10 @@ typedef struct pa_decode_desc {
 
 /* Per-call arguments.  Element strides are in elements of the cache dtype.
  * q, k_cache, v_cache, out and (when the plan splits) workspace must be
- * 16-byte aligned, each stride times the element size a multiple of 16
- * bytes, and kv_stride_slot >= D; otherwise pa_decode_run returns
+ * 16-byte aligned, each stride times the element size a non-negative
+ * multiple of 16 bytes, kv_stride_slot >= D, kv_stride_slot times the
+ * element size below 2^27 bytes and num_pages * kv_stride_page times the
+ * element size at most 2^50 bytes; otherwise pa_decode_run returns
  * PA_DECODE_INVALID_ARG (PA_DECODE_WORKSPACE_TOO_SMALL for a short
  * workspace) and launches nothing. */
 typedef struct pa_decode_args {
@@ -194,7 +196,12 @@ typedef struct pa_decode_handle_s* pa_decode_handle;
 
 /* Validate desc, read the device's properties and return a handle (with
  * desc.debug_checks = 1 it also allocates and zeroes the 4-byte status word
- * on desc.device).
+ * on desc.device).  The handle keeps what the host-side dispatch needs: the
+ * compute-unit count and the partial kernel's occupancy, from which the
+ * partition count is chosen per call (TVM PR #20426, section "Change": the
+ * host picks the kernel and its split before the launch; section "Open for
+ * reviewers": the split depends on the device), and the tuning overrides of
+ * pa_decode_plan_query, read from the environment once, here.
  * Errors: INVALID_ARG (null pointer, non-positive sizes, Hq % Hkv != 0,
  * rotary_mode not 0 or 1, rope_theta or rope_scale not finite and > 0 with
  * rotary_mode 1), UNSUPPORTED (shape or dtype not built), HIP_ERROR (no such
@@ -205,7 +212,14 @@ int pa_decode_create(const pa_decode_desc* desc, pa_decode_handle* handle);
 int pa_decode_destroy(pa_decode_handle handle);
 
 /* Bytes of device workspace pa_decode_run needs for these sizes
- * (partition_size 0 = the planner's choice).  Pure host computation. */
+ * (partition_size 0 = the planner's choice).  Pure host computation.  The
+ * workspace holds the partition states the merge reads: per (sequence, query
+ * head, partition) the normalised partial output, its maximum and its
+ * denominator (the paged_attention_v2 commit page, "Phase 1: Per-partition
+ * attention", stores the same three per partition), float32, laid out
+ * o[B][Hq][P][D], m[B][Hq][P], l[B][Hq][P] (each region 256-byte aligned),
+ * plus int32 state counts [B][Hq] under the length-balanced schedule.  0
+ * when one partition covers every context (no merge). */
 int pa_decode_workspace_size(pa_decode_handle handle, int32_t batch, int32_t max_context_len,
                              int32_t sliding_window, int32_t partition_size, size_t* bytes);
 
@@ -228,18 +242,26 @@ int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* str
  * it reads the word: a debugging aid, not for a timed loop. */
 int pa_decode_debug_status(pa_decode_handle handle, int32_t* status);
 
-/* The plan of the last successful pa_decode_run on this handle. */
+/* The plan of the last successful pa_decode_run / pa_decode_run_csr on this
+ * handle: the dispatch decision TVM PR #20426, section "Change", makes on the
+ * host (single pass or split, and how), as it was taken.  INVALID_ARG before
+ * the first run. */
 int pa_decode_last_plan(pa_decode_handle handle, pa_decode_plan* plan);
 
 /* Plan without a handle or device (pure host): the same planner that
  * pa_decode_run uses, for a given compute-unit count and number of
  * partial-kernel waves a compute unit holds at once (pa_decode_run uses the
  * device's values; the plan of a run reports them).
- * Tuning hooks (every planner call reads them): the environment variables
- * PA_DECODE_WAVES_PER_PARTITION and PA_DECODE_WAVES_PER_GROUP, when set to
- * 1, 2 or 4, override the plan's waves_per_partition / waves_per_group (other
- * values are ignored).  They change the work split only, never the result's
- * definition or the workspace size. */
+ * The split follows TVM PR #20426, section "Change" (a host-side choice
+ * before the launch) and the commit page's split-context "Phase 1".
+ * Tuning hooks for experiments: the environment variables
+ * PA_DECODE_WAVES_PER_PARTITION and PA_DECODE_WAVES_PER_GROUP (1, 2 or 4)
+ * override the plan's waves_per_partition / waves_per_group,
+ * PA_DECODE_BALANCED_START (0 .. 64) the balanced schedule's start charge in
+ * pages and PA_DECODE_BALANCED_WAVES_PER_CU (1 .. 16) its waves per compute
+ * unit; other values are ignored.  This function reads them at each call, a
+ * handle once at pa_decode_create.  They change the work split only, never
+ * the result's definition or the workspace size. */
 int pa_decode_plan_query(const pa_decode_desc* desc, int32_t num_cus, int32_t waves_per_cu,
                          int32_t batch, int32_t max_context_len, int32_t sliding_window,
                          int32_t partition_size, pa_decode_plan* plan);
@@ -278,7 +300,12 @@ typedef struct pa_decode_csr_args {
     int32_t sliding_window;       /* <= 0: no window; else keys [n_b - W, n_b) */
     int32_t partition_size;       /* 0: the host switch above -- one partition per    */
                                   /*   (sequence, KV head) when nnz_pages <=          */
-                                  /*   B * 256 / page_size, else the planner's split; */
+                                  /*   B * 256 / page_size; else, for 2 .. 64         */
+                                  /*   sequences with 4 * nnz_pages < 3 * B *         */
+                                  /*   ceil(max_context_len / page_size) (a ragged    */
+                                  /*   batch: mean below 3/4 of the longest), the     */
+                                  /*   length-balanced schedule; else the planner's   */
+                                  /*   fixed split;                                   */
                                   /*   > 0: tokens per partition, as in pa_decode_args; */
                                   /*   PA_DECODE_PARTITION_BALANCED as there          */
     void* out;                    /* device, [batch, Hq, D] contiguous, desc.dtype */

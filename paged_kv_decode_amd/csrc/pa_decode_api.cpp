@@ -18,6 +18,7 @@
 #include "kernels.h"
 #include "pa_decode.h"
 #include "planner.h"
+#include "validate.h"
 
 // Start/stop event pairs for kernel timing (see pa_decode_profile_begin).
 struct EventRing {
@@ -43,10 +44,52 @@ struct EventRing {
     }
 };
 
+// The plans of the last few call shapes (a decode loop repeats one shape, or
+// a few), so that a run with a shape seen before does not plan again.
+struct PlanCache {
+    struct Entry {
+        bool valid = false;
+        bool csr = false;
+        int32_t batch = 0, max_context_len = 0, sliding_window = 0, partition_size = 0,
+                nnz_pages = 0;
+        pa_decode_plan plan = {};
+        int32_t max_ctx_used = 0;
+    };
+    static constexpr int kEntries = 4;
+    Entry e[kEntries];
+    int next = 0;
+    const Entry* find(bool csr, int32_t batch, int32_t max_ctx, int32_t window, int32_t S,
+                      int32_t nnz) const
+    {
+        for (const Entry& x : e)
+            if (x.valid && x.csr == csr && x.batch == batch && x.max_context_len == max_ctx &&
+                x.sliding_window == window && x.partition_size == S && x.nnz_pages == nnz)
+                return &x;
+        return nullptr;
+    }
+    void put(bool csr, int32_t batch, int32_t max_ctx, int32_t window, int32_t S, int32_t nnz,
+             const pa_decode_plan& plan, int32_t max_ctx_used)
+    {
+        Entry& x = e[next];
+        next = (next + 1) % kEntries;
+        x.valid = true;
+        x.csr = csr;
+        x.batch = batch;
+        x.max_context_len = max_ctx;
+        x.sliding_window = window;
+        x.partition_size = S;
+        x.nnz_pages = nnz;
+        x.plan = plan;
+        x.max_ctx_used = max_ctx_used;
+    }
+};
+
 struct pa_decode_handle_s {
     pa_decode_desc desc;
     int num_cus;
     int waves_per_cu;  // partial-kernel waves one compute unit holds at once
+    pa::PlanTuning tune;  // read from the environment once, at create
+    PlanCache plans;
     pa_decode_plan last_plan;
     bool has_plan;
     int last_hip_error;
@@ -56,100 +99,6 @@ struct pa_decode_handle_s {
 };
 
 namespace {
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-// The arguments both page-table forms share.
-struct StepArgs {
-    const void* q;
-    const void* k_cache;
-    const void* v_cache;
-    int64_t kv_stride_page, kv_stride_head, kv_stride_slot;
-    int32_t num_pages;
-    int32_t batch;
-    int32_t max_context_len;
-    float scale;
-    int32_t sliding_window;
-    int32_t partition_size;
-    void* out;
-    float* lse;
-    void* workspace;
-    size_t workspace_bytes;
-};
-
-template <typename A>
-StepArgs common_args(const A& a)
-{
-    StepArgs c;
-    c.q = a.q;
-    c.k_cache = a.k_cache;
-    c.v_cache = a.v_cache;
-    c.kv_stride_page = a.kv_stride_page;
-    c.kv_stride_head = a.kv_stride_head;
-    c.kv_stride_slot = a.kv_stride_slot;
-    c.num_pages = a.num_pages;
-    c.batch = a.batch;
-    c.max_context_len = a.max_context_len;
-    c.scale = a.scale;
-    c.sliding_window = a.sliding_window;
-    c.partition_size = a.partition_size;
-    c.out = a.out;
-    c.lse = a.lse;
-    c.workspace = a.workspace;
-    c.workspace_bytes = a.workspace_bytes;
-    return c;
-}
-
-int check_common(const pa_decode_desc& d, const StepArgs& a)
-{
-    if (a.batch < 0 || a.batch > d.max_batch || a.max_context_len < 0 ||
-        a.max_context_len > d.max_context_len ||
-        (a.partition_size < 0 && a.partition_size != PA_DECODE_PARTITION_BALANCED))
-        return PA_DECODE_INVALID_ARG;
-    if (a.partition_size > 0 && a.partition_size % d.page_size != 0)
-        return PA_DECODE_INVALID_ARG;
-    if (!std::isfinite(a.scale))
-        return PA_DECODE_INVALID_ARG;
-    if (a.batch == 0)
-        return PA_DECODE_OK;
-    if (!a.q || !a.k_cache || !a.v_cache || !a.out || a.num_pages <= 0)
-        return PA_DECODE_INVALID_ARG;
-    const int eb = pa::dtype_bytes(d.dtype);
-    // Strides: non-negative, 16-byte granular (each lane reads 16-byte chunks).
-    const int64_t strides[3] = {a.kv_stride_page, a.kv_stride_head, a.kv_stride_slot};
-    for (int64_t s : strides)
-        if (s < 0 || (s * eb) % 16 != 0)
-            return PA_DECODE_INVALID_ARG;
-    if (a.kv_stride_slot < d.head_dim)
-        return PA_DECODE_INVALID_ARG;
-    if (!aligned16(a.q) || !aligned16(a.k_cache) || !aligned16(a.v_cache) || !aligned16(a.out))
-        return PA_DECODE_INVALID_ARG;
-    return PA_DECODE_OK;
-}
-
-int check_args(const pa_decode_desc& d, const pa_decode_args& a)
-{
-    int st = check_common(d, common_args(a));
-    if (st != PA_DECODE_OK || a.batch == 0)
-        return st;
-    if (!a.page_table || !a.context_lens || a.pt_stride <= 0)
-        return PA_DECODE_INVALID_ARG;
-    if (int64_t(a.pt_stride) * d.page_size < int64_t(a.max_context_len))
-        return PA_DECODE_INVALID_ARG;
-    return PA_DECODE_OK;
-}
-
-int check_csr_args(const pa_decode_desc& d, const pa_decode_csr_args& a)
-{
-    if (a.nnz_pages < 0 || (a.batch == 0 && a.nnz_pages != 0))
-        return PA_DECODE_INVALID_ARG;
-    int st = check_common(d, common_args(a));
-    if (st != PA_DECODE_OK || a.batch == 0)
-        return st;
-    if (!a.page_indptr || !a.last_page_len || (a.nnz_pages > 0 && !a.page_indices))
-        return PA_DECODE_INVALID_ARG;
-    return PA_DECODE_OK;
-}
 
 // Where the kernels find page ids and context lengths.
 struct PageSource {
@@ -162,13 +111,13 @@ struct PageSource {
 };
 
 // Launches one planned decode step on `stream` (arguments already checked).
-int launch_step(pa_decode_handle handle, const StepArgs& a, const PageSource& src,
+int launch_step(pa_decode_handle handle, const pa::StepArgs& a, const PageSource& src,
                 const pa_decode_plan& plan, void* stream)
 {
     const pa_decode_desc& d = handle->desc;
     if (plan.split && (!a.workspace || a.workspace_bytes < size_t(plan.workspace_bytes)))
         return PA_DECODE_WORKSPACE_TOO_SMALL;
-    if (plan.split && !aligned16(a.workspace))
+    if (plan.split && !pa::aligned16(a.workspace))
         return PA_DECODE_INVALID_ARG;
     handle->last_plan = plan;
     handle->has_plan = true;
@@ -218,7 +167,7 @@ int launch_step(pa_decode_handle handle, const StepArgs& a, const PageSource& sr
     pp.minus_one = -1.0f;
     pp.batch = a.batch;
     pp.bal_waves = plan.balanced_waves;
-    pp.bal_start = balanced ? pa::balanced_start_pages(d) : 0;
+    pp.bal_start = balanced ? pa::balanced_start_pages(d, handle->tune) : 0;
     pp.ws_cnt = balanced ? reinterpret_cast<int32_t*>(ws + wl.c_off) : nullptr;
 
     const dim3 grid(plan.grid_partial[0], plan.grid_partial[1], plan.grid_partial[2]);
@@ -258,6 +207,39 @@ int launch_step(pa_decode_handle handle, const StepArgs& a, const PageSource& sr
     return PA_DECODE_OK;
 }
 
+// The plan of a dense-table call (cached per call shape).
+int plan_dense(pa_decode_handle h, int32_t batch, int32_t max_ctx, int32_t window, int32_t S,
+               pa_decode_plan* plan)
+{
+    if (const PlanCache::Entry* x = h->plans.find(false, batch, max_ctx, window, S, 0)) {
+        *plan = x->plan;
+        return PA_DECODE_OK;
+    }
+    const int st = pa::make_plan(h->desc, h->num_cus, h->waves_per_cu, h->tune, batch, max_ctx,
+                                 window, S, plan);
+    if (st == PA_DECODE_OK)
+        h->plans.put(false, batch, max_ctx, window, S, 0, *plan, max_ctx);
+    return st;
+}
+
+// The plan of a CSR call and the context bound it used (cached per call shape).
+int plan_csr(pa_decode_handle h, int32_t batch, int32_t nnz, int32_t max_ctx, int32_t window,
+             int32_t S, pa_decode_plan* plan, int* max_ctx_used)
+{
+    if (const PlanCache::Entry* x = h->plans.find(true, batch, max_ctx, window, S, nnz)) {
+        *plan = x->plan;
+        if (max_ctx_used) *max_ctx_used = x->max_ctx_used;
+        return PA_DECODE_OK;
+    }
+    int used = 0;
+    const int st = pa::make_plan_csr(h->desc, h->num_cus, h->waves_per_cu, h->tune, batch, nnz,
+                                     max_ctx, window, S, plan, &used);
+    if (st == PA_DECODE_OK)
+        h->plans.put(true, batch, max_ctx, window, S, nnz, *plan, used);
+    if (max_ctx_used) *max_ctx_used = used;
+    return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -283,6 +265,7 @@ int pa_decode_create(const pa_decode_desc* desc, pa_decode_handle* handle)
         return PA_DECODE_HIP_ERROR;
     h->desc = *desc;
     h->num_cus = cus;
+    h->tune = pa::tuning_from_env();
     {
         // Occupancy of the partial kernel this description uses, for the
         // largest workgroup the planner gives it.
@@ -390,9 +373,7 @@ int pa_decode_workspace_size(pa_decode_handle handle, int32_t batch, int32_t max
     if (!handle || !bytes)
         return PA_DECODE_INVALID_ARG;
     pa_decode_plan plan;
-    int st = pa::make_plan(handle->desc, handle->num_cus, handle->waves_per_cu, batch,
-                           max_context_len, sliding_window,
-                           partition_size, &plan);
+    int st = plan_dense(handle, batch, max_context_len, sliding_window, partition_size, &plan);
     if (st != PA_DECODE_OK)
         return st;
     *bytes = size_t(plan.workspace_bytes);
@@ -405,8 +386,8 @@ int pa_decode_plan_query(const pa_decode_desc* desc, int32_t num_cus, int32_t wa
 {
     if (!desc || !plan)
         return PA_DECODE_INVALID_ARG;
-    return pa::make_plan(*desc, num_cus, waves_per_cu, batch, max_context_len, sliding_window,
-                         partition_size, plan);
+    return pa::make_plan(*desc, num_cus, waves_per_cu, pa::tuning_from_env(), batch,
+                         max_context_len, sliding_window, partition_size, plan);
 }
 
 int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* stream)
@@ -415,16 +396,15 @@ int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* str
         return PA_DECODE_INVALID_ARG;
     const pa_decode_desc& d = handle->desc;
     const pa_decode_args& a = *args;
-    int st = check_args(d, a);
+    int st = pa::check_args(d, a);
     if (st != PA_DECODE_OK)
         return st;
     pa_decode_plan plan;
-    st = pa::make_plan(d, handle->num_cus, handle->waves_per_cu, a.batch, a.max_context_len,
-                       a.sliding_window, a.partition_size, &plan);
+    st = plan_dense(handle, a.batch, a.max_context_len, a.sliding_window, a.partition_size, &plan);
     if (st != PA_DECODE_OK)
         return st;
     PageSource src = {a.page_table, a.pt_stride, a.context_lens, nullptr, nullptr, 0};
-    return launch_step(handle, common_args(a), src, plan, stream);
+    return launch_step(handle, pa::common_args(a), src, plan, stream);
 }
 
 int pa_decode_workspace_size_csr(pa_decode_handle handle, int32_t batch, int32_t nnz_pages,
@@ -434,9 +414,8 @@ int pa_decode_workspace_size_csr(pa_decode_handle handle, int32_t batch, int32_t
     if (!handle || !bytes)
         return PA_DECODE_INVALID_ARG;
     pa_decode_plan plan;
-    int st = pa::make_plan_csr(handle->desc, handle->num_cus, handle->waves_per_cu, batch,
-                               nnz_pages, max_context_len, sliding_window, partition_size, &plan,
-                               nullptr);
+    int st = plan_csr(handle, batch, nnz_pages, max_context_len, sliding_window, partition_size,
+                      &plan, nullptr);
     if (st != PA_DECODE_OK)
         return st;
     *bytes = size_t(plan.workspace_bytes);
@@ -450,8 +429,9 @@ int pa_decode_plan_query_csr(const pa_decode_desc* desc, int32_t num_cus, int32_
 {
     if (!desc || !plan)
         return PA_DECODE_INVALID_ARG;
-    return pa::make_plan_csr(*desc, num_cus, waves_per_cu, batch, nnz_pages, max_context_len,
-                             sliding_window, partition_size, plan, nullptr);
+    return pa::make_plan_csr(*desc, num_cus, waves_per_cu, pa::tuning_from_env(), batch,
+                             nnz_pages, max_context_len, sliding_window, partition_size, plan,
+                             nullptr);
 }
 
 int pa_decode_run_csr(pa_decode_handle handle, const pa_decode_csr_args* args, void* stream)
@@ -460,16 +440,16 @@ int pa_decode_run_csr(pa_decode_handle handle, const pa_decode_csr_args* args, v
         return PA_DECODE_INVALID_ARG;
     const pa_decode_desc& d = handle->desc;
     const pa_decode_csr_args& a = *args;
-    int st = check_csr_args(d, a);
+    int st = pa::check_csr_args(d, a);
     if (st != PA_DECODE_OK)
         return st;
     pa_decode_plan plan;
     int max_ctx = 0;
-    st = pa::make_plan_csr(d, handle->num_cus, handle->waves_per_cu, a.batch, a.nnz_pages,
-                           a.max_context_len, a.sliding_window, a.partition_size, &plan, &max_ctx);
+    st = plan_csr(handle, a.batch, a.nnz_pages, a.max_context_len, a.sliding_window,
+                  a.partition_size, &plan, &max_ctx);
     if (st != PA_DECODE_OK)
         return st;
-    StepArgs c = common_args(a);
+    pa::StepArgs c = pa::common_args(a);
     c.max_context_len = max_ctx;
     PageSource src = {a.page_indices, 0, nullptr, a.page_indptr, a.last_page_len, a.nnz_pages};
     return launch_step(handle, c, src, plan, stream);
@@ -482,7 +462,7 @@ int pa_decode_read_probe(const void* base, const uint64_t* chunk_addrs, int32_t 
         return PA_DECODE_INVALID_ARG;
     if (chunk_bytes != 2048 && chunk_bytes != 3072 && chunk_bytes != 4096 && chunk_bytes != 8192)
         return PA_DECODE_INVALID_ARG;
-    if (base && !aligned16(base))
+    if (base && !pa::aligned16(base))
         return PA_DECODE_INVALID_ARG;
     const hipError_t e = pa::launch_read_probe(base, chunk_addrs, num_chunks, chunk_bytes / 1024,
                                                sink, static_cast<hipStream_t>(stream));

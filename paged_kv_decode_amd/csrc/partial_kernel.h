@@ -1191,7 +1191,7 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
             if (p_rel >= prm.num_partitions)
                 break;
             for (int e = threadIdx.x; e < Gact * D; e += blockDim.x) {
-                const int g = e / D, dd = e % D;   // D is a power of two
+                const int g = e / D, dd = e % D;   // D a compile-time constant (96 too)
                 float M = -INFINITY;
                 for (int w = sl * wpp; w < sl * wpp + wpp; ++w) M = fmaxf(M, cm[w * GP4 + g]);
                 float L = 0.f, o = 0.f;

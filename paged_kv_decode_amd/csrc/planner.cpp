@@ -114,13 +114,16 @@ WorkspaceLayout workspace_layout(const pa_decode_desc& d, int batch, int num_par
 
 // Merge grid and block of a split plan with P state rows per (sequence,
 // head); `counts` (balanced schedule): the per-wave merge whatever P.
-static void set_merge_grid(const pa_decode_desc& d, int batch, int64_t P, pa_decode_plan* p,
-                           bool counts = false)
+// UNSUPPORTED when the wave count does not fit the kernels' 32-bit unit index.
+static int set_merge_grid(const pa_decode_desc& d, int batch, int64_t P, pa_decode_plan* p,
+                          bool counts = false)
 {
     if (P <= kMergeWaveMaxPartitions || counts) {
         // one wave per (sequence, query head, 64-dim slice), four per workgroup
         const int cw = merge_slice_width(batch, d.num_q_heads, d.head_dim);
         const int64_t units = int64_t(batch) * d.num_q_heads * ((d.head_dim + cw - 1) / cw);
+        if (units > INT32_MAX - 3)
+            return PA_DECODE_UNSUPPORTED;
         p->grid_merge[0] = int32_t((units + 3) / 4);
         p->grid_merge[1] = 1;
         p->grid_merge[2] = 1;
@@ -130,17 +133,36 @@ static void set_merge_grid(const pa_decode_desc& d, int batch, int64_t P, pa_dec
         p->grid_merge[2] = d.head_dim / 16;   // 16-column slices
     }
     p->block_merge = kMergeThreads;
+    return PA_DECODE_OK;
 }
 
-int balanced_start_pages(const pa_decode_desc& d)
+PlanTuning tuning_from_env()
+{
+    PlanTuning t;
+    auto read = [](const char* name, int* dst, int lo, int hi) {
+        if (const char* env = std::getenv(name)) {
+            char* end = nullptr;
+            const long v = std::strtol(env, &end, 10);
+            if (end != env && v >= lo && v <= hi) *dst = int(v);
+        }
+    };
+    read("PA_DECODE_WAVES_PER_PARTITION", &t.waves_per_partition, 1, 4);
+    read("PA_DECODE_WAVES_PER_GROUP", &t.waves_per_group, 1, 4);
+    read("PA_DECODE_BALANCED_START", &t.balanced_start, 0, 64);
+    read("PA_DECODE_BALANCED_WAVES_PER_CU", &t.balanced_waves_per_cu, 1, 16);
+    if (t.waves_per_partition == 3) t.waves_per_partition = 0;
+    if (t.waves_per_group == 3) t.waves_per_group = 0;
+    return t;
+}
+
+int balanced_start_pages(const pa_decode_desc& d, const PlanTuning& tune)
 {
     // Four blocks' worth, three with rotary: measured on MI355X over 2 .. 32
     // pages for batches of 16 with lengths up to 4096 at two pages per
     // block, the best charges were 8 (head_dim 128), 8 - 10 (head_dim 96)
     // and 6 - 7 (head_dim 128 with rotary, whose blocks take longer).
     int c = (d.rotary_mode == 1 ? 3 : 4) * pages_per_block(d.head_dim, d.dtype);
-    // Experiments only: PA_DECODE_BALANCED_START overrides the charge.
-    if (const char* env = std::getenv("PA_DECODE_BALANCED_START")) c = std::atoi(env);
+    if (tune.balanced_start >= 0) c = tune.balanced_start;
     return std::max(0, std::min(64, c));
 }
 
@@ -149,8 +171,9 @@ int balanced_start_pages(const pa_decode_desc& d)
 // multiple of the workgroup size), which split the batch's visible pages
 // evenly in the kernel.  A (sequence, head) then has at most min(W, its
 // visible pages) states.
-static int make_balanced_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
-                              int64_t vis_pages, pa_decode_plan* plan)
+static int make_balanced_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu,
+                              const PlanTuning& tune, int batch, int64_t vis_pages,
+                              pa_decode_plan* plan)
 {
     if (batch > kBalancedMaxBatch)
         return PA_DECODE_UNSUPPORTED;
@@ -158,10 +181,7 @@ static int make_balanced_plan(const pa_decode_desc& d, int num_cus, int waves_pe
         return PA_DECODE_UNSUPPORTED;
     const int nw = workgroup_waves(d);
     const int64_t capacity = int64_t(num_cus) * waves_per_cu;
-    int per_cu = 4;
-    // Experiments only: PA_DECODE_BALANCED_WAVES_PER_CU overrides the target.
-    if (const char* env = std::getenv("PA_DECODE_BALANCED_WAVES_PER_CU"))
-        per_cu = std::max(1, std::min(16, std::atoi(env)));
+    const int per_cu = tune.balanced_waves_per_cu > 0 ? tune.balanced_waves_per_cu : 4;
     const int64_t target = std::min<int64_t>(capacity, int64_t(num_cus) * per_cu);
     // Waves per KV head: the target shared by the heads, no more than the
     // batch's pages, a whole number of workgroups.
@@ -182,7 +202,8 @@ static int make_balanced_plan(const pa_decode_desc& d, int num_cus, int waves_pe
     p.grid_partial[1] = d.num_kv_heads;
     p.grid_partial[2] = 1;
     p.block_partial = nw * 64;
-    set_merge_grid(d, batch, P, &p, true);
+    if (set_merge_grid(d, batch, P, &p, true) != PA_DECODE_OK)
+        return PA_DECODE_UNSUPPORTED;
     p.workspace_bytes = int64_t(workspace_layout(d, batch, int(P), true).total);
     p.num_cus = num_cus;
     p.waves_per_cu = waves_per_cu;
@@ -191,8 +212,8 @@ static int make_balanced_plan(const pa_decode_desc& d, int num_cus, int waves_pe
     return PA_DECODE_OK;
 }
 
-int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
-              int max_context_len, int sliding_window, int partition_size,
+int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, const PlanTuning& tune,
+              int batch, int max_context_len, int sliding_window, int partition_size,
               pa_decode_plan* plan)
 {
     if (!plan)
@@ -217,7 +238,7 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
     // page aligned).
     const int64_t vis_pages = ceil_div(std::max<int64_t>(visible, 1), ps) + (windowed ? 1 : 0);
     if (balanced && batch > 0)   // (an empty batch launches nothing either way)
-        return make_balanced_plan(d, num_cus, waves_per_cu, batch, vis_pages, plan);
+        return make_balanced_plan(d, num_cus, waves_per_cu, tune, batch, vis_pages, plan);
     // Waves the grid aims for: about four per compute unit (one per SIMD),
     // never more than the device holds at once.  Measured on MI355X, fewer
     // waves with more pages each stream KV faster than more, shorter waves.
@@ -279,21 +300,15 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
     }
     if (!split)
         wpp = int(std::min<int64_t>(nw, std::max<int64_t>(1, blocks)));  // one partition: all waves on it
-    // Experiments only: PA_DECODE_WAVES_PER_PARTITION overrides the choice.
-    if (const char* env = std::getenv("PA_DECODE_WAVES_PER_PARTITION")) {
-        const int v = std::atoi(env);
-        if (v == 1 || v == 2 || v == 4) wpp = std::min(v, nw);
-    }
+    // Experiments only: an override of the choice.
+    if (tune.waves_per_partition > 0) wpp = std::min(tune.waves_per_partition, nw);
     // A grid with fewer partitions than two per compute unit gets one
     // partition per workgroup, so that its workgroups spread over the
     // compute units instead of sharing a few.
     if (!split || units * P < int64_t(num_cus) * 2)
         nw = wpp;
-    // Experiments only: PA_DECODE_WAVES_PER_GROUP overrides the workgroup size.
-    if (const char* env = std::getenv("PA_DECODE_WAVES_PER_GROUP")) {
-        const int v = std::atoi(env);
-        if ((v == 1 || v == 2 || v == 4) && v >= wpp) nw = v;
-    }
+    // Experiments only: an override of the workgroup size.
+    if (tune.waves_per_group > 0 && tune.waves_per_group >= wpp) nw = tune.waves_per_group;
     const int slots = nw / wpp;
     const int64_t gx = ceil_div(P, slots);
     if (gx > 65535)
@@ -311,7 +326,8 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
     p.grid_partial[2] = batch;
     p.block_partial = nw * 64;
     if (split) {
-        set_merge_grid(d, batch, P, &p);
+        if (set_merge_grid(d, batch, P, &p) != PA_DECODE_OK)
+            return PA_DECODE_UNSUPPORTED;
         p.workspace_bytes = int64_t(workspace_layout(d, batch, int(P)).total);
     }
     p.num_cus = num_cus;
@@ -320,9 +336,9 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
     return PA_DECODE_OK;
 }
 
-int make_plan_csr(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
-                  int nnz_pages, int max_context_len, int sliding_window, int partition_size,
-                  pa_decode_plan* plan, int* max_ctx_used)
+int make_plan_csr(const pa_decode_desc& d, int num_cus, int waves_per_cu, const PlanTuning& tune,
+                  int batch, int nnz_pages, int max_context_len, int sliding_window,
+                  int partition_size, pa_decode_plan* plan, int* max_ctx_used)
 {
     if (!plan || nnz_pages < 0 || batch < 0 || max_context_len < 0 ||
         (partition_size < 0 && partition_size != PA_DECODE_PARTITION_BALANCED))
@@ -342,8 +358,17 @@ int make_plan_csr(const pa_decode_desc& d, int num_cus, int waves_per_cu, int ba
         if (cover > INT32_MAX)
             return PA_DECODE_UNSUPPORTED;
         S = int(cover);
+    } else if (S == 0 && batch >= 2 && batch <= kBalancedMaxBatch &&
+               int64_t(nnz_pages) * kRaggedDen <
+                   int64_t(batch) * ((mc + ps - 1) / ps) * kRaggedNum) {
+        // A ragged batch: the length-balanced schedule, when it takes these
+        // sizes (else the fixed split below).
+        const int st = make_plan(d, num_cus, waves_per_cu, tune, batch, int(mc), sliding_window,
+                                 PA_DECODE_PARTITION_BALANCED, plan);
+        if (st != PA_DECODE_UNSUPPORTED)
+            return st;
     }
-    return make_plan(d, num_cus, waves_per_cu, batch, int(mc), sliding_window, S, plan);
+    return make_plan(d, num_cus, waves_per_cu, tune, batch, int(mc), sliding_window, S, plan);
 }
 
 int64_t rotary_table_bytes(const pa_decode_desc& d)

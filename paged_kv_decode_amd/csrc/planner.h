@@ -53,27 +53,50 @@ int template_group(int G);
 // Checks the static description; returns a PA_DECODE_* status.
 int check_desc(const pa_decode_desc& d);
 
+// Overrides of the planner's choices for experiments (0 / -1: the planner's
+// own).  They change the work split only, never the result's definition or
+// the workspace size.  A handle reads them from the environment once, at
+// pa_decode_create (tuning_from_env); the plan-query functions read them at
+// each call.
+struct PlanTuning {
+    int waves_per_partition = 0;   // PA_DECODE_WAVES_PER_PARTITION: 1, 2 or 4
+    int waves_per_group = 0;       // PA_DECODE_WAVES_PER_GROUP: 1, 2 or 4
+    int balanced_start = -1;       // PA_DECODE_BALANCED_START: 0 .. 64 pages
+    int balanced_waves_per_cu = 0; // PA_DECODE_BALANCED_WAVES_PER_CU: 1 .. 16
+};
+PlanTuning tuning_from_env();
+
 // Fills `plan` for the given call sizes; returns a PA_DECODE_* status.
 // waves_per_cu: how many waves of the partial kernel one compute unit holds
 // at once (from the kernel's register and LDS use).
-int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
-              int max_context_len, int sliding_window, int partition_size,
+int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, const PlanTuning& tune,
+              int batch, int max_context_len, int sliding_window, int partition_size,
               pa_decode_plan* plan);
 
-// The plan for a CSR page table (nnz_pages pages in use): the host switch of
-// TVM PR #20426, section "Change" -- with partition_size 0, one partition per
-// (sequence, KV head) when nnz_pages <= batch * 256 / page_size, else the
-// planner's split.  max_context_len 0 stands for nnz_pages * page_size; the
-// bound actually used is returned in *max_ctx_used (may be null).
-int make_plan_csr(const pa_decode_desc& d, int num_cus, int waves_per_cu, int batch,
-                  int nnz_pages, int max_context_len, int sliding_window, int partition_size,
-                  pa_decode_plan* plan, int* max_ctx_used);
+// Ragged-batch rule of the CSR form with partition_size 0: a batch of 2 ..
+// 64 sequences whose mean page count is below kRaggedNum / kRaggedDen of the
+// longest possible (nnz_pages * kRaggedDen < batch * ceil(max_context_len /
+// page_size) * kRaggedNum) runs the length-balanced schedule.
+constexpr int kRaggedNum = 3;
+constexpr int kRaggedDen = 4;
 
-// LDS bytes of one wave's rotary base table (0 without rotary): the (cos,
-// sin) of every frequency at each page of a block.
+// The plan for a CSR page table (nnz_pages pages in use).  With
+// partition_size 0: the host switch of TVM PR #20426, section "Change" (one
+// partition per (sequence, KV head) when nnz_pages <= batch * 256 /
+// page_size); else, for a ragged batch (the rule above, also a page count
+// known on the host), the length-balanced schedule; else the planner's fixed
+// split.  max_context_len 0 stands for nnz_pages * page_size; the bound
+// actually used is returned in *max_ctx_used (may be null).
+int make_plan_csr(const pa_decode_desc& d, int num_cus, int waves_per_cu, const PlanTuning& tune,
+                  int batch, int nnz_pages, int max_context_len, int sliding_window,
+                  int partition_size, pa_decode_plan* plan, int* max_ctx_used);
+
 // Waves per workgroup of the partial kernel for this description (1, 2 or 4;
 // LDS-limited).
 int workgroup_waves(const pa_decode_desc& d);
+
+// LDS bytes of one wave's rotary base table (0 without rotary): the (cos,
+// sin) of every frequency at each page of a block.
 int64_t rotary_table_bytes(const pa_decode_desc& d);
 
 // LDS bytes of a workgroup's rotary offset table (0 without rotary): the
@@ -100,6 +123,6 @@ constexpr int kBalancedMaxBatch = 64;
 // four blocks' worth, three with rotary (a segment's start waits for its
 // page ids and q before the first block's loads go out, and its pipeline
 // starts empty).
-int balanced_start_pages(const pa_decode_desc& d);
+int balanced_start_pages(const pa_decode_desc& d, const PlanTuning& tune);
 
 }  // namespace pa

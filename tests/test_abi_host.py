@@ -227,9 +227,37 @@ def test_csr_host_switch_follows_the_page_count(batch, avg_tokens):
     if nnz * 16 <= batch * 256:
         assert p.split == 0 and p.num_partitions == 1 and p.partition_size >= max_ctx
         assert p.workspace_bytes == 0
+    elif 2 <= batch <= 64:
+        # mean length half the bound: a ragged batch, the balanced schedule
+        assert 4 * nnz < 3 * batch * (-(-max_ctx // 16))
+        dense = plan(w, batch=batch, max_ctx=max_ctx, S=B.PA_DECODE_PARTITION_BALANCED)
+        assert p.balanced_waves > 0 and p.as_dict() == dense.as_dict()
     else:
         dense = plan(w, batch=batch, max_ctx=max_ctx, S=0)
         assert p.as_dict() == dense.as_dict()
+
+
+@pytest.mark.parametrize("batch,lens", [
+    (16, [4096] * 16),                         # uniform: fixed partitions
+    (16, [4096 - 37 * i for i in range(16)]),   # nearly uniform: fixed
+    (16, [1 + 273 * i for i in range(16)]),     # ragged 1 .. 4096: balanced
+    (2, [100000, 3060]),                       # one long, one short: balanced
+    (65, [4096] + [17] * 64),                  # ragged but above 64 sequences: fixed
+    (4, [8192] * 4),                           # the windowed workload's batch: fixed
+])
+def test_csr_ragged_rule_picks_the_balanced_schedule(batch, lens):
+    """With partition_size 0 and pages above the single-pass switch, the CSR
+    host picks the length-balanced schedule when the mean page count is
+    below 3/4 of what max_context_len allows (batches of 2 .. 64), else the
+    fixed partitions; the choice is made on host counts only."""
+    w = W.CONFIGS["llama8b_b16_ragged_f16"]
+    nnz = sum(-(-n // 16) for n in lens)
+    max_ctx = max(lens)
+    p = csr_plan(w, batch, nnz, max_ctx=max_ctx)
+    ragged = 2 <= batch <= 64 and 4 * nnz < 3 * batch * (-(-max_ctx // 16))
+    assert (p.balanced_waves > 0) == ragged, p.as_dict()
+    if not ragged:
+        assert p.as_dict() == plan(w, batch=batch, max_ctx=max_ctx, S=0).as_dict()
 
 
 def test_csr_plan_defaults_and_forced_partitions():

@@ -94,3 +94,26 @@ def test_csr_shared_pages():
     for S in (0, 64):
         out, lse, _ = run_gpu_csr(p2, csr, partition_size=S)
         compare(out, lse, ref_out, ref_lse, torch.float16, "csr shared S=%d" % S)
+
+
+def test_csr_ragged_batch_plans_the_balanced_schedule_itself():
+    """partition_size 0 on the CSR path: the ragged batch-16 workload
+    (lengths 1 .. 4096, mean about half the longest) gets the length-balanced
+    schedule from the host's page count; a batch of equal lengths keeps the
+    fixed partitions.  Both match the oracle."""
+    p = W.generate(W.CONFIGS["llama8b_b16_ragged_f16"])
+    csr = W.to_csr(p)
+    out, lse, plan = run_gpu_csr(p, csr, partition_size=0)
+    assert plan["balanced_waves"] > 0, plan
+    ref = run_oracle(p)
+    compare(out, lse, ref[0], ref[1], torch.float16, "csr ragged auto")
+    # the same schedule as asking for it
+    out_b, lse_b, plan_b = run_gpu_csr(p, csr, partition_size=W.BALANCED)
+    assert plan_b == plan and torch.equal(out_b, out) and torch.equal(lse_b, lse)
+    uni = W.custom(batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype=torch.float16,
+                   context_lens=[2171] * 16, seed=904)
+    pu = W.generate(uni)
+    out, lse, plan = run_gpu_csr(pu, W.to_csr(pu), partition_size=0)
+    assert plan["balanced_waves"] == 0 and plan["split"] == 1, plan
+    ref = run_oracle(pu)
+    compare(out, lse, ref[0], ref[1], torch.float16, "csr uniform auto")
