@@ -9,9 +9,13 @@ Timed region: W eager warm-up steps, then exactly K steps replayed from one
 HIP graph, bracketed by synchronisations, timed with events on the launch
 stream.  The K steps cycle over R replicas of the workload whose page pools
 are independent random permutations of the same pages (every replica computes
-the same result); R is large enough that the KV the rotation touches exceeds
-the GPU's last-level caches, so each step reads its KV from HBM rather than
-from cache.  Inputs are resident in HBM before the timed region starts.
+the same result); R is large enough that a replica's KV is read again only
+after four times the GPU's last-level cache capacity of other replicas' KV,
+and a 1 GiB read-and-write flush runs before the timed replay (and before
+every other measured phase), so each step reads its KV from HBM rather than
+from cache at any K.  Inputs are resident in HBM before the timed region
+starts.  cold_per_call_us: single calls timed one at a time, each after a
+flush (p10 / median / p90 over --cold-calls calls).
 
 value = algorithmic KV bytes per step / seconds per step (GB/s), where the
 algorithmic bytes are the K and V bytes of the visible keys only.
@@ -50,6 +54,7 @@ from paged_kv_decode_amd import workloads as W  # noqa: E402
 METRIC = "decode-attention µs/step + achieved KV HBM GB/s (% of peak) at ctx 3k / 100k"
 PEAK_GBPS = 8000.0
 CACHE_BYTES = 288 << 20          # 256 MiB MALL + 8 x 4 MiB L2
+FLUSH_BYTES = 1 << 30            # read and written before every timed phase
 KERNEL_SOURCES = ["paged_kv_decode_amd/csrc/pa_decode_kernels.hip",
                   "paged_kv_decode_amd/csrc/partial_kernel.h",
                   "paged_kv_decode_amd/csrc/pa_decode_balanced.hip",
@@ -141,11 +146,60 @@ def run_oracle_baseline(p: W.Problem, budget_s: float):
     return out, lse, reps, el, threads
 
 
+def replica_count(kv_bytes, pool_bytes, layers=1, replicas=None):
+    """Replicas in the cold-cache rotation: enough that a replica's K/V is
+    read again only after 4 x CACHE_BYTES of other replicas' K/V (at most
+    64 GiB of pools, at least two per layer), a whole number of steps of
+    `layers` distinct caches; or the count asked for."""
+    if replicas is None:
+        R = max(2 * layers, math.ceil(4 * CACHE_BYTES / max(kv_bytes, 1)) + 1)
+        R = min(R, max(2 * layers, int((64 << 30) // pool_bytes)))
+    else:
+        R = max(replicas, layers)
+    return -(-R // layers) * layers
+
+
+class Flusher:
+    """Evicts the GPU's caches: a reduction kernel (torch's sum) reads
+    FLUSH_BYTES, four times the 256 MB MALL, well past the 8 x 4 MB of L2.
+    Reads rather than writes, so that the caches hold no dirty lines whose
+    write-back would fall into the next timed interval.  Queued on the
+    current stream outside every timed interval, right before its start
+    event (no host synchronisation in between, so the GPU is busy with the
+    flush while the timed work is being submitted)."""
+
+    def __init__(self):
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        self.count = 0
+
+    def __call__(self):
+        self.sink = self.buf.sum()
+        self.count += 1
+
+
+def percentiles(xs):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    q = lambda f: xs[min(len(xs) - 1, int(round(f * (len(xs) - 1))))]  # noqa: E731
+    return {"p10": round(q(0.10), 3), "median": round(q(0.5), 3), "p90": round(q(0.90), 3),
+            "min": round(xs[0], 3), "max": round(xs[-1], 3), "n": len(xs)}
+
+
 def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cache,
-                   table="dense", layers=1):
+                   table="dense", layers=1, phases="all", cold_calls=100, flusher=None):
     """One step = `layers` decode-attention calls on distinct KV caches
     (page-permuted copies of the workload's pool, one per layer), launched
-    back to back."""
+    back to back.
+
+    Cold caches at any step count: each replica's K/V is read again only
+    after at least 4 x CACHE_BYTES of other replicas' K/V (R replicas in
+    rotation), and a FLUSH_BYTES flush runs before every phase (warm-up,
+    graph upload replay, timed replay, kernel-timing pass, each spread
+    replay, the per-call figures), so no phase starts on data a previous
+    phase left in a cache.  phases="cold" leaves out the warm-cache figure,
+    the spread replays and the read probe (the profiler then sees only cold
+    launches of the kernels)."""
     w = W.CONFIGS[name]
     S = w.partition_size if partition_size is None else partition_size
     t0 = time.perf_counter()
@@ -158,14 +212,10 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
                                   max_batch=max(w.batch, 64), max_context_len=1 << 20,
                                   rope=w.rope)
         eng_cache[key] = eng
+    flush = flusher if flusher is not None else Flusher()
     kv_bytes = p.kv_bytes()
-    if replicas is None:
-        pool_bytes = 2 * p.k_cache.numel() * p.k_cache.element_size()
-        R = max(2 * layers, math.ceil(4 * CACHE_BYTES / kv_bytes))
-        R = min(R, max(2 * layers, int((64 << 30) // pool_bytes)))
-    else:
-        R = max(replicas, layers)
-    R = -(-R // layers) * layers   # whole steps of `layers` distinct caches
+    R = replica_count(kv_bytes, 2 * p.k_cache.numel() * p.k_cache.element_size(), layers,
+                      replicas)
     reps = Replicas(p, R, eng, S, table)
     log("%s: %d replicas, %.1f MB KV per step" % (name, R, kv_bytes / 1e6))
     stream = torch.cuda.current_stream()
@@ -182,6 +232,7 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
     plan = eng.last_plan().as_dict()
 
     L = layers
+    flush()
     for i in range(warmup * L):
         reps.run(reps.args[i % R], sp)
     torch.cuda.synchronize()
@@ -196,10 +247,12 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
                 for i in range(steps * L):
                     reps.run(reps.args[i % R], cs)
         stream.wait_stream(cap)
+        flush()
         g.replay()  # upload / first replay, untimed
         torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    flush()
     start.record(stream)
     if mode == "graph":
         g.replay()
@@ -212,14 +265,15 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
     ms_per_step = ms_total / steps
 
     # Spread and warm-cache figures (after the timed region; not part of it):
-    # the same graph replayed five more times (µs/step of each replay), and,
-    # for graph mode, K steps on one replica only, so that its K/V stays in
-    # the L2 and the 256 MB MALL where it fits.
+    # the same graph replayed five more times, each after a flush (µs/step
+    # of each replay), and, for graph mode, K steps on one replica only, so
+    # that its K/V stays in the L2 and the 256 MB MALL where it fits.
     spread = None
     warm = None
-    if mode == "graph":
+    if mode == "graph" and phases == "all":
         per = []
         for _ in range(5):
+            flush()
             start.record(stream)
             g.replay()
             stop.record(stream)
@@ -245,9 +299,12 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
             torch.cuda.synchronize()
             warm = round(1e3 * start.elapsed_time(stop) / steps, 3)
             del gw
+    if mode == "graph":
+        del g
 
     # Kernel durations: start/stop events recorded around each launch.
     nprof = min(steps, 2000)
+    flush()
     binding.pa_decode_profile_begin(eng.handle, nprof)
     for i in range(nprof):
         reps.run(reps.args[i % R], sp)
@@ -255,11 +312,37 @@ def bench_workload(name, steps, warmup, replicas, partition_size, mode, eng_cach
     partial_us = 1e3 * pm / max(pn, 1)
     merge_us = 1e3 * mm / max(mn, 1) if mn else 0.0
 
-    ceiling = same_pages_probe(reps, p, min(steps, 500), sp) if layers == 1 else None
+    # One cold call at a time (layers == 1): a flush, then events around one
+    # step (all of its kernels); the flush keeps the GPU busy while the step
+    # is queued, so the interval holds the step's kernels and the gaps
+    # between them, not the host's launch time.
+    cold = None
+    if layers == 1 and cold_calls > 0:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(cold_calls)]
+        for i in range(cold_calls):
+            flush()
+            ev[i][0].record(stream)
+            reps.run(reps.args[i % R], sp)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        cold = percentiles([1e3 * a.elapsed_time(b) for a, b in ev])
+
+    ceiling = None
+    if layers == 1 and phases == "all":
+        flush()
+        ceiling = same_pages_probe(reps, p, min(steps, 500), sp, flush)
 
     res = {
         "workload": name, "p": p, "plan": plan, "kv_bytes": kv_bytes * L, "replicas": R,
         "read_ceiling": ceiling, "spread": spread, "warm_us_per_step": warm,
+        "cold_per_call_us": cold,
+        "cold_guard": {"flush_bytes": FLUSH_BYTES, "flushes": flush.count,
+                       "reread_after_bytes": int(kv_bytes * (R - 1)),
+                       "cache_bytes": CACHE_BYTES,
+                       "flushed_before": ["warm-up", "graph upload replay", "timed replay",
+                                          "each spread replay", "kernel-timing pass",
+                                          "each cold call", "read probe"]},
         "layers": L, "ms_per_step": ms_per_step, "us_per_step": 1e3 * ms_per_step,
         "us_per_layer": 1e3 * ms_per_step / L,
         "gbps": kv_bytes * L / (ms_per_step * 1e-3) / 1e9,
@@ -295,7 +378,7 @@ def chunk_addresses(p: W.Problem, k: torch.Tensor, v: torch.Tensor, pt: torch.Te
     return torch.cat(rows).contiguous()
 
 
-def same_pages_probe(reps, p: W.Problem, launches: int, stream_ptr: int):
+def same_pages_probe(reps, p: W.Problem, launches: int, stream_ptr: int, flush):
     """Read-rate ceiling next to the kernel: pa_decode_read_probe reading
     exactly the KV chunks a step reads (same replicas, same cold-cache
     rotation, graph-replayed like the steps), and a plain contiguous read of
@@ -330,6 +413,7 @@ def same_pages_probe(reps, p: W.Problem, launches: int, stream_ptr: int):
     g.replay()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flush()
     a.record(stream)
     g.replay()
     b.record(stream)
@@ -357,15 +441,20 @@ def same_pages_probe(reps, p: W.Problem, launches: int, stream_ptr: int):
 
 
 def parity_against(res, ref_out, ref_lse):
-    """rel-L2 of the GPU output against the oracle's (rounded to the output
-    dtype) and the largest lse error, from outputs the cpu_baseline leg's
-    oracle run already produced."""
+    """Errors of the GPU output against the oracle's, from outputs the
+    cpu_baseline leg's oracle run already produced: rel-L2 against the
+    oracle rounded to the output dtype, the worst (sequence, head) row (error
+    beyond one output ulp per element, as a fraction of the row's norm; see
+    tests/parity.py) and the largest lse error."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import parity
     p = res["p"]
-    ref = torch.from_numpy(ref_out).to(p.q.dtype).double()
-    rel = ((res["gpu_out"].double() - ref).norm() / ref.norm()).item()
-    fin = np.isfinite(ref_lse)
-    lerr = float(np.abs(res["gpu_lse"].double().numpy()[fin] - ref_lse[fin]).max())
-    return rel, lerr
+    e = parity.out_errors(res["gpu_out"], ref_out, p.q.dtype)
+    lerr, _ = parity.lse_error(res["gpu_lse"], ref_lse)
+    b, h = divmod(e["row_worst"], p.q.shape[1])
+    return {"out_rel_l2": e["rel_l2"], "row_excess_max": e["row_excess"],
+            "worst_row": {"b": b, "h": h}, "row_rel_l2_max": e["row_rel_l2_max"],
+            "out_max_abs_err": e["max_abs"], "lse_max_abs_err": lerr}
 
 
 def traffic_for(name, plan):
@@ -401,6 +490,13 @@ def main():
                          "layer-stacked decode step); the extra workloads keep 1")
     ap.add_argument("--page-table", choices=["dense", "csr"], default="dense",
                     help="page-table form passed to the library (csr: pa_decode_run_csr)")
+    ap.add_argument("--phases", choices=["all", "cold"], default="all",
+                    help="cold: leave out the warm-cache figure, the spread replays and the "
+                         "read probe (profiling runs, so that a kernel's trace holds cold "
+                         "launches only)")
+    ap.add_argument("--cold-calls", type=int, default=100,
+                    help="single calls timed one at a time, each after a cache flush "
+                         "(p10 / median / p90 reported)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
     ap.add_argument("--probe", choices=["copy"], default=None,
@@ -437,16 +533,17 @@ def main():
     engines = {}
     if args.layers < 1:
         ap.error("--layers must be >= 1")
+    flusher = Flusher()
     main_res = bench_workload(args.workload, args.steps, args.warmup, args.replicas,
                               args.partition_size, args.mode, engines, args.page_table,
-                              args.layers)
+                              args.layers, args.phases, args.cold_calls, flusher)
     log("%s: %.2f us/step, %.0f GB/s; partial %.2f us (%.0f GB/s), merge %.2f us" % (
         args.workload, main_res["us_per_step"], main_res["gbps"], main_res["partial_us"],
         main_res["partial_gbps"], main_res["merge_us"]))
     also = {}
     for name in [s for s in args.also.split(",") if s and s != args.workload]:
         r = bench_workload(name, args.also_steps, 20, None, None, args.mode, engines,
-                           args.page_table)
+                           args.page_table, 1, args.phases, args.cold_calls, flusher)
         also[name] = {
             "us_per_step": round(r["us_per_step"], 3), "GBps": round(r["gbps"], 1),
             "frac_of_peak": round(r["gbps"] / PEAK_GBPS, 4),
@@ -457,6 +554,7 @@ def main():
             "plan": {k: r["plan"][k] for k in ("partition_size", "num_partitions",
                                                "waves_per_group", "split")},
             "read_ceiling": r["read_ceiling"],
+            "cold_per_call_us": r["cold_per_call_us"],
         }
         log("%s: %.2f us/step, %.0f GB/s; partial %.2f us (%.0f GB/s), merge %.2f us" % (
             name, r["us_per_step"], r["gbps"], r["partial_us"], r["partial_gbps"],
@@ -476,8 +574,7 @@ def main():
                "sample": "%d decode-attention calls (one layer each) of the %s workload (float64 C oracle, OpenMP), %.1f s"
                          % (reps, args.workload, el),
                "us_per_step": round(1e6 * el / reps, 1)}
-        rel, lerr = parity_against(main_res, ref_out, ref_lse)
-        par = {"out_rel_l2": rel, "lse_max_abs_err": lerr}
+        par = parity_against(main_res, ref_out, ref_lse)
     dtype_name = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}
     w = W.CONFIGS[args.workload]
     traffic = traffic_for(args.workload, main_res["plan"])
@@ -505,6 +602,8 @@ def main():
                    "us_per_layer": round(main_res["us_per_layer"], 3),
                    "us_per_step_replays": main_res["spread"],
                    "warm_us_per_step": main_res["warm_us_per_step"],
+                   "cold_per_call_us": main_res["cold_per_call_us"],
+                   "cold_guard": main_res["cold_guard"],
                    "plan": main_res["plan"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
@@ -557,7 +656,8 @@ def profile_commands(outdir):
     cmds = []
     for w in PROFILED:
         steps = 2000 if w == "llama1b_ctx3060_f16" else 300
-        run = "python3 %s --workload %s --also '' --cpu-budget 0 --steps %d --warmup 20" % (b, w, steps)
+        run = ("python3 %s --workload %s --also '' --cpu-budget 0 --steps %d --warmup 20 "
+               "--phases cold --cold-calls 0" % (b, w, steps))
         cmds.append(("bench_%s" % w, run))
         cmds.append(("trace_%s" % w, "rocprofv3 --kernel-trace --stats --output-format csv -d %s/trace_%s "
                                      "-o %s -- %s" % (outdir, w, w, run)))
@@ -565,7 +665,8 @@ def profile_commands(outdir):
         for w in PROFILED:
             cmds.append(("pmc_%s_%s" % (w, c),
                          "rocprofv3 --pmc %s --output-format csv -d %s/pmc_%s_%s -o %s -- python3 %s "
-                         "--workload %s --also '' --cpu-budget 0 --steps 20 --warmup 2 --mode eager"
+                         "--workload %s --also '' --cpu-budget 0 --steps 20 --warmup 2 --mode eager "
+                         "--phases cold --cold-calls 0"
                          % (c, outdir, w, c, w, b, w)))
         cmds.append(("pmc_copy_%s" % c,
                      "rocprofv3 --pmc %s --output-format csv -d %s/pmc_copy_%s -o copy -- python3 %s "

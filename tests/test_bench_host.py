@@ -6,6 +6,9 @@
 * traffic_for reports stored HBM traffic only while the stored kernel hash
   matches the sources.
 * bench.py refuses more than one GPU with a message.
+* the cold-cache rotation: a replica is read again only after four times the
+  last-level caches of other replicas' K/V, for every workload, at any step
+  count (a flush also runs before each measured phase).
 """
 import json
 import os
@@ -63,3 +66,25 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert r.returncode == 2
     assert "single" in r.stderr and "--gpus 2" not in r.stdout
+
+
+def test_replica_rotation_rereads_only_after_four_cache_sizes():
+    for name in W.CONFIG_ORDER:
+        p = W.generate(W.CONFIGS[name])
+        kv = p.kv_bytes()
+        pool = 2 * p.k_cache.numel() * p.k_cache.element_size()
+        for layers in (1, 16):
+            R = bench.replica_count(kv, pool, layers)
+            assert R % layers == 0 and R >= 2 * layers
+            if R * pool < (64 << 30) - pool:       # not capped by the 64 GiB of pools
+                assert (R - 1) * kv >= 4 * bench.CACHE_BYTES, (name, layers, R)
+    assert bench.FLUSH_BYTES >= 4 * (256 << 20)
+    assert bench.replica_count(1 << 20, 1 << 20, 1, replicas=7) == 7
+    assert bench.replica_count(1 << 20, 1 << 20, 4, replicas=7) == 8
+
+
+def test_percentiles():
+    r = bench.percentiles([float(x) for x in range(1, 101)])
+    assert r["n"] == 100 and r["min"] == 1 and r["max"] == 100
+    assert r["p10"] == 11 and r["median"] == 51 and r["p90"] == 90
+    assert bench.percentiles([]) is None
