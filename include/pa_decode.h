@@ -64,6 +64,8 @@ enum {
     PA_DECODE_UNSUPPORTED = -2,         /* head_dim / page_size / dtype / G not built */
     PA_DECODE_WORKSPACE_TOO_SMALL = -3, /* args.workspace_bytes below the plan's need */
     PA_DECODE_HIP_ERROR = -4,           /* a HIP call failed; see pa_decode_last_hip_error */
+    PA_DECODE_EXCEEDS_SCRATCH = -5,     /* pa_decode_run_noalloc: the plan needs more than */
+                                        /*   pa_decode_noalloc_scratch_bytes() of states   */
 };
 
 /* Bits of the device-side contract check (pa_decode_debug_status).  The
@@ -235,6 +237,27 @@ int pa_decode_workspace_size(pa_decode_handle handle, int32_t batch, int32_t max
  * contract reads no memory outside the caller's buffers (see
  * PA_DECODE_VIOLATION_*); its out/lse are then unspecified. */
 int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* stream);
+
+/* One decode step that allocates nothing, for callers that cannot allocate
+ * device memory or hand over a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * plan, kernels and result as pa_decode_run, except that args->workspace and
+ * args->workspace_bytes are ignored: the partition states go to a fixed
+ * device array of pa_decode_noalloc_scratch_bytes() bytes (64 MiB) that the
+ * library's code object holds on each GPU from its load until the process
+ * ends.  Calls no allocating routine and never synchronises.
+ * Limit: a plan whose workspace (pa_decode_workspace_size) exceeds that size
+ * is rejected with PA_DECODE_EXCEEDS_SCRATCH before anything launches; plans
+ * without a split need none.  Every handle on one GPU shares that GPU's
+ * array, which keeps the last call's contents (nothing in it has to start
+ * at zero: each call writes every state it reads): calls that can overlap on
+ * one GPU (other streams, other threads, other handles) race and must be
+ * serialised by the caller.  HIP_ERROR (pa_decode_last_hip_error) when the
+ * array's address could not be found at pa_decode_create. */
+int pa_decode_run_noalloc(pa_decode_handle handle, const pa_decode_args* args, void* stream);
+
+/* Size in bytes of the fixed device scratch of pa_decode_run_noalloc. */
+size_t pa_decode_noalloc_scratch_bytes(void);
 
 /* Violation bits (PA_DECODE_VIOLATION_*) collected by the runs on this
  * handle since the previous call, then cleared.  Needs desc.debug_checks = 1

@@ -23,6 +23,7 @@ PA_DECODE_INVALID_ARG = -1
 PA_DECODE_UNSUPPORTED = -2
 PA_DECODE_WORKSPACE_TOO_SMALL = -3
 PA_DECODE_HIP_ERROR = -4
+PA_DECODE_EXCEEDS_SCRATCH = -5
 
 # partition_size value for the length-balanced schedule (batch <= 64).
 PA_DECODE_PARTITION_BALANCED = -1
@@ -40,7 +41,8 @@ EXPORTED = ["pa_decode_create", "pa_decode_destroy", "pa_decode_workspace_size",
             "pa_decode_profile_begin", "pa_decode_profile_end",
             "pa_decode_last_hip_error", "pa_decode_status_string",
             "pa_decode_workspace_size_csr", "pa_decode_run_csr", "pa_decode_plan_query_csr",
-            "pa_decode_debug_status", "pa_decode_read_probe"]
+            "pa_decode_debug_status", "pa_decode_read_probe", "pa_decode_run_noalloc",
+            "pa_decode_noalloc_scratch_bytes"]
 
 
 class PaDecodeDesc(ctypes.Structure):
@@ -141,11 +143,14 @@ def load_library(path: Optional[str] = None):
         lib.pa_decode_last_hip_error.argtypes = [vp]
         lib.pa_decode_debug_status.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
         lib.pa_decode_read_probe.argtypes = [vp, vp, i32, i32, vp, vp]
+        lib.pa_decode_run_noalloc.argtypes = [vp, ctypes.POINTER(PaDecodeArgs), vp]
+        lib.pa_decode_noalloc_scratch_bytes.argtypes = []
         lib.pa_decode_status_string.argtypes = [ctypes.c_int]
         lib.pa_decode_status_string.restype = ctypes.c_char_p
         for name in EXPORTED:
             if name != "pa_decode_status_string":
                 getattr(lib, name).restype = ctypes.c_int
+        lib.pa_decode_noalloc_scratch_bytes.restype = ctypes.c_size_t
         if path is None:
             _lib = lib
         return lib
@@ -211,6 +216,18 @@ def pa_decode_workspace_size(handle, batch: int, max_context_len: int, sliding_w
 def pa_decode_run(handle, args: PaDecodeArgs, stream: int = 0) -> None:
     _check(load_library().pa_decode_run(handle, ctypes.byref(args), ctypes.c_void_p(stream)),
            "pa_decode_run")
+
+
+def pa_decode_run_noalloc(handle, args: PaDecodeArgs, stream: int = 0) -> None:
+    """pa_decode_run with the partition states in the library's fixed device
+    scratch (args.workspace is ignored); allocates nothing."""
+    _check(load_library().pa_decode_run_noalloc(handle, ctypes.byref(args),
+                                                ctypes.c_void_p(stream)),
+           "pa_decode_run_noalloc")
+
+
+def pa_decode_noalloc_scratch_bytes() -> int:
+    return int(load_library().pa_decode_noalloc_scratch_bytes())
 
 
 def pa_decode_last_plan(handle) -> PaDecodePlan:
@@ -453,6 +470,13 @@ class PagedDecode:
         if stream is None:
             stream = torch.cuda.current_stream(self.device).cuda_stream
         pa_decode_run(self.handle, args, stream)
+
+    def run_noalloc_args(self, args: PaDecodeArgs, stream: Optional[int] = None) -> None:
+        """pa_decode_run_noalloc on an argument block from make_args (its
+        workspace is ignored)."""
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        pa_decode_run_noalloc(self.handle, args, stream)
 
     def __call__(self, q, k_cache, v_cache, page_table, context_lens, scale,
                  max_context_len=None, sliding_window=0, partition_size=0, out=None,

@@ -19,6 +19,7 @@ SOURCES = [
     os.path.join(HERE, "csrc", "pa_decode_api.cpp"),
     os.path.join(HERE, "csrc", "planner.cpp"),
     os.path.join(HERE, "csrc", "validate.cpp"),
+    os.path.join(HERE, "csrc", "pa_decode_scratch.hip"),
 ]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -18,6 +18,7 @@
 #include "kernels.h"
 #include "pa_decode.h"
 #include "planner.h"
+#include "scratch.h"
 #include "validate.h"
 
 // Start/stop event pairs for kernel timing (see pa_decode_profile_begin).
@@ -96,6 +97,8 @@ struct pa_decode_handle_s {
     bool profiling;
     EventRing prof_partial, prof_merge;
     int32_t* status_word;  // device, with desc.debug_checks: violation bits
+    void* scratch;         // desc.device's fixed scratch array (pa_decode_run_noalloc)
+    int scratch_error;     // hipError_t of its address lookup at create (0: found)
 };
 
 namespace {
@@ -282,6 +285,11 @@ int pa_decode_create(const pa_decode_desc* desc, pa_decode_handle* handle)
     h->last_hip_error = 0;
     h->profiling = false;
     h->status_word = nullptr;
+    // The device address of the fixed scratch array, looked up once per
+    // device (the lookup makes desc.device current and restores the caller's
+    // device).  A failure only disables pa_decode_run_noalloc on this handle.
+    h->scratch = nullptr;
+    h->scratch_error = int(pa::scratch_address(desc->device, &h->scratch));
     if (desc->debug_checks) {
         int prev = -1;
         hipError_t e = hipGetDevice(&prev);
@@ -407,6 +415,34 @@ int pa_decode_run(pa_decode_handle handle, const pa_decode_args* args, void* str
     return launch_step(handle, pa::common_args(a), src, plan, stream);
 }
 
+int pa_decode_run_noalloc(pa_decode_handle handle, const pa_decode_args* args, void* stream)
+{
+    if (!handle || !args)
+        return PA_DECODE_INVALID_ARG;
+    const pa_decode_desc& d = handle->desc;
+    const pa_decode_args& a = *args;
+    int st = pa::check_args(d, a);
+    if (st != PA_DECODE_OK)
+        return st;
+    pa_decode_plan plan;
+    st = plan_dense(handle, a.batch, a.max_context_len, a.sliding_window, a.partition_size, &plan);
+    if (st != PA_DECODE_OK)
+        return st;
+    if (plan.workspace_bytes > int64_t(pa::kScratchBytes))
+        return PA_DECODE_EXCEEDS_SCRATCH;
+    if (!handle->scratch) {
+        handle->last_hip_error = handle->scratch_error;
+        return PA_DECODE_HIP_ERROR;
+    }
+    pa::StepArgs c = pa::common_args(a);
+    c.workspace = handle->scratch;   // the device address, never the array's host-side name
+    c.workspace_bytes = pa::kScratchBytes;
+    PageSource src = {a.page_table, a.pt_stride, a.context_lens, nullptr, nullptr, 0};
+    return launch_step(handle, c, src, plan, stream);
+}
+
+size_t pa_decode_noalloc_scratch_bytes(void) { return pa::kScratchBytes; }
+
 int pa_decode_workspace_size_csr(pa_decode_handle handle, int32_t batch, int32_t nnz_pages,
                                  int32_t max_context_len, int32_t sliding_window,
                                  int32_t partition_size, size_t* bytes)
@@ -511,6 +547,9 @@ const char* pa_decode_status_string(int status)
     case PA_DECODE_UNSUPPORTED: return "unsupported configuration";
     case PA_DECODE_WORKSPACE_TOO_SMALL: return "workspace too small";
     case PA_DECODE_HIP_ERROR: return "HIP error";
+    case PA_DECODE_EXCEEDS_SCRATCH:
+        return "the plan's partition states exceed the fixed device scratch of "
+               "pa_decode_run_noalloc";
     default: return "unknown status";
     }
 }

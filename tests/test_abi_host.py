@@ -29,7 +29,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol():
     text = open(HEADER).read()
-    declared = set(re.findall(r"^\s*(?:int|const char\*)\s+(pa_decode_\w+)\s*\(", text, re.M))
+    declared = set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(pa_decode_\w+)\s*\(", text, re.M))
     assert declared == set(B.EXPORTED), declared ^ set(B.EXPORTED)
     L = lib()
     for name in declared:
