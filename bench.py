@@ -11,8 +11,8 @@ stream.  The K steps cycle over R replicas of the workload whose page pools
 are independent random permutations of the same pages (every replica computes
 the same result); R is large enough that a replica's KV is read again only
 after four times the GPU's last-level cache capacity of other replicas' KV,
-and a 1 GiB read-and-write flush runs before the timed replay (and before
-every other measured phase), so each step reads its KV from HBM rather than
+and a 1 GiB read flush runs before the timed replay (and before every
+other measured phase), so each step reads its KV from HBM rather than
 from cache at any K.  Inputs are resident in HBM before the timed region
 starts.  cold_per_call_us: single calls timed one at a time, each after a
 flush (p10 / median / p90 over --cold-calls calls).
@@ -160,20 +160,27 @@ def replica_count(kv_bytes, pool_bytes, layers=1, replicas=None):
 
 
 class Flusher:
-    """Evicts the GPU's caches: a reduction kernel (torch's sum) reads
-    FLUSH_BYTES, four times the 256 MB MALL, well past the 8 x 4 MB of L2.
-    Reads rather than writes, so that the caches hold no dirty lines whose
-    write-back would fall into the next timed interval.  Queued on the
-    current stream outside every timed interval, right before its start
-    event (no host synchronisation in between, so the GPU is busy with the
-    flush while the timed work is being submitted)."""
+    """Evicts the K/V a previous phase left in the GPU's caches: the library's
+    read probe (the partial kernel's own 16-byte non-temporal load) reads
+    FLUSH_BYTES, four times the 256 MB MALL and far past the 8 x 4 MB of L2.
+    Measured on MI355X, a step timed right after this flush costs what it
+    costs after 20 steps over another replica's K/V (the eviction a decode
+    loop sees), while a flush with ordinary loads (torch's fill_ or sum over
+    1 GiB) adds about 1 us per call more and slows the next ~20 ms of steps
+    for reasons other than K/V residency.  Queued on the current stream
+    outside every timed interval, right before its start event (no host
+    synchronisation in between, so the GPU is busy with the flush while the
+    timed work is being submitted)."""
 
     def __init__(self):
         self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
         self.count = 0
 
     def __call__(self):
-        self.sink = self.buf.sum()
+        binding.pa_decode_read_probe(self.buf.data_ptr(), 0, FLUSH_BYTES // 8192, 8192,
+                                     self.sink.data_ptr(),
+                                     torch.cuda.current_stream().cuda_stream)
         self.count += 1
 
 
@@ -497,6 +504,9 @@ def main():
     ap.add_argument("--cold-calls", type=int, default=100,
                     help="single calls timed one at a time, each after a cache flush "
                          "(p10 / median / p90 reported)")
+    ap.add_argument("--library", default=None,
+                    help="load this build of the library instead of the package's (comparison "
+                         "builds, e.g. python -m paged_kv_decode_amd.build --variant qk_valu)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
     ap.add_argument("--probe", choices=["copy"], default=None,
@@ -507,13 +517,17 @@ def main():
                     help="print the rocprofv3 commands whose output --summarize-profiles reads")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="write profiles/*.md and profiles/traffic.json from that output")
+    ap.add_argument("--profile-set", choices=["main", "ab"], default="main",
+                    help="which runs --profile-commands / --summarize-profiles cover (ab: q.k "
+                         "on the matrix cores against the vector ALUs)")
     args = ap.parse_args()
 
     if args.profile_commands:
-        print("\n".join("%s\t%s" % nc for nc in profile_commands(args.profile_commands)))
+        print("\n".join("%s\t%s" % nc for nc in profile_commands(args.profile_commands,
+                                                                  args.profile_set)))
         return
     if args.summarize_profiles:
-        summarize_profiles(args.summarize_profiles)
+        summarize_profiles(args.summarize_profiles, args.profile_set)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -528,7 +542,10 @@ def main():
     if args.probe == "copy":
         copy_probe(args.probe_bytes, args.steps, args.warmup)
         return
-    binding.load_library()
+    if args.library:
+        binding.use_library(os.path.join(ROOT, args.library))
+    else:
+        binding.load_library()
 
     engines = {}
     if args.layers < 1:
@@ -645,32 +662,67 @@ def copy_probe(nbytes, steps, warmup):
 PROFILED = ["llama1b_ctx3060_f16", "llama8b_b16_ragged_f16", "d256_window4096_bf16",
             "ctx100k_gqa6_f16", "llama8b_ctx32k_rope_f16", "ctx100k_gqa6_rope_f16"]
 COPY_BYTES = 256 << 20
+# Counter passes of every profiled workload (one rocprofv3 --pmc run each; at
+# most 8 SQ and 4 TCC counters per run).
+PMC_SETS = {
+    "FETCH_SIZE": ["FETCH_SIZE"],
+    "WRITE_SIZE": ["WRITE_SIZE"],
+    "sqA": ["SQ_WAVES", "SQ_INSTS", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+            "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SMEM", "TCC_HIT", "TCC_MISS"],
+    "sqB": ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY",
+            "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_VALU",
+            "SQ_LDS_IDX_ACTIVE"],
+}
+# q.k on the matrix cores (the library) against the vector ALUs (the
+# comparison build python -m paged_kv_decode_amd.build --variant qk_valu).
+AB_WORKLOADS = ["llama1b_ctx3060_f16", "ctx100k_gqa6_f16", "llama8b_b16_ragged_f16",
+                "d256_window4096_bf16"]
+AB_LIBS = {"mfma": None, "valu": "paged_kv_decode_amd/libpa_decode_qk_valu.so"}
 
 
-def profile_commands(outdir):
-    """(name, command) of every run behind profiles/: per workload a plain
-    benchmark run (its stdout goes to <outdir>/<name>.log) and a kernel trace,
-    then the FETCH_SIZE and WRITE_SIZE passes and their copy calibration.
+def _run(w, steps, lib=None, eager=False, warmup=20):
+    b = "/root/repo/bench.py"
+    return ("python3 %s --workload %s --also '' --cpu-budget 0 --steps %d --warmup %d "
+            "--phases cold --cold-calls 0%s%s" % (b, w, steps, warmup,
+                                                  " --mode eager" if eager else "",
+                                                  " --library %s" % lib if lib else ""))
+
+
+def profile_commands(outdir, which="main"):
+    """(name, command) of every run behind profiles/.  which="main": per
+    workload a plain benchmark run (its stdout goes to <outdir>/<name>.log),
+    a kernel trace and one counter run per PMC_SETS entry, then the copy
+    calibration of FETCH_SIZE / WRITE_SIZE.  which="ab": per AB_WORKLOADS
+    entry and library (AB_LIBS) a plain run and the two SQ counter passes.
     The rocprofv3 commands run from /tmp with TMPDIR=/tmp."""
     b = "/root/repo/bench.py"
     cmds = []
+    if which == "ab":
+        for w in AB_WORKLOADS:
+            for lib_name, lib in AB_LIBS.items():
+                steps = 2000 if w == "llama1b_ctx3060_f16" else 300
+                cmds.append(("ab_bench_%s_%s" % (lib_name, w), _run(w, steps, lib)))
+                for c in ("sqA", "sqB"):
+                    cmds.append(("ab_pmc_%s_%s_%s" % (lib_name, w, c),
+                                 "rocprofv3 --pmc %s --output-format csv -d %s/ab_pmc_%s_%s_%s -o %s -- %s"
+                                 % (" ".join(PMC_SETS[c]), outdir, lib_name, w, c, w,
+                                    _run(w, 20, lib, eager=True, warmup=2))))
+        return cmds
     for w in PROFILED:
         steps = 2000 if w == "llama1b_ctx3060_f16" else 300
-        run = ("python3 %s --workload %s --also '' --cpu-budget 0 --steps %d --warmup 20 "
-               "--phases cold --cold-calls 0" % (b, w, steps))
+        run = _run(w, steps)
         cmds.append(("bench_%s" % w, run))
         cmds.append(("trace_%s" % w, "rocprofv3 --kernel-trace --stats --output-format csv -d %s/trace_%s "
                                      "-o %s -- %s" % (outdir, w, w, run)))
-    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+    for c, names in PMC_SETS.items():
         for w in PROFILED:
             cmds.append(("pmc_%s_%s" % (w, c),
-                         "rocprofv3 --pmc %s --output-format csv -d %s/pmc_%s_%s -o %s -- python3 %s "
-                         "--workload %s --also '' --cpu-budget 0 --steps 20 --warmup 2 --mode eager "
-                         "--phases cold --cold-calls 0"
-                         % (c, outdir, w, c, w, b, w)))
-        cmds.append(("pmc_copy_%s" % c,
-                     "rocprofv3 --pmc %s --output-format csv -d %s/pmc_copy_%s -o copy -- python3 %s "
-                     "--probe copy --probe-bytes %d --steps 10 --warmup 2" % (c, outdir, c, b, COPY_BYTES)))
+                         "rocprofv3 --pmc %s --output-format csv -d %s/pmc_%s_%s -o %s -- %s"
+                         % (" ".join(names), outdir, w, c, w, _run(w, 20, eager=True, warmup=2))))
+        if c in ("FETCH_SIZE", "WRITE_SIZE"):
+            cmds.append(("pmc_copy_%s" % c,
+                         "rocprofv3 --pmc %s --output-format csv -d %s/pmc_copy_%s -o copy -- python3 %s "
+                         "--probe copy --probe-bytes %d --steps 10 --warmup 2" % (c, outdir, c, b, COPY_BYTES)))
     return cmds
 
 
@@ -692,11 +744,85 @@ def _short(name):
     return None
 
 
-def summarize_profiles(indir):
+def _pmc_medians(path, names):
+    """{(kernel family, counter): median per-dispatch value} of one counter
+    run (rocprofv3 sums a counter over its instances in each dispatch)."""
+    import statistics
+    rows = _csv_rows(path)
+    out = {}
+    for k in ("partial_kernel", "merge_kernel"):
+        for c in names:
+            v = [float(r["Counter_Value"]) for r in rows
+                 if _short(r["Kernel_Name"]) == k and r["Counter_Name"] == c]
+            if v:
+                out[(k, c)] = statistics.median(v)
+    return out
+
+
+def sq_summary(m, kernel="partial_kernel"):
+    """Per-wave instruction mix and cycle figures of one kernel from the sqA /
+    sqB medians (None when the counters are missing).  SQ_WAVE_CYCLES,
+    SQ_WAIT_* and SQ_ACTIVE_INST_VALU count quad-cycles."""
+    g = lambda c: m.get((kernel, c))  # noqa: E731
+    waves = g("SQ_WAVES")
+    if not waves:
+        return None
+    r = {"waves": int(waves)}
+    for c, key in (("SQ_INSTS", "insts"), ("SQ_INSTS_VALU", "valu"), ("SQ_INSTS_MFMA", "mfma"),
+                   ("SQ_INSTS_LDS", "lds"), ("SQ_INSTS_SALU", "salu"),
+                   ("SQ_INSTS_VMEM_RD", "vmem_rd"), ("SQ_INSTS_SMEM", "smem")):
+        if g(c) is not None:
+            r[key + "_per_wave"] = round(g(c) / waves, 1)
+    if g("TCC_HIT") is not None and g("TCC_MISS") is not None:
+        tot = g("TCC_HIT") + g("TCC_MISS")
+        r["l2_hit_rate"] = round(g("TCC_HIT") / tot, 4) if tot else None
+    wc = g("SQ_WAVE_CYCLES")
+    if wc:
+        r["wave_cycles_per_wave"] = round(4 * wc / waves, 0)
+        for c, key in (("SQ_WAIT_INST_ANY", "wait_inst_frac"), ("SQ_WAIT_ANY", "wait_any_frac"),
+                       ("SQ_ACTIVE_INST_VALU", "valu_active_frac")):
+            if g(c) is not None:
+                r[key] = round(g(c) / wc, 4)
+    if g("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+        r["mfma_busy_cycles"] = int(g("SQ_VALU_MFMA_BUSY_CYCLES"))
+    if g("SQ_BUSY_CYCLES") is not None:
+        r["busy_cycles"] = int(g("SQ_BUSY_CYCLES"))
+    if g("SQ_LDS_IDX_ACTIVE"):
+        r["lds_bank_conflict_frac"] = round((g("SQ_LDS_BANK_CONFLICT") or 0) / g("SQ_LDS_IDX_ACTIVE"), 4)
+    return r
+
+
+SQ_ROWS = [("waves", "waves"), ("insts_per_wave", "instructions / wave"),
+           ("valu_per_wave", "VALU / wave"), ("mfma_per_wave", "MFMA / wave"),
+           ("lds_per_wave", "LDS / wave"), ("salu_per_wave", "SALU / wave"),
+           ("vmem_rd_per_wave", "vector memory reads / wave"), ("smem_per_wave", "scalar memory / wave"),
+           ("l2_hit_rate", "L2 hit rate (TCC_HIT / (HIT + MISS))"),
+           ("wave_cycles_per_wave", "cycles / wave (SQ_WAVE_CYCLES x 4 / waves)"),
+           ("wait_any_frac", "waiting on anything / wave cycles"),
+           ("wait_inst_frac", "waiting for issue / wave cycles"),
+           ("valu_active_frac", "VALU active / wave cycles"),
+           ("mfma_busy_cycles", "MFMA busy cycles (SQ_VALU_MFMA_BUSY_CYCLES)"),
+           ("busy_cycles", "SQ busy cycles"),
+           ("lds_bank_conflict_frac", "LDS bank-conflict cycles / LDS active cycles")]
+
+
+def _bench_line(path):
+    line = None
+    if os.path.exists(path):
+        for ln in open(path):
+            if ln.startswith("{"):
+                line = json.loads(ln)
+    return line
+
+
+def summarize_profiles(indir, which="main"):
     """Writes profiles/<kernel>_<workload>.md and profiles/traffic.json from the
-    output of profile_commands(indir)."""
+    output of profile_commands(indir) (which="ab": profiles/qk_mfma_vs_valu.md)."""
     import statistics
     prof = os.path.join(ROOT, "profiles")
+    named = dict(profile_commands(indir, which))
+    if which == "ab":
+        return summarize_ab(indir, named)
     counters = {}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         rows = _csv_rows(os.path.join(indir, "pmc_copy_%s" % c, "copy_counter_collection.csv"))
@@ -705,7 +831,6 @@ def summarize_profiles(indir):
         counters[c] = statistics.median(vals)
     fetch_scale = COPY_BYTES / 1024.0 / counters["FETCH_SIZE"]
     write_scale = COPY_BYTES / 1024.0 / counters["WRITE_SIZE"]
-    named = dict(profile_commands(indir))
     traffic = {"kernel_hash": kernel_hash(), "kernel_sources": KERNEL_SOURCES,
                "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
                "calibration": "plain %d KiB device copy (__amd_rocclr_copyBuffer): FETCH_SIZE "
@@ -719,25 +844,18 @@ def summarize_profiles(indir):
         kv = p.kv_bytes()
         stats = {_short(r["Name"]): r for r in
                  _csv_rows(os.path.join(indir, "trace_%s" % w, "%s_kernel_stats.csv" % w))}
-        line = None
-        logp = os.path.join(indir, "bench_%s.log" % w)
-        if os.path.exists(logp):
-            for ln in open(logp):
-                if ln.startswith("{"):
-                    line = json.loads(ln)
+        line = _bench_line(os.path.join(indir, "bench_%s.log" % w))
         pmc = {}
-        for c in ("FETCH_SIZE", "WRITE_SIZE"):
-            rows = _csv_rows(os.path.join(indir, "pmc_%s_%s" % (w, c), "%s_counter_collection.csv" % w))
-            for k in ("partial_kernel", "merge_kernel"):
-                v = [float(r["Counter_Value"]) for r in rows
-                     if _short(r["Kernel_Name"]) == k and r["Counter_Name"] == c]
-                if v:
-                    pmc[(k, c)] = statistics.median(v)
+        for c, names in PMC_SETS.items():
+            path = os.path.join(indir, "pmc_%s_%s" % (w, c), "%s_counter_collection.csv" % w)
+            if os.path.exists(path):
+                pmc.update(_pmc_medians(path, names))
         fb = int(round(pmc[("partial_kernel", "FETCH_SIZE")] * 1024 * fetch_scale))
         wb = int(round(pmc[("partial_kernel", "WRITE_SIZE")] * 1024 * write_scale))
+        sq = {k: sq_summary(pmc, k) for k in ("partial_kernel", "merge_kernel")}
         e = {"kernel": "partial_kernel", "fetch_bytes": fb, "write_bytes": wb,
              "bytes_per_launch": fb + wb, "algorithmic_kv_bytes": kv,
-             "fetch_over_algorithmic": round(fb / kv, 4)}
+             "fetch_over_algorithmic": round(fb / kv, 4), "sq": sq}
         if ("merge_kernel", "FETCH_SIZE") in pmc:
             e["merge_kernel_fetch_bytes"] = int(round(pmc[("merge_kernel", "FETCH_SIZE")] * 1024 * fetch_scale))
             e["merge_kernel_write_bytes"] = int(round(pmc[("merge_kernel", "WRITE_SIZE")] * 1024 * write_scale))
@@ -746,7 +864,8 @@ def summarize_profiles(indir):
         part = stats["partial_kernel"]
         avg_us = float(part["AverageNs"]) / 1e3
         out = ["# %s -- partial and merge kernels on MI355X (gfx950)" % w, "",
-               "Kernel trace (rocprofv3 --kernel-trace --stats), run from /tmp with TMPDIR=/tmp:",
+               "Kernel trace (rocprofv3 --kernel-trace --stats), run from /tmp with TMPDIR=/tmp "
+               "(cold launches only: --phases cold):",
                "  " + named["trace_%s" % w], "",
                "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
         for k in ("partial_kernel", "merge_kernel"):
@@ -781,14 +900,66 @@ def summarize_profiles(indir):
                 out.append("| %s | %.1f | %d | %.1f | %d |" % (
                     k, pmc[(k, "FETCH_SIZE")], round(pmc[(k, "FETCH_SIZE")] * 1024 * fetch_scale),
                     pmc[(k, "WRITE_SIZE")], round(pmc[(k, "WRITE_SIZE")] * 1024 * write_scale)))
-        out += ["", "partial kernel fetched / algorithmic KV bytes = %.4f" % (fb / kv),
-                "kernel sources hash (bench.kernel_hash): %s" % kernel_hash(), ""]
+        out += ["", "partial kernel fetched / algorithmic KV bytes = %.4f" % (fb / kv)]
+        if sq["partial_kernel"]:
+            out += ["", "SQ / TCC counters (two --pmc runs, median per dispatch):",
+                    "  " + named["pmc_%s_sqA" % w], "  " + named["pmc_%s_sqB" % w], "",
+                    "| figure | partial kernel | merge kernel |", "|---|---|---|"]
+            for key, label in SQ_ROWS:
+                vals = [sq[k].get(key) if sq[k] else None for k in ("partial_kernel", "merge_kernel")]
+                if vals[0] is not None:
+                    out.append("| %s | %s | %s |" % (label, vals[0], "-" if vals[1] is None else vals[1]))
+        out += ["", "kernel sources hash (bench.kernel_hash): %s" % kernel_hash(), ""]
         with open(os.path.join(prof, "partial_kernel_%s.md" % w), "w") as f:
             f.write("\n".join(out))
     with open(os.path.join(prof, "traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
         f.write("\n")
     print("wrote profiles/ for %s (kernel hash %s)" % (", ".join(PROFILED), kernel_hash()))
+
+
+def summarize_ab(indir, named):
+    """profiles/qk_mfma_vs_valu.md: per workload, step and partial-kernel time
+    and the SQ figures of q.k on the matrix cores against the vector ALUs."""
+    out = ["# q.k on the matrix cores against the vector ALUs (MI355X, gfx950)", "",
+           "mfma: the library (the score MFMA, the K page tile as A and the GQA group's query "
+           "rows as B).  valu: the comparison build `python -m paged_kv_decode_amd.build "
+           "--variant qk_valu` (lane (token, chunk group) forms packed f16/bf16 dot products "
+           "of its key row's chunks with every query row, the four chunk groups summed by lane "
+           "swaps, the scores passed through a per-wave LDS buffer into the P.V operand "
+           "layout).  Everything else is the same kernel; P.V is on the matrix cores in both.",
+           "", "Commands (run from /tmp with TMPDIR=/tmp):"]
+    out += ["  " + c for n, c in named.items()]
+    rows = []
+    res = {}
+    for w in AB_WORKLOADS:
+        for lib_name in AB_LIBS:
+            line = _bench_line(os.path.join(indir, "ab_bench_%s_%s.log" % (lib_name, w)))
+            pmc = {}
+            for c in ("sqA", "sqB"):
+                path = os.path.join(indir, "ab_pmc_%s_%s_%s" % (lib_name, w, c),
+                                    "%s_counter_collection.csv" % w)
+                if os.path.exists(path):
+                    pmc.update(_pmc_medians(path, PMC_SETS[c]))
+            res[(w, lib_name)] = (line, sq_summary(pmc))
+    out += ["", "| workload | q.k on | us / step | partial us (events) | partial % of 8 TB/s | "
+                "instructions / wave | VALU / wave | MFMA / wave | LDS / wave | cycles / wave | "
+                "VALU active | waiting |", "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for w in AB_WORKLOADS:
+        for lib_name in AB_LIBS:
+            line, sq = res[(w, lib_name)]
+            if not line:
+                continue
+            sq = sq or {}
+            out.append("| %s | %s | %.2f | %.2f | %.1f | %s | %s | %s | %s | %s | %s | %s |" % (
+                w, lib_name, line["us_per_step"], line["roofline"]["kernel_us"],
+                100 * line["roofline"]["frac"], sq.get("insts_per_wave"), sq.get("valu_per_wave"),
+                sq.get("mfma_per_wave"), sq.get("lds_per_wave"), sq.get("wave_cycles_per_wave"),
+                sq.get("valu_active_frac"), sq.get("wait_any_frac")))
+    out += ["", "kernel sources hash (bench.kernel_hash): %s" % kernel_hash(), ""]
+    with open(os.path.join(ROOT, "profiles", "qk_mfma_vs_valu.md"), "w") as f:
+        f.write("\n".join(out))
+    print("wrote profiles/qk_mfma_vs_valu.md")
 
 
 def p_lens(p):

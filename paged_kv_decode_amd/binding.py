@@ -156,6 +156,16 @@ def load_library(path: Optional[str] = None):
         return lib
 
 
+def use_library(path: str):
+    """Load the library at `path` (a comparison build, for measurement) and
+    make it the one every call of this module uses."""
+    global _lib
+    lib = load_library(path)
+    with _lock:
+        _lib = lib
+    return lib
+
+
 def _check(status: int, what: str):
     if status != PA_DECODE_OK:
         raise PaDecodeError(status, what)

@@ -41,15 +41,28 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+# Comparison builds (measurement only, never loaded by the package itself):
+# name -> (library file, extra defines).  qk_valu: the scores on the vector
+# ALUs (packed dot products, lane-swap sums) instead of the score MFMA.
+VARIANTS = {"qk_valu": ("libpa_decode_qk_valu.so", ["-DPA_QK_VALU=1"])}
+
+
+def build(verbose: bool = False, variant: str = None) -> str:
     """Compile the library (always recompiles) and return its path.
 
     Each source compiles to an object in its own hipcc process (all at
-    once: the two kernel translation units dominate), then one link."""
-    tag = ".tmp%d" % os.getpid()
+    once: the two kernel translation units dominate), then one link.
+    variant: a key of VARIANTS, for a comparison build written next to the
+    library under its own name."""
+    lib_path = LIB_PATH
+    extra = []
+    if variant is not None:
+        name, extra = VARIANTS[variant]
+        lib_path = os.path.join(HERE, name)
+    tag = ".tmp%d" % os.getpid() + ("." + variant if variant else "")
     objs = [os.path.join(tempfile.gettempdir(), os.path.basename(src) + tag + ".o")
             for src in SOURCES]
-    cmds = [[HIPCC] + FLAGS + ["-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+    cmds = [[HIPCC] + FLAGS + extra + ["-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
     try:
         procs = []
         for cmd in cmds:
@@ -65,7 +78,7 @@ def build(verbose: bool = False) -> str:
                 failed = True
         if failed:
             raise RuntimeError("hipcc failed building libpa_decode.so")
-        tmp = LIB_PATH + tag
+        tmp = lib_path + tag
         link = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]
         if verbose:
             print(" ".join(link), flush=True)
@@ -73,13 +86,17 @@ def build(verbose: bool = False) -> str:
         if res.returncode != 0:
             sys.stderr.write(res.stdout + res.stderr)
             raise RuntimeError("hipcc failed linking libpa_decode.so")
-        os.replace(tmp, LIB_PATH)
+        os.replace(tmp, lib_path)
     finally:
         for obj in objs:
             if os.path.exists(obj):
                 os.remove(obj)
-    return LIB_PATH
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser(description="build libpa_decode.so for gfx950")
+    ap.add_argument("--variant", choices=sorted(VARIANTS), default=None,
+                    help="a comparison build (measurement only)")
+    print(build(verbose=True, variant=ap.parse_args().variant))

@@ -448,6 +448,53 @@ template <> struct PV<PA_DTYPE_BF16> {
     }
 };
 
+// ---- q.k on the vector ALUs (comparison build only) ----
+// A library built with PA_QK_VALU=1 forms the scores with packed dot
+// products instead of the score MFMA, for measuring one against the other;
+// the shipped library uses the MFMA.
+#ifndef PA_QK_VALU
+#define PA_QK_VALU 0
+#endif
+
+// Dot product of two 16-byte chunks (8 f16 / 8 bf16 / 4 f32 elements),
+// accumulated in f32.  Each 32-bit element is copied to a scalar before the
+// bit cast: hipcc (ROCm 7.2) compiles __builtin_bit_cast of a vector element
+// expression, v[j], as a cast of element 0 for every j.
+template <int DT> struct Dot;
+template <> struct Dot<PA_DTYPE_F16> {
+    __device__ static float dot(u32x4 a, u32x4 b, float c)
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t x = a[j], y = b[j];
+            c = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, y), c,
+                                       false);
+        }
+        return c;
+    }
+};
+template <> struct Dot<PA_DTYPE_BF16> {
+    __device__ static float dot(u32x4 a, u32x4 b, float c)
+    {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t x = a[j], y = b[j];
+            c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, x), __builtin_bit_cast(b2, y), c,
+                                                false);
+        }
+        return c;
+    }
+};
+template <> struct Dot<PA_DTYPE_F32> {
+    __device__ static float dot(u32x4 a, u32x4 b, float c)
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c = __builtin_fmaf(__uint_as_float(a[j]), __uint_as_float(b[j]), c);
+        return c;
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Partial kernel.
 //   DT: element type; D: head_dim; G: instantiated group size (>= actual);
@@ -499,7 +546,14 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
     constexpr int KT = NB * kPage * CHP;  // 16-byte slots of one block's K (or V) tile
     constexpr int HD = D / 2;         // rotary frequencies
     constexpr int NE = ROT ? (NB * HD + kWave - 1) / kWave : 1;  // base-table entries per lane
-    constexpr int WS = 8 * KT + (ROT ? NB * D : 0);  // floats of LDS per wave
+    // Comparison build (PA_QK_VALU): scores on the vector ALUs; q in VGPRs
+    // when G x KS chunks fit in 96 VGPRs, else in a per-wave LDS copy; the
+    // scores pass through a per-wave [NB][16][16] LDS buffer on their way to
+    // the P.V operand layout.
+    constexpr bool QKV = PA_QK_VALU != 0 && !ROT;
+    constexpr bool QREG = QKV && G * KS <= 24;
+    constexpr int QW = QKV ? (QREG ? 0 : G * CH * 4) + NB * 256 : 0;   // floats
+    constexpr int WS = 8 * KT + (ROT ? NB * D : 0) + QW;  // floats of LDS per wave
     static_assert(KS * 4 == CH && KS * kWave == kPage * CH, "lane map");
     static_assert(CH == 8 || CH == 12 || CH == 16 || CH == 32, "tiles");
     static_assert(G <= 16, "one 16-row MFMA block of query heads");
@@ -765,7 +819,7 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         // q as the MFMA B operand, held in VGPRs: column i16 = query head
         // kvh*G + i16 (zero past G), chunk 4*ks + grp of head_dim.
         u32x4 qa[KS];
-        {
+        if constexpr (!QKV) {
             const bool real = i16 < Gact;
             const char* qrow = static_cast<const char*>(prm.q) +
                                (size_t(b) * prm.num_q_heads + size_t(kvh) * Gact + (real ? i16 : 0)) * D * EB;
@@ -773,6 +827,29 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
             for (int ks = 0; ks < KS; ++ks) {
                 u32x4 z = {0u, 0u, 0u, 0u};
                 qa[ks] = real ? load16(qrow + (4 * ks + grp) * 16) : z;
+            }
+        }
+        // Comparison build: lane (token i16, group grp) takes chunks 4 ks +
+        // grp of every query row of the group (zero rows past G).
+        [[maybe_unused]] u32x4 qv[QREG ? G : 1][QREG ? KS : 1];
+        [[maybe_unused]] u32x4* qcopy =
+            reinterpret_cast<u32x4*>(smem + wave * WS + 8 * KT + (ROT ? NB * D : 0));
+        [[maybe_unused]] float* sbuf =
+            smem + wave * WS + 8 * KT + (ROT ? NB * D : 0) + (QREG ? 0 : G * CH * 4);
+        if constexpr (QKV) {
+            const char* q0 = static_cast<const char*>(prm.q) +
+                             (size_t(b) * prm.num_q_heads + size_t(kvh) * Gact) * D * EB;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            if constexpr (QREG) {
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        qv[g][ks] = g < Gact ? load16(q0 + (size_t(g) * CH + 4 * ks + grp) * 16) : z;
+            } else {
+                for (int x = lane; x < G * CH; x += kWave)
+                    qcopy[x] = x / CH < Gact ? load16(q0 + size_t(x) * 16) : z;
+                wave_lds_sync();
             }
         }
 
@@ -1004,6 +1081,34 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
                     // VGPRs while they are formed.
                     pin_loads();
                     d = turned_scores(nb);
+                } else if constexpr (QKV) {
+                    // Lane (token i16, group grp): partial dots of its key row's
+                    // chunks 4 ks + grp with every query row, summed over the four
+                    // groups by lane swaps, then written [head][token] and read back
+                    // as (head i16, tokens 4 grp .. 4 grp + 3).
+                    float part[G];
+#pragma unroll
+                    for (int g = 0; g < G; ++g) part[g] = 0.f;
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const u32x4 kc = ktile[tix(nb * kPage + i16, 4 * ks + grp)];
+#pragma unroll
+                        for (int g = 0; g < G; ++g) {
+                            u32x4 qc;
+                            if constexpr (QREG) qc = qv[g][ks];
+                            else qc = qcopy[g * CH + 4 * ks + grp];
+                            part[g] = Dot<DT>::dot(kc, qc, part[g]);
+                        }
+                    }
+                    float* sb = sbuf + nb * 256;
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        part[g] = rows4_sum(part[g]);
+                        if (grp == 0) sb[g * 16 + i16] = part[g];
+                    }
+                    wave_lds_sync();
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    d = i16 < G ? *reinterpret_cast<const f32x4*>(sb + i16 * 16 + 4 * grp) : z;
                 } else {
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks)

@@ -400,6 +400,16 @@ size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan)
         size_t(nw) * (2 * ktile + size_t(rotary_table_bytes(d)) / sizeof(float)) +
         size_t(rotary_offset_table_bytes(d)) / sizeof(float);
     const size_t comb = size_t(nw) * size_t(2 * gp4 + G * d.head_dim);
+#if PA_QK_VALU
+    // Comparison build (scores on the vector ALUs): per wave a q copy when G
+    // x (chunks / 4) > 24, and [pages per block][16][16] score floats.
+    if (d.rotary_mode == 0) {
+        const int ch = d.head_dim * dtype_bytes(d.dtype) / 16;
+        const size_t extra = (G * (ch / 4) <= 24 ? 0 : size_t(G) * ch * 4) +
+                             size_t(plan.pages_per_block) * 256;
+        return std::max(loop + size_t(nw) * extra, comb) * sizeof(float);
+    }
+#endif
     return std::max(loop, comb) * sizeof(float);
 }
 
