@@ -806,6 +806,26 @@ SQ_ROWS = [("waves", "waves"), ("insts_per_wave", "instructions / wave"),
            ("lds_bank_conflict_frac", "LDS bank-conflict cycles / LDS active cycles")]
 
 
+def trace_phases(path, steps, warm=20):
+    """Mean partial-kernel duration per phase of a --phases cold benchmark run
+    from its rocprofv3 kernel trace: the two replica checks and the warm-up,
+    the graph upload replay, the graph timed replay and the eager timing pass
+    (in launch order); None when the trace does not have that shape."""
+    import statistics
+    if not os.path.exists(path):
+        return None
+    rows = [r for r in _csv_rows(path) if _short(r["Kernel_Name"]) == "partial_kernel"]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    pre = 2 + warm
+    if len(d) != pre + 3 * steps:
+        return None
+    segs = [("checks and warm-up", d[:pre]), ("graph upload replay", d[pre:pre + steps]),
+            ("graph timed replay", d[pre + steps:pre + 2 * steps]),
+            ("eager timing pass", d[pre + 2 * steps:])]
+    return {k: (len(v), statistics.mean(v)) for k, v in segs}
+
+
 def _bench_line(path):
     line = None
     if os.path.exists(path):
@@ -877,6 +897,19 @@ def summarize_profiles(indir, which="main"):
         out += ["", "Algorithmic KV bytes per launch: %d; at the trace's average partial-kernel "
                     "duration that is %.1f GB/s (%.1f%% of 8 TB/s)." % (kv, kv / avg_us / 1e3,
                                                                         kv / avg_us / 1e3 / PEAK_GBPS * 100)]
+        phases = trace_phases(os.path.join(indir, "trace_%s" % w, "%s_kernel_trace.csv" % w),
+                              2000 if w == "llama1b_ctx3060_f16" else 300)
+        if phases:
+            out += ["", "Partial-kernel dispatches of the traced run by phase (trace timestamps, "
+                        "mean us): %s." % ", ".join("%s %d x %.3f" % (k, n, v) for k, (n, v) in phases.items())]
+            if line:
+                ev = line["roofline"]["kernel_us"]
+                out += ["The benchmark's HIP events bracket the eager launches: %.3f us against the "
+                        "trace's %.3f us for that phase (ratio %.3f); graph-replayed launches (the "
+                        "timed region) run at %.3f us, so the event figure is %.1f%% conservative."
+                        % (ev, phases["eager timing pass"][1], ev / phases["eager timing pass"][1],
+                           phases["graph timed replay"][1],
+                           100 * (ev / phases["graph timed replay"][1] - 1))]
         if line:
             ro = line["roofline"]
             out += ["", "The same benchmark without the profiler (HIP events around each launch):",
