@@ -509,9 +509,11 @@ def main():
                          "builds, e.g. python -m paged_kv_decode_amd.build --variant qk_valu)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
-    ap.add_argument("--probe", choices=["copy"], default=None,
-                    help="calibration only: time a plain device copy of --probe-bytes "
-                         "(the reference kernel for the HBM traffic counters)")
+    ap.add_argument("--probe", choices=["copy", "read-sweep"], default=None,
+                    help="copy: time a plain device copy of --probe-bytes (the reference kernel "
+                         "for the HBM traffic counters); read-sweep: the read probe's time "
+                         "against size, contiguous and gathered, cold (the fixed cost and the "
+                         "streaming rate of a kernel that only reads)")
     ap.add_argument("--probe-bytes", type=int, default=256 << 20)
     ap.add_argument("--profile-commands", metavar="DIR", default=None,
                     help="print the rocprofv3 commands whose output --summarize-profiles reads")
@@ -541,6 +543,10 @@ def main():
     torch.cuda.set_device(0)
     if args.probe == "copy":
         copy_probe(args.probe_bytes, args.steps, args.warmup)
+        return
+    if args.probe == "read-sweep":
+        binding.load_library()
+        read_sweep()
         return
     if args.library:
         binding.use_library(os.path.join(ROOT, args.library))
@@ -633,6 +639,72 @@ def main():
         "also": also,
     }
     print(json.dumps(line), flush=True)
+
+
+def read_sweep(launches=50):
+    """Time pa_decode_read_probe reading N bytes per launch, N from 4 MiB to
+    1 GiB, as 8 KiB chunks that are contiguous or gathered at random from a
+    pool, each launch on bytes no launch touched for >= 4 x CACHE_BYTES
+    (rotation over a 6 GiB pool; a flush before each timed graph), graph-
+    replayed; prints one JSON line per (layout, size) and a least-squares fit
+    t = fixed + bytes / rate over the sizes from 64 MiB."""
+    pool_bytes = 6 << 30
+    pool = torch.ones(pool_bytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    flush = Flusher()
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(77)
+    chunk = 8192
+    nchunks_pool = pool_bytes // chunk
+    fits = {}
+    for layout in ("contiguous", "gathered"):
+        pts = []
+        for mib in (4, 8, 16, 32, 64, 128, 256, 512, 1024):
+            n = (mib << 20) // chunk
+            # launches over disjoint ranges of the pool, in rotation, enough
+            # of them that a range is read again only after 4 x CACHE_BYTES
+            L = max(launches, -(-4 * CACHE_BYTES // (n * chunk)) + 1)
+            per = max(1, min(L, nchunks_pool // n))
+            if layout == "gathered":
+                perm = torch.randperm(nchunks_pool, generator=gen)[: per * n]
+                addrs = (pool.data_ptr() + perm.to(torch.int64) * chunk).to("cuda")
+            else:
+                addrs = (pool.data_ptr() + torch.arange(per * n, dtype=torch.int64) * chunk).to("cuda")
+            g = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(stream)
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(g, stream=cap):
+                    cs = torch.cuda.current_stream().cuda_stream
+                    for i in range(L):
+                        binding.pa_decode_read_probe(0, addrs[(i % per) * n:].data_ptr(), n, chunk,
+                                                     sink.data_ptr(), cs)
+            stream.wait_stream(cap)
+            g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            flush()
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = 1e3 * a.elapsed_time(b) / L
+            cold = per * n * chunk - n * chunk >= 4 * CACHE_BYTES
+            pts.append((n * chunk, us))
+            print(json.dumps({"probe": "read-sweep", "layout": layout, "bytes": n * chunk,
+                              "us_per_launch": round(us, 3),
+                              "GBps": round(n * chunk / (us * 1e-6) / 1e9, 1),
+                              "frac_of_8TBps": round(n * chunk / (us * 1e-6) / 1e9 / PEAK_GBPS, 4),
+                              "rotation_launches": per, "cold": bool(cold)}), flush=True)
+            del g
+        big = [(x, y) for x, y in pts if x >= (64 << 20)]
+        xs = np.array([x for x, _ in big], dtype=np.float64)
+        ys = np.array([y for _, y in big], dtype=np.float64)
+        A = np.stack([np.ones_like(xs), xs], 1)
+        (c0, c1), *_ = np.linalg.lstsq(A, ys, rcond=None)
+        fits[layout] = {"fixed_us": round(float(c0), 3), "rate_GBps": round(1e-3 / float(c1), 1)}
+    print(json.dumps({"probe": "read-sweep-fit", "fit_from_bytes": 64 << 20, **fits}), flush=True)
 
 
 def copy_probe(nbytes, steps, warmup):
