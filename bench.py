@@ -509,7 +509,7 @@ def main():
                          "builds, e.g. python -m paged_kv_decode_amd.build --variant qk_valu)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
-    ap.add_argument("--probe", choices=["copy", "read-sweep"], default=None,
+    ap.add_argument("--probe", choices=["copy", "read-sweep", "schedule-sweep"], default=None,
                     help="copy: time a plain device copy of --probe-bytes (the reference kernel "
                          "for the HBM traffic counters); read-sweep: the read probe's time "
                          "against size, contiguous and gathered, cold (the fixed cost and the "
@@ -547,6 +547,10 @@ def main():
     if args.probe == "read-sweep":
         binding.load_library()
         read_sweep()
+        return
+    if args.probe == "schedule-sweep":
+        binding.load_library()
+        schedule_sweep()
         return
     if args.library:
         binding.use_library(os.path.join(ROOT, args.library))
@@ -705,6 +709,80 @@ def read_sweep(launches=50):
         (c0, c1), *_ = np.linalg.lstsq(A, ys, rcond=None)
         fits[layout] = {"fixed_us": round(float(c0), 3), "rate_GBps": round(1e-3 / float(c1), 1)}
     print(json.dumps({"probe": "read-sweep-fit", "fit_from_bytes": 64 << 20, **fits}), flush=True)
+
+
+def schedule_sweep(steps=200):
+    """Fixed partitions (partition_size 0) against the length-balanced
+    schedule (PA_DECODE_PARTITION_BALANCED) on Llama-3.1-8B-shaped batches
+    (Hq 32 / Hkv 8, head_dim 128, f16; the first sequence 4096 tokens) of 4,
+    8, 16 and 32 sequences with four length mixes (uniform in [1, 4096],
+    uniform in [2048, 4096], mostly short (u^3 scaled), all 300), plus the
+    batch-16 ragged workload's own lengths, without and with rotary: µs per
+    graph-replayed step with cold caches (replica rotation, a flush before
+    the timed replay), median of three replays; one JSON line per case with
+    the mean / longest page ratio the CSR host rule looks at."""
+    flush = Flusher()
+    stream = torch.cuda.current_stream()
+    c3 = W.generate(W.CONFIGS["llama8b_b16_ragged_f16"]).context_lens.tolist()
+    for rope in (None, (500000.0, 1.0)):
+        eng = binding.PagedDecode(32, 8, 128, torch.float16, max_batch=64,
+                                  max_context_len=1 << 20, rope=rope)
+        gen = torch.Generator().manual_seed(11)
+        cases = []
+        for B in (4, 8, 16, 32):
+            for kind in ("uniform", "upper_half", "mostly_short", "one_long"):
+                if kind == "uniform":
+                    lens = torch.randint(1, 4097, (B,), generator=gen).tolist()
+                elif kind == "upper_half":
+                    lens = torch.randint(2048, 4097, (B,), generator=gen).tolist()
+                elif kind == "mostly_short":
+                    lens = [int(x) for x in (torch.rand(B, generator=gen) ** 3 * 4095 + 1).tolist()]
+                else:
+                    lens = [300] * B
+                lens[0] = 4096
+                cases.append((B, kind, lens))
+        cases.append((16, "batch16_ragged_workload", c3))
+        for B, kind, lens in cases:
+            w = W.custom(name="schedule_sweep", batch=B, num_q_heads=32, num_kv_heads=8,
+                         head_dim=128, dtype=torch.float16, context_lens=lens,
+                         seed=B * 7 + len(kind), rope=rope)
+            p = W.generate(w)
+            res = {}
+            for label, S in (("fixed_us", 0), ("balanced_us", binding.PA_DECODE_PARTITION_BALANCED)):
+                R = min(24, replica_count(p.kv_bytes(),
+                                          2 * p.k_cache.numel() * p.k_cache.element_size()))
+                reps = Replicas(p, R, eng, S)
+                g = torch.cuda.CUDAGraph()
+                cap = torch.cuda.Stream()
+                cap.wait_stream(stream)
+                with torch.cuda.stream(cap):
+                    with torch.cuda.graph(g, stream=cap):
+                        cs = torch.cuda.current_stream().cuda_stream
+                        for i in range(steps):
+                            reps.run(reps.args[i % R], cs)
+                stream.wait_stream(cap)
+                g.replay()
+                torch.cuda.synchronize()
+                ts = []
+                for _ in range(3):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    torch.cuda.synchronize()
+                    flush()
+                    a.record(stream)
+                    g.replay()
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    ts.append(1e3 * a.elapsed_time(b) / steps)
+                res[label] = round(sorted(ts)[1], 3)
+                del g, reps
+                torch.cuda.empty_cache()
+            nnz = sum(-(-n // 16) for n in lens)
+            print(json.dumps({"probe": "schedule-sweep", "rotary": rope is not None, "batch": B,
+                              "lengths": kind, "mean_over_longest_pages": round(nnz / (B * 256), 3),
+                              "tokens": sum(lens), **res,
+                              "balanced_gain": round(res["fixed_us"] / res["balanced_us"] - 1, 3)}),
+                  flush=True)
+        eng.close()
 
 
 def copy_probe(nbytes, steps, warmup):

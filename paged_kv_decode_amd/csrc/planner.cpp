@@ -336,6 +336,9 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, const Plan
     return PA_DECODE_OK;
 }
 
+int ragged_num(const pa_decode_desc& d) { return d.rotary_mode == 1 ? 3 : 1; }
+int ragged_den(const pa_decode_desc& d) { return d.rotary_mode == 1 ? 4 : 2; }
+
 int make_plan_csr(const pa_decode_desc& d, int num_cus, int waves_per_cu, const PlanTuning& tune,
                   int batch, int nnz_pages, int max_context_len, int sliding_window,
                   int partition_size, pa_decode_plan* plan, int* max_ctx_used)
@@ -358,9 +361,9 @@ int make_plan_csr(const pa_decode_desc& d, int num_cus, int waves_per_cu, const 
         if (cover > INT32_MAX)
             return PA_DECODE_UNSUPPORTED;
         S = int(cover);
-    } else if (S == 0 && batch >= 2 && batch <= kBalancedMaxBatch &&
-               int64_t(nnz_pages) * kRaggedDen <
-                   int64_t(batch) * ((mc + ps - 1) / ps) * kRaggedNum) {
+    } else if (S == 0 && batch >= kRaggedMinBatch && batch <= kBalancedMaxBatch &&
+               int64_t(nnz_pages) * ragged_den(d) <
+                   int64_t(batch) * ((mc + ps - 1) / ps) * ragged_num(d)) {
         // A ragged batch: the length-balanced schedule, when it takes these
         // sizes (else the fixed split below).
         const int st = make_plan(d, num_cus, waves_per_cu, tune, batch, int(mc), sliding_window,

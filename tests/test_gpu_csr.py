@@ -97,23 +97,27 @@ def test_csr_shared_pages():
 
 
 def test_csr_ragged_batch_plans_the_balanced_schedule_itself():
-    """partition_size 0 on the CSR path: the ragged batch-16 workload
-    (lengths 1 .. 4096, mean about half the longest) gets the length-balanced
-    schedule from the host's page count; a batch of equal lengths keeps the
-    fixed partitions.  Both match the oracle."""
-    p = W.generate(W.CONFIGS["llama8b_b16_ragged_f16"])
-    csr = W.to_csr(p)
-    out, lse, plan = run_gpu_csr(p, csr, partition_size=0)
-    assert plan["balanced_waves"] > 0, plan
-    ref = run_oracle(p)
-    compare(out, lse, ref[0], ref[1], torch.float16, "csr ragged auto")
-    # the same schedule as asking for it
-    out_b, lse_b, plan_b = run_gpu_csr(p, csr, partition_size=W.BALANCED)
-    assert plan_b == plan and torch.equal(out_b, out) and torch.equal(lse_b, lse)
-    uni = W.custom(batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype=torch.float16,
-                   context_lens=[2171] * 16, seed=904)
-    pu = W.generate(uni)
-    out, lse, plan = run_gpu_csr(pu, W.to_csr(pu), partition_size=0)
-    assert plan["balanced_waves"] == 0 and plan["split"] == 1, plan
-    ref = run_oracle(pu)
-    compare(out, lse, ref[0], ref[1], torch.float16, "csr uniform auto")
+    """partition_size 0 on the CSR path: a batch whose mean page count is
+    well below the longest gets the length-balanced schedule from the host's
+    page count (one 4096-token sequence among 200-token ones; the batch-16
+    ragged workload with rotary, mean ~0.53 of the longest), the same plan
+    and bits as asking for it; the batch-16 ragged workload without rotary
+    (mean ~0.53, below the 1/2 rule's reach) and a batch of equal lengths keep
+    fixed partitions.  All match the oracle."""
+    skew = W.custom(batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype=torch.float16,
+                    context_lens=[4096] + [200] * 15, seed=905)
+    cases = [(W.generate(skew), True),
+             (W.generate(W.CONFIGS["llama8b_b16_ragged_rope_f16"]), True),
+             (W.generate(W.CONFIGS["llama8b_b16_ragged_f16"]), False),
+             (W.generate(W.custom(batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                  dtype=torch.float16, context_lens=[2171] * 16, seed=904)), False)]
+    for p, balanced in cases:
+        csr = W.to_csr(p)
+        out, lse, plan = run_gpu_csr(p, csr, partition_size=0)
+        assert (plan["balanced_waves"] > 0) == balanced, plan
+        assert plan["split"] == 1
+        ref = run_oracle(p)
+        compare(out, lse, ref[0], ref[1], torch.float16, "csr auto balanced=%s" % balanced)
+        if balanced:
+            out_b, lse_b, plan_b = run_gpu_csr(p, csr, partition_size=W.BALANCED)
+            assert plan_b == plan and torch.equal(out_b, out) and torch.equal(lse_b, lse)

@@ -98,17 +98,20 @@ def test_rotary_window_at_far_positions(D, dtype):
 
 def test_rotary_csr_equals_dense_bitwise():
     """The CSR table gives the dense table's bits under the same schedule:
-    this ragged batch plans the length-balanced schedule on the CSR path
-    (from its page count), and the dense path is asked for it; forced fixed
-    partitions too."""
+    the plan the CSR host picks (fixed partitions for these four sequences),
+    the length-balanced schedule and forced fixed partitions, asked of both."""
     w = W.custom(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype=torch.float16,
                  context_lens=[1, 17, 3060, 700], seed=450, rope=(500000.0, 1.0))
     p = W.generate(w)
     b_out, b_lse, b_plan = run_gpu_csr(p, W.to_csr(p))
-    assert b_plan["balanced_waves"] > 0
-    a_out, a_lse, a_plan = run_gpu(p, partition_size=W.BALANCED)
+    S = W.BALANCED if b_plan["balanced_waves"] > 0 else 0
+    a_out, a_lse, a_plan = run_gpu(p, partition_size=S)
     assert a_plan == b_plan
     assert torch.equal(a_out, b_out) and torch.equal(a_lse, b_lse)
+    for S in (W.BALANCED,):
+        a = run_gpu(p, partition_size=S)
+        c = run_gpu_csr(p, W.to_csr(p), partition_size=S)
+        assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1]) and a[2] == c[2], S
     for S in (64, 1024):
         a = run_gpu(p, partition_size=S)
         c = run_gpu_csr(p, W.to_csr(p), partition_size=S)
