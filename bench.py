@@ -174,7 +174,7 @@ class Flusher:
 
     def __init__(self):
         self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
-        self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.sink = torch.zeros(binding.PA_DECODE_PROBE_WAVES, dtype=torch.int32, device="cuda")
         self.count = 0
 
     def __call__(self):
@@ -398,7 +398,7 @@ def same_pages_probe(reps, p: W.Problem, launches: int, stream_ptr: int, flush):
     n = int(lists[0].numel())
     if n == 0:
         return None
-    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(binding.PA_DECODE_PROBE_WAVES, dtype=torch.int32, device="cuda")
     R = len(lists)
 
     def probe(i, sp):
@@ -654,7 +654,7 @@ def read_sweep(launches=50):
     t = fixed + bytes / rate over the sizes from 64 MiB."""
     pool_bytes = 6 << 30
     pool = torch.ones(pool_bytes // 4, dtype=torch.int32, device="cuda")
-    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(binding.PA_DECODE_PROBE_WAVES, dtype=torch.int32, device="cuda")
     flush = Flusher()
     stream = torch.cuda.current_stream()
     gen = torch.Generator(device="cpu")

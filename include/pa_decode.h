@@ -375,16 +375,21 @@ int pa_decode_profile_end(pa_decode_handle handle, double* partial_ms, int32_t* 
  * num_chunks chunks of chunk_bytes bytes each (2048, 3072, 4096 or 8192:
  * one KV head's slice of a page, 16 tokens x D x element size) on `stream`
  * (the current device), with the partial kernel's 16-byte streaming load,
- * one wave per SIMD with 24-32 KiB in flight each.  Chunk i starts at chunk_addrs[i] (a
+ * in PA_DECODE_PROBE_WAVES waves (one per SIMD): wave w reads the chunks
+ * [w n / W, (w + 1) n / W) of the list in order, keeping 15-16 KiB of loads
+ * in flight from its start to its end.  Chunk i starts at chunk_addrs[i] (a
  * device array of device addresses, each 16-byte aligned, whole chunks
  * inside one allocation), or at base + i * chunk_bytes when chunk_addrs is
- * NULL (base 16-byte aligned).  *sink (device, 4 bytes) is XORed with the
- * XOR of every 32-bit word read (one atomic per workgroup), which uses the data
- * and lets a caller check what was read; clear it first to get that XOR.
- * Calls that share a sink must not overlap.  Asynchronous; the caller
- * times it.  Errors: INVALID_ARG (null sink, num_chunks < 0, other chunk
- * sizes, no base and no chunk_addrs, base misaligned), HIP_ERROR (launch
- * failed). */
+ * NULL (base 16-byte aligned).  sink (device, PA_DECODE_PROBE_WAVES 32-bit
+ * words): word w is overwritten with the XOR of every 32-bit word wave w
+ * read (0 for a wave without chunks), so the XOR of all the words is the
+ * XOR of everything read; the data is used and a caller can check what
+ * was read.  num_chunks = 0 launches nothing and leaves the sink as it is.  No atomics (a few hundred atomics on one word serialise into
+ * microseconds).  Calls that share a sink must not overlap.  Asynchronous;
+ * the caller times it.  Errors: INVALID_ARG (null sink, num_chunks < 0,
+ * other chunk sizes, no base and no chunk_addrs, base misaligned),
+ * HIP_ERROR (launch failed). */
+#define PA_DECODE_PROBE_WAVES 1024
 int pa_decode_read_probe(const void* base, const uint64_t* chunk_addrs, int32_t num_chunks,
                          int32_t chunk_bytes, uint32_t* sink, void* stream);
 

@@ -6,6 +6,7 @@ C ABI of include/pa_decode.h); ``binding`` is its ctypes front end and
 """
 from .binding import (  # noqa: F401
     PA_DECODE_PARTITION_BALANCED,
+    PA_DECODE_PROBE_WAVES,
     PagedDecode,
     PaDecodeArgs,
     PaDecodeDesc,

@@ -27,6 +27,8 @@ PA_DECODE_EXCEEDS_SCRATCH = -5
 
 # partition_size value for the length-balanced schedule (batch <= 64).
 PA_DECODE_PARTITION_BALANCED = -1
+# Words of the read probe's sink (one per probe wave).
+PA_DECODE_PROBE_WAVES = 1024
 
 PA_DTYPE_F32 = 0
 PA_DTYPE_F16 = 1
@@ -293,8 +295,9 @@ def pa_decode_read_probe(base: int, chunk_addrs: int, num_chunks: int, chunk_byt
                          sink: int, stream: int = 0) -> None:
     """Measurement tool: read num_chunks chunks (device addresses in the
     uint64 device array at chunk_addrs, or contiguous from base when
-    chunk_addrs is 0) on `stream`; the device uint32 at sink is XORed with
-    the XOR of every 32-bit word read."""
+    chunk_addrs is 0) on `stream`.  sink: a device array of
+    PA_DECODE_PROBE_WAVES uint32 words, each overwritten with the XOR of the
+    words one probe wave read (their XOR is that of everything read)."""
     _check(load_library().pa_decode_read_probe(base or None, chunk_addrs or None, num_chunks,
                                                chunk_bytes, sink or None, stream or None),
            "pa_decode_read_probe")

@@ -16,25 +16,6 @@
 namespace pa {
 namespace {
 
-// Four consecutive output elements (16-byte aligned for f32, 8-byte for
-// f16/bf16: out is 16-byte aligned and idx a multiple of 4), rounded to the
-// output type as store_out does.
-template <int DT> __device__ __forceinline__ void store_out4(void* out, size_t idx, f32x4 x);
-template <> __device__ __forceinline__ void store_out4<PA_DTYPE_F32>(void* out, size_t idx, f32x4 x)
-{
-    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = x;
-}
-template <> __device__ __forceinline__ void store_out4<PA_DTYPE_F16>(void* out, size_t idx, f32x4 x)
-{
-    const f16x4 h = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
-    *reinterpret_cast<f16x4*>(static_cast<_Float16*>(out) + idx) = h;
-}
-template <> __device__ __forceinline__ void store_out4<PA_DTYPE_BF16>(void* out, size_t idx, f32x4 x)
-{
-    const bf16x4 h = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
-    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out) + idx) = h;
-}
-
 // ---------------------------------------------------------------------------
 // Merge kernel for any partition count: one 256-thread workgroup per (query
 // head, sequence, 16-column slice of head_dim), so that even one sequence
@@ -329,12 +310,14 @@ __global__ __launch_bounds__(256) void merge_count_kernel(const MergeParams prm,
 // ---------------------------------------------------------------------------
 // Read probe (a measurement tool, not part of the decode step): the rate at
 // which the memory system delivers a given set of KV chunks to the same
-// streaming load the partial kernel uses.  One wave per SIMD (1024 waves;
-// on MI355X more waves measured slower: 8192 waves read a 100k-token page
-// set at 3.5 TB/s against 6.2 TB/s with 1024).  Each wave reads U chunks
-// (24-32 KiB) at a time, all issued before the first use, and folds them
-// into an XOR; at the end each workgroup XORs its result into *sink, so the
-// reads are used and can be checked.
+// streaming load the partial kernel uses.  W = PA_DECODE_PROBE_WAVES waves
+// (one per SIMD); wave w reads the chunks [w n / W, (w + 1) n / W) of the
+// list through a ring of NBUF chunk slots in registers (~16 KiB): a slot is
+// refilled with the chunk NBUF ahead as soon as its data has been folded
+// into the wave's XOR, so the wave keeps its loads in flight from start to
+// end.  Each wave then stores its XOR in sink[w]: no atomics (atomics on one
+// word serialise at ~10 ns each on MI355X, microseconds for a few hundred
+// workgroups).
 // ---------------------------------------------------------------------------
 template <int KPC>
 __global__ __launch_bounds__(256) void read_probe_kernel(const char* base,
@@ -342,62 +325,43 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const char* base,
                                                          int32_t num_chunks, uint32_t* sink)
 {
     constexpr int CB = KPC * kWave * 16;   // chunk bytes
-    constexpr int U = KPC >= 8 ? 4 : KPC >= 3 ? 8 : 16;   // chunks in flight per wave (24-32 KiB)
+    constexpr int NBUF = KPC == 8 ? 2 : KPC == 4 ? 4 : KPC == 3 ? 5 : 8;   // slots (15-16 KiB)
     const int lane = threadIdx.x & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x / kWave) +
                                                  threadIdx.x / kWave);
     const int nwv = gridDim.x * (blockDim.x / kWave);
+    const int c0 = int(int64_t(w) * num_chunks / nwv);
+    const int c1 = int(int64_t(w + 1) * num_chunks / nwv);
     typedef __attribute__((address_space(1))) const u32x4 gvec;   // global memory
-    // Lane u (< U) holds the address of chunk c0 + u (past the end: the
-    // last chunk, re-read but not counted); the next pass's addresses are
-    // loaded while this pass's data is in flight.
-    auto chunk_addr = [&](int c0) -> uint64_t {
-        const int c = min(c0 + (lane & (U - 1)), num_chunks - 1);
+    auto chunk = [&](int c) -> uint64_t {
         return chunk_addrs ? chunk_addrs[c] : reinterpret_cast<uint64_t>(base) + uint64_t(c) * CB;
     };
+    u32x4 r[NBUF][KPC];
+    auto issue = [&](int s, int c) {
+        const uint64_t a = chunk(c) + uint64_t(lane * 16);
+#pragma unroll
+        for (int k = 0; k < KPC; ++k)
+            r[s][k] = __builtin_nontemporal_load(reinterpret_cast<gvec*>(a + uint64_t(k * kWave * 16)));
+    };
+#pragma unroll
+    for (int s = 0; s < NBUF; ++s)
+        if (c0 + s < c1) issue(s, c0 + s);
     u32x4 acc = {0u, 0u, 0u, 0u};
-    uint64_t av = w * U < num_chunks ? chunk_addr(w * U) : 0;
-    for (int c0 = w * U; c0 < num_chunks; c0 += nwv * U) {
-        uint64_t addr[U];
+    for (int c = c0; c < c1; c += NBUF) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(av), u);
-            const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(av >> 32), u);
-            addr[u] = (uint64_t(hi) << 32) | lo;
-        }
-        const int cn = c0 + nwv * U;
-        if (cn < num_chunks)
-            av = chunk_addr(cn);
-        u32x4 r[U][KPC];
+        for (int s = 0; s < NBUF; ++s) {
+            if (c + s < c1) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int k = 0; k < KPC; ++k)
-                r[u][k] = __builtin_nontemporal_load(
-                    reinterpret_cast<gvec*>(addr[u] + uint64_t((k * kWave + lane) * 16)));
-        pin_loads();   // all U * KPC loads in flight before the first use
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            const bool counted = c0 + u < num_chunks;
-#pragma unroll
-            for (int k = 0; k < KPC; ++k) acc ^= counted ? r[u][k] : z;
+                for (int k = 0; k < KPC; ++k) acc ^= r[s][k];
+                if (c + s + NBUF < c1) issue(s, c + s + NBUF);
+            }
         }
     }
     uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off);
-    // One atomic per workgroup that read anything (atomics on one word
-    // serialise: one per wave cost microseconds on small chunk sets).
-    __shared__ uint32_t red[4];
     if (lane == 0)
-        red[threadIdx.x / kWave] = x;
-    __syncthreads();
-    if (threadIdx.x == 0 && int(blockIdx.x) * int(blockDim.x / kWave) * U < num_chunks) {
-        uint32_t y = 0;
-        for (int i = 0; i < int(blockDim.x / kWave); ++i) y ^= red[i];
-        __hip_atomic_fetch_xor(sink, y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+        sink[w] = x;
 }
 
 }  // namespace
@@ -448,12 +412,11 @@ hipError_t launch_read_probe(const void* base, const uint64_t* chunk_addrs, int3
                              int kpc, uint32_t* sink, hipStream_t stream)
 {
     if (num_chunks <= 0)
-        return hipSuccess;
-    // At most 256 workgroups of 4 waves (one wave per SIMD of 256 compute
-    // units); waves loop over their chunks.
-    const int64_t waves = (int64_t(num_chunks) + 3) / 4;
-    const int64_t groups = (waves + 3) / 4;
-    const dim3 grid(unsigned(groups < 256 ? groups : 256)), block(256);
+        return hipSuccess;   // nothing to read; the sink is left as it is
+    // PA_DECODE_PROBE_WAVES waves in workgroups of four, whatever the chunk
+    // count (waves without chunks store 0).
+    static_assert(PA_DECODE_PROBE_WAVES % 4 == 0, "workgroups of four waves");
+    const dim3 grid(PA_DECODE_PROBE_WAVES / 4), block(4 * kWave);
     const char* b = static_cast<const char*>(base);
     switch (kpc) {
     case 2: hipLaunchKernelGGL(read_probe_kernel<2>, grid, block, 0, stream, b, chunk_addrs, num_chunks, sink); break;

@@ -355,6 +355,24 @@ template <> __device__ __forceinline__ void store_out<PA_DTYPE_BF16>(void* out, 
 {
     static_cast<__bf16*>(out)[idx] = (__bf16)x;
 }
+// Four consecutive output elements (16-byte aligned for f32, 8-byte for
+// f16/bf16: out is 16-byte aligned and idx a multiple of 4), rounded to the
+// output type as store_out does.
+template <int DT> __device__ __forceinline__ void store_out4(void* out, size_t idx, f32x4 x);
+template <> __device__ __forceinline__ void store_out4<PA_DTYPE_F32>(void* out, size_t idx, f32x4 x)
+{
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = x;
+}
+template <> __device__ __forceinline__ void store_out4<PA_DTYPE_F16>(void* out, size_t idx, f32x4 x)
+{
+    const f16x4 h = {(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+    *reinterpret_cast<f16x4*>(static_cast<_Float16*>(out) + idx) = h;
+}
+template <> __device__ __forceinline__ void store_out4<PA_DTYPE_BF16>(void* out, size_t idx, f32x4 x)
+{
+    const bf16x4 h = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out) + idx) = h;
+}
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *static_cast<const u32x4*>(p); }
 
@@ -1226,41 +1244,54 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         // Denominator of head i16 over the four lane groups.
         l_run = rows4_sum(l_run);
 
-        // Result of (query head g of the group, partition p_rel): the partition
+        // Results: per (query head g of the group, partition) the partition
         // state (o normalised, max, denominator) for the merge, or, when one
         // partition covers the context, out and lse (an empty context gives
-        // out = 0, lse = -inf).
-        auto emit = [&](int g, int p_rel, int dd, float o, float M, float L, bool head_lane) {
-            const size_t h = size_t(b) * prm.num_q_heads + size_t(kvh) * Gact + g;
-            if (prm.split) {
-                const size_t row = h * prm.num_partitions + p_rel;
-                prm.ws_o[row * D + dd] = o;
-                if (head_lane) {
-                    prm.ws_m[row] = M;
-                    prm.ws_l[row] = L;
-                }
-            } else {
-                store_out<DT>(prm.out, h * D + dd, o);
-                if (head_lane && prm.lse) prm.lse[h] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
-            }
-        };
+        // out = 0, lse = -inf).  Head g's rows: ws_o + (h0 + g) P D + p D,
+        // ws_m / ws_l + (h0 + g) P + p, out + (h0 + g) D.  The split / out
+        // choice is one uniform branch around each store sequence, and the
+        // stores run from one base address with constant offsets.
+        const size_t h0 = size_t(b) * prm.num_q_heads + size_t(kvh) * Gact;
+        const int P = prm.num_partitions;
 
         if (wpp == 1) {
             // Every wave owns its partition: write straight from the output
             // blocks (row 4*grp + r of block db is head 4*grp + r, column
             // 16*db + i16); the max and denominator of head 4*grp + r sit in
             // lane 4*grp + r.  No LDS, no barrier.
-            if (uint32_t(srow) < uint32_t(prm.num_partitions)) {
+            if (uint32_t(srow) < uint32_t(P)) {
+                float Mr[4], Lr[4], inv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int g = 4 * grp + r;
-                    const float M = __shfl(m_run, g);
-                    const float L = __shfl(l_run, g);
-                    if (g < Gact) {
-                        const float inv = M == -INFINITY ? 0.f : 1.f / L;
+                    Mr[r] = __shfl(m_run, 4 * grp + r);
+                    Lr[r] = __shfl(l_run, 4 * grp + r);
+                    inv[r] = Mr[r] == -INFINITY ? 0.f : __builtin_amdgcn_rcpf(Lr[r]);
+                }
+                if (prm.split) {
 #pragma unroll
-                        for (int db = 0; db < NDB; ++db)
-                            emit(g, srow, 16 * db + i16, acc[db][r] * inv, M, L, db == 0 && i16 == 0);
+                    for (int r = 0; r < 4; ++r) {
+                        const int g = 4 * grp + r;
+                        if (g < Gact) {
+                            float* o = prm.ws_o + ((h0 + g) * P + srow) * D + i16;
+#pragma unroll
+                            for (int db = 0; db < NDB; ++db) o[16 * db] = acc[db][r] * inv[r];
+                            if (i16 == 0) {
+                                prm.ws_m[(h0 + g) * P + srow] = Mr[r];
+                                prm.ws_l[(h0 + g) * P + srow] = Lr[r];
+                            }
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int g = 4 * grp + r;
+                        if (g < Gact) {
+#pragma unroll
+                            for (int db = 0; db < NDB; ++db)
+                                store_out<DT>(prm.out, (h0 + g) * D + 16 * db + i16, acc[db][r] * inv[r]);
+                            if (i16 == 0 && prm.lse)
+                                prm.lse[h0 + g] = Mr[r] == -INFINITY ? -INFINITY : (Mr[r] + log2f(Lr[r])) * kLn2;
+                        }
                     }
                 }
             }
@@ -1291,24 +1322,41 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         }
         __syncthreads();
 
-        for (int sl = 0; sl < nslots; ++sl) {
+        // One thread per (slot, head, 4 consecutive columns): the slot's
+        // waves' weights 2^(m_w - M), the denominator, then a float4 of the
+        // output from float4 LDS reads and one 16-byte (8-byte) store.
+        constexpr int D4 = D / 4;
+        const int items = nslots * Gact * D4;
+        for (int e = threadIdx.x; e < items; e += blockDim.x) {
+            const int sl = e / (Gact * D4);
+            const int g = (e / D4) % Gact;
+            const int c = 4 * (e % D4);
             const int p_rel = blockIdx.x * nslots + sl;
-            if (p_rel >= prm.num_partitions)
-                break;
-            for (int e = threadIdx.x; e < Gact * D; e += blockDim.x) {
-                const int g = e / D, dd = e % D;   // D a compile-time constant (96 too)
-                float M = -INFINITY;
-                for (int w = sl * wpp; w < sl * wpp + wpp; ++w) M = fmaxf(M, cm[w * GP4 + g]);
-                float L = 0.f, o = 0.f;
-                if (M != -INFINITY) {
-                    for (int w = sl * wpp; w < sl * wpp + wpp; ++w) {
-                        const float sc = fast_exp2(cm[w * GP4 + g] - M);
-                        L += sc * cl[w * GP4 + g];
-                        o += sc * ca[(w * G + g) * D + dd];
-                    }
-                    o = o / L;
+            if (p_rel >= P)
+                continue;
+            const int w0 = sl * wpp;
+            float M = -INFINITY;
+            for (int w = w0; w < w0 + wpp; ++w) M = fmaxf(M, cm[w * GP4 + g]);
+            float L = 0.f;
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+            if (M != -INFINITY) {
+                for (int w = w0; w < w0 + wpp; ++w) {
+                    const float sc = fast_exp2(cm[w * GP4 + g] - M);
+                    L += sc * cl[w * GP4 + g];
+                    o += sc * *reinterpret_cast<const f32x4*>(ca + (w * G + g) * D + c);
                 }
-                emit(g, p_rel, dd, o, M, L, dd == 0);
+                o *= __builtin_amdgcn_rcpf(L);
+            }
+            if (prm.split) {
+                *reinterpret_cast<f32x4*>(prm.ws_o + ((h0 + g) * P + p_rel) * D + c) = o;
+                if (c == 0) {
+                    prm.ws_m[(h0 + g) * P + p_rel] = M;
+                    prm.ws_l[(h0 + g) * P + p_rel] = L;
+                }
+            } else {
+                store_out4<DT>(prm.out, (h0 + g) * D + c, o);
+                if (c == 0 && prm.lse)
+                    prm.lse[h0 + g] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
             }
         }
         return;
