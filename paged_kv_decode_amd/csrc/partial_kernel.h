@@ -1089,6 +1089,20 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
                 pin_loads();
             }
 
+            // Without rotary, every K tile read of the block goes out before
+            // the first score MFMA, and every V transpose read (P.V operand)
+            // right after the score MFMAs, so that each LDS latency is paid
+            // once per block rather than once per page (32 VGPRs each).
+            constexpr bool PRE = !ROT && !QKV && DT != PA_DTYPE_F32;
+            [[maybe_unused]] u32x4 kt[PRE ? NB : 1][PRE ? KS : 1];
+            if constexpr (PRE) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) kt[nb][ks] = ktile[tix(nb * kPage + i16, 4 * ks + grp)];
+                pin_loads();
+            }
+
             // Scores (base 2) of head i16 against token 4*grp + r of each page.
             float s[NB][4];
 #pragma unroll
@@ -1127,17 +1141,49 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
                     wave_lds_sync();
                     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
                     d = i16 < G ? *reinterpret_cast<const f32x4*>(sb + i16 * 16 + 4 * grp) : z;
+                } else if constexpr (PRE) {
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) d = Chunk<DT>::mfma(kt[nb][ks], qa[ks], d);
                 } else {
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks)
                         d = Chunk<DT>::mfma(ktile[tix(nb * kPage + i16, 4 * ks + grp)], qa[ks], d);
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tok = (pgb + nb) * kPage + 4 * grp + r;
-                    const bool ok = nb < nbv && tok >= t0 && tok < t1;
-                    s[nb][r] = ok ? d[r] * prm.scale_log2 : -INFINITY;
-                }
+                for (int r = 0; r < 4; ++r) s[nb][r] = d[r] * prm.scale_log2;
+            }
+
+            // P.V operand reads: V rows 4*grp + i16/4 of each page, columns
+            // 16*db + 4*(i16%4) .. +3 through the LDS transpose read.
+            auto tr_read = [&](int nb, int db) -> s16x4 {
+                const int vrow = nb * kPage + 4 * grp + (i16 >> 2);
+                const int j = 2 * db + ((i16 & 3) >> 1);
+                const char* addr = reinterpret_cast<const char*>(vtile + tix(vrow, j)) + (i16 & 1) * 8;
+                return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(addr));
+            };
+            [[maybe_unused]] s16x4 vt[PRE ? NB : 1][PRE ? NDB : 1];
+            if constexpr (PRE) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) vt[nb][db] = tr_read(nb, db);
+                pin_loads();
+            }
+            auto vop = [&](int nb, int db) -> s16x4 {
+                if constexpr (PRE) return vt[nb][db];
+                else return tr_read(nb, db);
+            };
+            // Tokens outside [t0, t1) and pages past the block's end score
+            // -inf; only edge blocks have any (wave-uniform branch).
+            if (edge) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int tok = (pgb + nb) * kPage + 4 * grp + r;
+                        const bool ok = nb < nbv && tok >= t0 && tok < t1;
+                        s[nb][r] = ok ? s[nb][r] : -INFINITY;
+                    }
             }
 
             // Block maximum of head i16: the lane's own 4*NB scores, then the
@@ -1181,14 +1227,7 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
                 }
             }
 
-            // P.V: V rows 4*grp + i16/4 of each page, columns 16*db +
-            // 4*(i16%4) .. +3 for the transpose read.
-            auto tr_read = [&](int nb, int db) -> s16x4 {
-                const int vrow = nb * kPage + 4 * grp + (i16 >> 2);
-                const int j = 2 * db + ((i16 & 3) >> 1);
-                const char* addr = reinterpret_cast<const char*>(vtile + tix(vrow, j)) + (i16 & 1) * 8;
-                return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(addr));
-            };
+            // P.V on the matrix cores.
             if constexpr (DT == PA_DTYPE_F32) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
@@ -1211,13 +1250,13 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
                 for (int nb = 0; nb < NB; nb += 2) {
 #pragma unroll
                     for (int db = 0; db < NDB; ++db)
-                        acc[db] = PV2<DT>::mma(s[nb], s[nb + 1], tr_read(nb, db), tr_read(nb + 1, db), acc[db]);
+                        acc[db] = PV2<DT>::mma(s[nb], s[nb + 1], vop(nb, db), vop(nb + 1, db), acc[db]);
                 }
             } else {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db) acc[db] = PV<DT>::mma(s[nb], tr_read(nb, db), acc[db]);
+                    for (int db = 0; db < NDB; ++db) acc[db] = PV<DT>::mma(s[nb], vop(nb, db), acc[db]);
                 }
             }
         };
