@@ -785,16 +785,23 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         return r;
     };
     // Every wave of the workgroup runs this exactly once (it holds the one
-    // barrier that publishes otab), before q is loaded so that the set-up
-    // holds few live registers.
+    // barrier that publishes otab).  Each thread takes one frequency i
+    // (rev_per_pos once) and every T-th offset t of it, T = threads per
+    // frequency; with fewer threads than frequencies, several frequencies and
+    // all 16 offsets.  The fixed schedule runs it while the wave's first K/V
+    // loads are in flight; the balanced schedule before its segments.
     auto rotary_setup = [&]() {
-        // Task (i, r): frequency i at offsets t = 4r .. 4r + 3.
+        const int T = int(blockDim.x) >= HD ? int(blockDim.x) / HD : 1;
+        const int i0 = int(threadIdx.x) % (T * HD) % HD;
+        const int j = int(threadIdx.x) < T * HD ? int(threadIdx.x) / HD : T;
+        const int istep = int(blockDim.x) >= HD ? HD : int(blockDim.x);
 #pragma unroll 1
-        for (int task = threadIdx.x; task < 4 * HD; task += blockDim.x) {
-            const int i = task % HD, r = task / HD;
+        for (int i = i0; j < T && i < HD; i += istep) {
             const double f = rev_per_pos(i);
+            if (j == 0)
+                ftab[i] = f;
 #pragma unroll 1
-            for (int t = 4 * r; t < 4 * r + 4; ++t) {
+            for (int t = j; t < kPage; t += T) {
                 double x = t * f;
                 x -= rint(x);
                 float sn, c;
@@ -803,11 +810,15 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
                 otab[t * TS + 2 * i + 1] = sn;
             }
         }
-        for (int i = threadIdx.x; i < HD; i += blockDim.x) ftab[i] = rev_per_pos(i);
         __syncthreads();
     };
-    if constexpr (ROT)
-        rotary_setup();
+    // Rotary tables not yet built by this wave.  Every wave takes part in
+    // the build exactly once, before any other barrier of the workgroup:
+    // fixed schedule, in its one pass, after its first loads if it has
+    // blocks; balanced schedule (no other barrier), after the first loads of
+    // its first segment (every segment has blocks), or after the segment
+    // loop when it has no segment.
+    bool tables_pending = ROT;
 
     // One segment per pass; the fixed schedule makes exactly one pass.
     for (;;) {
@@ -1262,16 +1273,35 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         };
 
         // Outer loop over chunks of IPV blocks (one page-id vector each); the
-        // pipelined inner loop itself issues no load but K/V.
+        // pipelined inner loop itself issues no load but K/V.  With rotary
+        // (fixed schedule) the first chunk's first loads go out before the
+        // workgroup builds its rotary tables, so the two overlap.
+        bool first_issued = false;
+        if constexpr (ROT) {
+            if (tables_pending) {
+                if (nit > 0) {
+                    fetch_ids(0, 0, min(nit, IPV));
+                    issue(kbase, kr);
+                    pin_loads();
+                    issue(vbase, vr);
+                    pin_loads();
+                    first_issued = true;
+                }
+                rotary_setup();
+                tables_pending = false;
+            }
+        }
         for (int it0 = 0; it0 < nit; it0 += IPV) {
             const int it1 = min(nit, it0 + IPV);
-            if (it0 > 0)
-                ids = load_ids(pg0, pg1, it0);
-            fetch_ids(it0, it0, it1);
-            issue(kbase, kr);
-            pin_loads();
-            issue(vbase, vr);
-            pin_loads();
+            if (it0 > 0 || !first_issued) {
+                if (it0 > 0)
+                    ids = load_ids(pg0, pg1, it0);
+                fetch_ids(it0, it0, it1);
+                issue(kbase, kr);
+                pin_loads();
+                issue(vbase, vr);
+                pin_loads();
+            }
             for (int it = it0; it < it1; ++it) step(it, it0, it1);
         }  // chunks of IPV blocks
 
@@ -1401,6 +1431,10 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         return;
     }  // segments
 
+    if constexpr (ROT && BAL) {
+        if (tables_pending)
+            rotary_setup();   // a wave without segments still joins the build's barrier
+    }
     if (prm.status && violation != 0 && lane == 0)
         __hip_atomic_fetch_or(prm.status, violation, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
