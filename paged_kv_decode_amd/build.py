@@ -44,7 +44,10 @@ FLAGS = [
 # Comparison builds (measurement only, never loaded by the package itself):
 # name -> (library file, extra defines).  qk_valu: the scores on the vector
 # ALUs (packed dot products, lane-swap sums) instead of the score MFMA.
-VARIANTS = {"qk_valu": ("libpa_decode_qk_valu.so", ["-DPA_QK_VALU=1"])}
+# fused_merge: no merge kernel for fixed partitions; the last workgroup of a
+# (sequence, KV head) merges its states.
+VARIANTS = {"qk_valu": ("libpa_decode_qk_valu.so", ["-DPA_QK_VALU=1"]),
+            "fused_merge": ("libpa_decode_fused_merge.so", ["-DPA_FUSED_MERGE=1"])}
 
 
 def build(verbose: bool = False, variant: str = None) -> str:

@@ -172,6 +172,10 @@ int launch_step(pa_decode_handle handle, const pa::StepArgs& a, const PageSource
     pp.bal_waves = plan.balanced_waves;
     pp.bal_start = balanced ? pa::balanced_start_pages(d, handle->tune) : 0;
     pp.ws_cnt = balanced ? reinterpret_cast<int32_t*>(ws + wl.c_off) : nullptr;
+#if PA_FUSED_MERGE
+    if (!balanced && plan.split)
+        pp.ws_cnt = reinterpret_cast<int32_t*>(ws + wl.c_off);   // merge counters (zero between calls)
+#endif
 
     const dim3 grid(plan.grid_partial[0], plan.grid_partial[1], plan.grid_partial[2]);
     const dim3 block(plan.block_partial);
@@ -187,7 +191,12 @@ int launch_step(pa_decode_handle handle, const pa::StepArgs& a, const PageSource
         handle->last_hip_error = int(e);
         return PA_DECODE_HIP_ERROR;
     }
-    if (plan.split) {
+#if PA_FUSED_MERGE
+    const bool merge_kernel = plan.split && balanced;
+#else
+    const bool merge_kernel = plan.split;
+#endif
+    if (merge_kernel) {
         pa::MergeParams mp;
         mp.batch = a.batch;
         mp.num_q_heads = d.num_q_heads;

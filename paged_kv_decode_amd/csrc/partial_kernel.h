@@ -474,6 +474,34 @@ template <> struct PV<PA_DTYPE_BF16> {
 #define PA_QK_VALU 0
 #endif
 
+// ---- fused merge (comparison build only) ----
+// A library built with PA_FUSED_MERGE=1 launches no merge kernel for the fixed
+// schedule: the partial kernel writes its partition states with agent-scope
+// stores (written through to memory), then the last workgroup of each
+// (sequence, KV head), found with an agent-scope counter in the workspace,
+// merges that group's states itself.  The shipped library keeps the merge
+// kernel.
+#ifndef PA_FUSED_MERGE
+#define PA_FUSED_MERGE 0
+#endif
+__device__ __forceinline__ void st_state(float* p, float v)
+{
+#if PA_FUSED_MERGE
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+    *p = v;
+#endif
+}
+__device__ __forceinline__ void st_state4(float* p, f32x4 v)
+{
+#if PA_FUSED_MERGE
+#pragma unroll
+    for (int k = 0; k < 4; ++k) __hip_atomic_store(p + k, v[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+    *reinterpret_cast<f32x4*>(p) = v;
+#endif
+}
+
 // Dot product of two 16-byte chunks (8 f16 / 8 bf16 / 4 f32 elements),
 // accumulated in f32.  Each 32-bit element is copied to a scalar before the
 // bit cast: hipcc (ROCm 7.2) compiles __builtin_bit_cast of a vector element
@@ -1322,6 +1350,79 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
         // stores run from one base address with constant offsets.
         const size_t h0 = size_t(b) * prm.num_q_heads + size_t(kvh) * Gact;
         const int P = prm.num_partitions;
+#if PA_FUSED_MERGE
+        // Comparison build: once every thread's state stores (written through
+        // to memory) have completed, one agent-scope add per workgroup on the
+        // (sequence, KV head) counter; the workgroup that completes the count
+        // takes an agent-scope acquire fence (the L2 lines it may hold of
+        // the states are dropped), stages the group's maxima and denominators
+        // in LDS, forms each partition's weight 2^(m_p - M) l_p once, and
+        // sums the weighted state rows with float4 loads, as the merge kernels
+        // do; then it clears the counter for the next call.
+        auto fused_tail = [&]() {
+            if (!prm.split)
+                return;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            int* flag = reinterpret_cast<int*>(smem);
+            int32_t* cnt = prm.ws_cnt + size_t(b) * gridDim.y + kvh;
+            if (threadIdx.x == 0) {
+                const int valid = min(nslots, P - int(blockIdx.x) * nslots);
+                const int old = __hip_atomic_fetch_add(cnt, valid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                *flag = old + valid == P;
+            }
+            __syncthreads();
+            if (!*flag)
+                return;
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            const int GP = Gact * P, bd = blockDim.x, tid = threadIdx.x;
+            float* wm = smem + 4;          // [Gact][P]: maxima, then weights
+            float* wl = wm + GP;           // [Gact][P]: denominators
+            float* hM = wl + GP;           // [Gact]
+            float* hL = hM + 16;           // [Gact]
+            for (int e = tid; e < GP; e += bd) {
+                const size_t row = (h0 + e / P) * P + e % P;
+                wm[e] = prm.ws_m[row];
+                wl[e] = prm.ws_l[row];
+            }
+            __syncthreads();
+            for (int g = tid; g < Gact; g += bd) {
+                float M = -INFINITY;
+                for (int p = 0; p < P; ++p) M = fmaxf(M, wm[g * P + p]);
+                hM[g] = M;
+            }
+            __syncthreads();
+            for (int e = tid; e < GP; e += bd) {
+                const float M = hM[e / P], l = wl[e];
+                wm[e] = (M != -INFINITY && l > 0.f) ? fast_exp2(wm[e] - M) * l : 0.f;
+            }
+            __syncthreads();
+            for (int g = tid; g < Gact; g += bd) {
+                float L = 0.f;
+                for (int p = 0; p < P; ++p) L += wm[g * P + p];
+                hL[g] = L;
+            }
+            __syncthreads();
+            constexpr int D4 = D / 4;
+            for (int e = tid; e < Gact * D4; e += bd) {
+                const int g = e / D4, c = 4 * (e % D4);
+                const size_t h = h0 + g;
+                const float* orow = prm.ws_o + h * P * D + c;
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+                for (int p = 0; p < P; ++p)
+                    o += wm[g * P + p] * *reinterpret_cast<const f32x4*>(orow + size_t(p) * D);
+                const float M = hM[g], L = hL[g];
+                if (M != -INFINITY)
+                    o *= 1.f / L;
+                store_out4<DT>(prm.out, h * D + c, o);
+                if (c == 0 && prm.lse)
+                    prm.lse[h] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
+            }
+            if (tid == 0)
+                __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+#endif
 
         if (wpp == 1) {
             // Every wave owns its partition: write straight from the output
@@ -1343,10 +1444,10 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
                         if (g < Gact) {
                             float* o = prm.ws_o + ((h0 + g) * P + srow) * D + i16;
 #pragma unroll
-                            for (int db = 0; db < NDB; ++db) o[16 * db] = acc[db][r] * inv[r];
+                            for (int db = 0; db < NDB; ++db) st_state(o + 16 * db, acc[db][r] * inv[r]);
                             if (i16 == 0) {
-                                prm.ws_m[(h0 + g) * P + srow] = Mr[r];
-                                prm.ws_l[(h0 + g) * P + srow] = Lr[r];
+                                st_state(prm.ws_m + (h0 + g) * P + srow, Mr[r]);
+                                st_state(prm.ws_l + (h0 + g) * P + srow, Lr[r]);
                             }
                         }
                     }
@@ -1366,6 +1467,9 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
             }
             if constexpr (BAL)
                 continue;
+#if PA_FUSED_MERGE
+            fused_tail();
+#endif
             return;
         }
 
@@ -1417,10 +1521,10 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
                 o *= __builtin_amdgcn_rcpf(L);
             }
             if (prm.split) {
-                *reinterpret_cast<f32x4*>(prm.ws_o + ((h0 + g) * P + p_rel) * D + c) = o;
+                st_state4(prm.ws_o + ((h0 + g) * P + p_rel) * D + c, o);
                 if (c == 0) {
-                    prm.ws_m[(h0 + g) * P + p_rel] = M;
-                    prm.ws_l[(h0 + g) * P + p_rel] = L;
+                    st_state(prm.ws_m + (h0 + g) * P + p_rel, M);
+                    st_state(prm.ws_l + (h0 + g) * P + p_rel, L);
                 }
             } else {
                 store_out4<DT>(prm.out, (h0 + g) * D + c, o);
@@ -1428,6 +1532,9 @@ __global__ __launch_bounds__(256) void partial_kernel(const PartialParams prm)
                     prm.lse[h0 + g] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
             }
         }
+#if PA_FUSED_MERGE
+        fused_tail();
+#endif
         return;
     }  // segments
 

@@ -101,6 +101,9 @@ WorkspaceLayout workspace_layout(const pa_decode_desc& d, int batch, int num_par
                                  bool counts)
 {
     auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
+#if PA_FUSED_MERGE
+    counts = true;   // comparison build: the per-(sequence, KV head) merge counters
+#endif
     size_t rows = size_t(batch) * size_t(d.num_q_heads) * size_t(num_partitions);
     WorkspaceLayout w;
     w.o_off = 0;
