@@ -8,7 +8,7 @@ sequence ends, and the merge combines each sequence's pieces.  Covered:
     rotary ragged, head_dim 256 with a window) and single sequences;
   * edge batches: every context empty, 64 one-token sequences, 64 sequences
     mixing empty, one-token, page-multiple and long contexts, windows that
-    cut pages;
+    cut pages; the same batches with rotary (waves without a segment);
   * NaN in every slot the method must not read;
   * the CSR page table and a token-major cache layout;
   * a workspace filled with garbage, then a second call with a smaller batch
@@ -69,6 +69,19 @@ def test_balanced_edge_batches(label, D, dtype, G, hkv):
     w = W.custom(batch=len(lens), num_q_heads=G * hkv, num_kv_heads=hkv, head_dim=D, dtype=dtype,
                  context_lens=lens, seed=len(lens) + D)
     _check(W.generate(w), "%s D=%d G=%d" % (label, D, G))
+
+
+@pytest.mark.parametrize("label", sorted(EDGE))
+@pytest.mark.parametrize("D,dtype,G,hkv", [(128, torch.float16, 4, 2), (256, torch.bfloat16, 2, 4)])
+def test_balanced_rotary_edge_batches(label, D, dtype, G, hkv):
+    """Rotary under the balanced schedule with waves that have no segment
+    (every context empty, or fewer charged pages than waves): each wave
+    still joins the workgroup's one barrier, where the rotary tables are
+    built, exactly once."""
+    lens = EDGE[label]
+    w = W.custom(batch=len(lens), num_q_heads=G * hkv, num_kv_heads=hkv, head_dim=D, dtype=dtype,
+                 context_lens=lens, seed=2 * len(lens) + D, rope=(500000.0, 1.0))
+    _check(W.generate(w), "rotary %s D=%d G=%d" % (label, D, G))
 
 
 @pytest.mark.parametrize("window", [1, 100, 4096])
