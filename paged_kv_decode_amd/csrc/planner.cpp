@@ -19,11 +19,16 @@ int dtype_bytes(int dtype)
 
 int pages_per_block(int head_dim, int dtype)
 {
-    // 8 KiB of K per block.  (Two 512-byte-row pages per block, for 32-token
-    // P.V MFMAs, measured slower on MI355X: the doubled load registers push
-    // the kernel to one wave per SIMD with AGPR spills.)
+    // 4 KiB of K (and of V) per block where a page allows it: two pages of
+    // 128-byte rows, one of 256- or 192-byte rows, one page of 512-byte rows
+    // (8 KiB).  Measured on MI355X against 8 KiB blocks, steps 1-8 % faster on
+    // every head_dim 64/96/128 and f32 shape tried (half the load registers
+    // and LDS per wave, twice the waves, a shorter exposed last block); two
+    // 512-byte-row pages per block (for 32-token P.V MFMAs) measured slower
+    // still: the doubled load registers push the kernel to one wave per SIMD
+    // with AGPR spills.
     int row = head_dim * dtype_bytes(dtype);
-    return std::max(1, std::min(4, 512 / row));
+    return std::max(1, std::min(4, 256 / row));
 }
 
 int tile_row_slots(int head_dim, int dtype)
@@ -310,8 +315,10 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, const Plan
     // compute units instead of sharing a few.
     if (!split || units * P < int64_t(num_cus) * 2)
         nw = wpp;
-    // Experiments only: an override of the workgroup size.
-    if (tune.waves_per_group > 0 && tune.waves_per_group >= wpp) nw = tune.waves_per_group;
+    // Experiments only: an override of the workgroup size (a multiple of the
+    // waves per partition, so that the workgroup splits into whole slots).
+    if (tune.waves_per_group > 0 && tune.waves_per_group >= wpp && tune.waves_per_group % wpp == 0)
+        nw = tune.waves_per_group;
     const int slots = nw / wpp;
     const int64_t gx = ceil_div(P, slots);
     if (gx > 65535)

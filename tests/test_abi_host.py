@@ -309,8 +309,9 @@ def test_csr_conversion_round_trips():
 @pytest.mark.parametrize("dtype", [B.PA_DTYPE_F16, B.PA_DTYPE_BF16])
 def test_head_dim_96_is_planned(dtype):
     """head_dim 96 (12 chunks of 16 bytes per row, TVM PR #20426, "Tests",
-    lays out D = 96 too): accepted, two pages per block, the merge grid covers
-    a partial 64-column slice, LDS within 64 KiB per workgroup."""
+    lays out D = 96 too): accepted, one page per block (192-byte rows), the
+    merge grid covers a partial 64-column slice, LDS within 64 KiB per
+    workgroup."""
     d = B.PaDecodeDesc(num_q_heads=32, num_kv_heads=8, head_dim=96, page_size=16, dtype=dtype,
                        max_batch=64, max_context_len=8192, device=0)
     h = ctypes.c_void_p()
@@ -318,7 +319,7 @@ def test_head_dim_96_is_planned(dtype):
                                                                          B.PA_DECODE_HIP_ERROR)
     for S, P in ((16, 256), (512, 8)):
         p = B.pa_decode_plan_query(d, 256, 8, 2, 4096, 0, S)
-        assert p.pages_per_block == 2 and p.num_partitions == P
+        assert p.pages_per_block == 1 and p.num_partitions == P
         if P <= 64:   # 2 x 32 x 2 = 128 waves at 64 columns: 16-column slices
             assert list(p.grid_merge) == [-(-2 * 32 * (96 // 16) // 4), 1, 1]
         else:
