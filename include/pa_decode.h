@@ -279,7 +279,8 @@ int pa_decode_last_plan(pa_decode_handle handle, pa_decode_plan* plan);
  * before the launch) and the commit page's split-context "Phase 1".
  * Tuning hooks for experiments: the environment variables
  * PA_DECODE_WAVES_PER_PARTITION and PA_DECODE_WAVES_PER_GROUP (1, 2 or 4)
- * override the plan's waves_per_partition / waves_per_group,
+ * override the plan's waves_per_partition / waves_per_group (the latter only
+ * where it is a multiple of the former),
  * PA_DECODE_BALANCED_START (0 .. 64) the balanced schedule's start charge in
  * pages and PA_DECODE_BALANCED_WAVES_PER_CU (1 .. 16) its waves per compute
  * unit; other values are ignored.  This function reads them at each call, a
