@@ -325,11 +325,11 @@ typedef struct pa_decode_csr_args {
     int32_t partition_size;       /* 0: the host switch above -- one partition per    */
                                   /*   (sequence, KV head) when nnz_pages <=          */
                                   /*   B * 256 / page_size; else, for 8 .. 64         */
-                                  /*   sequences with 2 * nnz_pages < B *             */
+                                  /*   sequences with 8 * nnz_pages < 5 * B *         */
                                   /*   ceil(max_context_len / page_size) (a ragged    */
-                                  /*   batch: mean pages below 1/2 of the longest;    */
-                                  /*   3/4 with rotary_mode 1), the length-balanced   */
-                                  /*   schedule; else the planner's fixed split;      */
+                                  /*   batch: mean pages below 5/8 of the longest),   */
+                                  /*   the length-balanced schedule; else the         */
+                                  /*   planner's fixed split;                         */
                                   /*   > 0: tokens per partition, as in pa_decode_args; */
                                   /*   PA_DECODE_PARTITION_BALANCED as there          */
     void* out;                    /* device, [batch, Hq, D] contiguous, desc.dtype */

@@ -168,7 +168,9 @@ int balanced_start_pages(const pa_decode_desc& d, const PlanTuning& tune)
     // Four blocks' worth, three with rotary: measured on MI355X over 2 .. 32
     // pages for batches of 16 with lengths up to 4096 at two pages per
     // block, the best charges were 8 (head_dim 128), 8 - 10 (head_dim 96)
-    // and 6 - 7 (head_dim 128 with rotary, whose blocks take longer).
+    // and 6 - 7 (head_dim 128 with rotary, whose blocks take longer).  At one
+    // page per block (4 KiB blocks) charges of 2 .. 12 pages measured within
+    // 2 % of each other at head_dim 128 and 96, 3 % with rotary.
     int c = (d.rotary_mode == 1 ? 3 : 4) * pages_per_block(d.head_dim, d.dtype);
     if (tune.balanced_start >= 0) c = tune.balanced_start;
     return std::max(0, std::min(64, c));
@@ -346,9 +348,6 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, const Plan
     return PA_DECODE_OK;
 }
 
-int ragged_num(const pa_decode_desc& d) { return d.rotary_mode == 1 ? 3 : 1; }
-int ragged_den(const pa_decode_desc& d) { return d.rotary_mode == 1 ? 4 : 2; }
-
 int make_plan_csr(const pa_decode_desc& d, int num_cus, int waves_per_cu, const PlanTuning& tune,
                   int batch, int nnz_pages, int max_context_len, int sliding_window,
                   int partition_size, pa_decode_plan* plan, int* max_ctx_used)
@@ -372,8 +371,8 @@ int make_plan_csr(const pa_decode_desc& d, int num_cus, int waves_per_cu, const 
             return PA_DECODE_UNSUPPORTED;
         S = int(cover);
     } else if (S == 0 && batch >= kRaggedMinBatch && batch <= kBalancedMaxBatch &&
-               int64_t(nnz_pages) * ragged_den(d) <
-                   int64_t(batch) * ((mc + ps - 1) / ps) * ragged_num(d)) {
+               int64_t(nnz_pages) * kRaggedDen <
+                   int64_t(batch) * ((mc + ps - 1) / ps) * kRaggedNum) {
         // A ragged batch: the length-balanced schedule, when it takes these
         // sizes (else the fixed split below).
         const int st = make_plan(d, num_cus, waves_per_cu, tune, batch, int(mc), sliding_window,

@@ -75,17 +75,17 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, const Plan
 
 // Ragged-batch rule of the CSR form with partition_size 0: a batch of
 // kRaggedMinBatch .. 64 sequences whose mean page count is below
-// ragged_num / ragged_den of the longest possible (nnz_pages * den < batch *
-// ceil(max_context_len / page_size) * num) runs the length-balanced
-// schedule: below 1/2, or 3/4 with rotary.  Measured on MI355X (batches of 4
-// .. 32 at head_dim 128, four length mixes, with and without rotary): the
-// balanced schedule lost at every mix at batch 4 (6 - 19 %), and without
-// rotary from a mean of ~0.57 of the longest on (1 - 10 %), while it gained
-// 11 - 133 % at 0.10 - 0.40; with rotary (more work per block, so the waves
-// of the longest sequences set the time) it gained up to a mean of ~0.77.
+// kRaggedNum / kRaggedDen = 5/8 of the longest possible (nnz_pages * 8 <
+// batch * ceil(max_context_len / page_size) * 5) runs the length-balanced
+// schedule.  Measured on MI355X (batches of 4 .. 32 at head_dim 128, four
+// length mixes, with and without rotary): the balanced schedule lost at
+// every mix at batch 4 (3 - 15 %) and from a mean of ~0.66 of the longest on
+// (1 - 9 %), while it gained 7 - 191 % at means of 0.10 - 0.57 (under fixed
+// partitions the waves of the longest sequences, which hold the most
+// blocks, set the step time).
 constexpr int kRaggedMinBatch = 8;
-int ragged_num(const pa_decode_desc& d);
-int ragged_den(const pa_decode_desc& d);
+constexpr int kRaggedNum = 5;
+constexpr int kRaggedDen = 8;
 
 // The plan for a CSR page table (nnz_pages pages in use).  With
 // partition_size 0: the host switch of TVM PR #20426, section "Change" (one

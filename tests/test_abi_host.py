@@ -227,7 +227,7 @@ def test_csr_host_switch_follows_the_page_count(batch, avg_tokens):
     if nnz * 16 <= batch * 256:
         assert p.split == 0 and p.num_partitions == 1 and p.partition_size >= max_ctx
         assert p.workspace_bytes == 0
-    elif 8 <= batch <= 64 and 2 * nnz < batch * (-(-max_ctx // 16)):
+    elif 8 <= batch <= 64 and 8 * nnz < 5 * batch * (-(-max_ctx // 16)):
         dense = plan(w, batch=batch, max_ctx=max_ctx, S=B.PA_DECODE_PARTITION_BALANCED)
         assert p.balanced_waves > 0 and p.as_dict() == dense.as_dict()
     else:
@@ -238,9 +238,12 @@ def test_csr_host_switch_follows_the_page_count(batch, avg_tokens):
 @pytest.mark.parametrize("batch,lens,rope,balanced", [
     (16, [4096] * 16, False, False),                       # uniform
     (16, [4096 - 37 * i for i in range(16)], False, False),  # nearly uniform
-    (16, [1 + 273 * i for i in range(16)], False, False),  # mean ~1/2 of the longest: fixed
+    (16, [1 + 273 * i for i in range(16)], False, True),   # mean ~0.53 of the longest: balanced
+    (16, [4096] + [2500] * 15, False, False),              # mean 0.64 (just above 5/8): fixed
+    (16, [4096] + [2440] * 15, False, True),               # mean 0.62 (just below 5/8): balanced
     (16, [4096] + [200] * 15, False, True),                # one long, many short: balanced
     (16, [1 + 273 * i for i in range(16)], True, True),    # the same with rotary: balanced
+    (16, [4096] + [2500] * 15, True, False),               # mean 0.64 with rotary: fixed
     (16, [4096 - 100 * i for i in range(16)], True, False),  # mean 0.82, rotary: fixed
     (4, [4096, 17, 17, 17], False, False),                 # below 8 sequences: fixed
     (8, [4096] + [300] * 7, False, True),                  # 8 sequences, very ragged
@@ -250,8 +253,8 @@ def test_csr_host_switch_follows_the_page_count(batch, avg_tokens):
 def test_csr_ragged_rule_picks_the_balanced_schedule(batch, lens, rope, balanced):
     """With partition_size 0 and pages above the single-pass switch, the CSR
     host picks the length-balanced schedule for 8 .. 64 sequences whose mean
-    page count is below 1/2 (3/4 with rotary) of what max_context_len allows,
-    else fixed partitions (the rule measured in bench.py --probe
+    page count is below 5/8 of what max_context_len allows, with or without
+    rotary, else fixed partitions (the rule measured in bench.py --probe
     schedule-sweep); the choice uses host counts only."""
     w = W.CONFIGS["llama8b_b16_ragged_f16"]
     d = B.make_desc(w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype, max_batch=4096,
@@ -259,8 +262,7 @@ def test_csr_ragged_rule_picks_the_balanced_schedule(batch, lens, rope, balanced
     nnz = sum(-(-n // 16) for n in lens)
     max_ctx = max(lens)
     p = B.pa_decode_plan_query_csr(d, 256, 8, batch, nnz, max_ctx, 0, 0)
-    num, den = (3, 4) if rope else (1, 2)
-    assert (8 <= batch <= 64 and den * nnz < num * batch * (-(-max_ctx // 16))) == balanced
+    assert (8 <= batch <= 64 and 8 * nnz < 5 * batch * (-(-max_ctx // 16))) == balanced
     assert (p.balanced_waves > 0) == balanced, p.as_dict()
     fixed = B.pa_decode_plan_query(d, 256, 8, batch, max_ctx, 0, 0)
     if not balanced:

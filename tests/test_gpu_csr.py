@@ -100,15 +100,18 @@ def test_csr_ragged_batch_plans_the_balanced_schedule_itself():
     """partition_size 0 on the CSR path: a batch whose mean page count is
     well below the longest gets the length-balanced schedule from the host's
     page count (one 4096-token sequence among 200-token ones; the batch-16
-    ragged workload with rotary, mean ~0.53 of the longest), the same plan
-    and bits as asking for it; the batch-16 ragged workload without rotary
-    (mean ~0.53, below the 1/2 rule's reach) and a batch of equal lengths keep
-    fixed partitions.  All match the oracle."""
+    ragged workload, mean ~0.53 of the longest, with and without rotary), the
+    same plan and bits as asking for it; a batch at a mean of 0.64 (above
+    the 5/8 rule) and a batch of equal lengths keep fixed partitions.  All
+    match the oracle."""
     skew = W.custom(batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype=torch.float16,
                     context_lens=[4096] + [200] * 15, seed=905)
+    near = W.custom(batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype=torch.float16,
+                    context_lens=[4096] + [2500] * 15, seed=906)
     cases = [(W.generate(skew), True),
              (W.generate(W.CONFIGS["llama8b_b16_ragged_rope_f16"]), True),
-             (W.generate(W.CONFIGS["llama8b_b16_ragged_f16"]), False),
+             (W.generate(W.CONFIGS["llama8b_b16_ragged_f16"]), True),
+             (W.generate(near), False),
              (W.generate(W.custom(batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128,
                                   dtype=torch.float16, context_lens=[2171] * 16, seed=904)), False)]
     for p, balanced in cases:
