@@ -23,7 +23,10 @@ int pages_per_block(int head_dim, int dtype)
     // 128-byte rows, one of 256- or 192-byte rows, one page of 512-byte rows
     // (8 KiB).  Measured on MI355X against 8 KiB blocks, steps 1-8 % faster on
     // every head_dim 64/96/128 and f32 shape tried (half the load registers
-    // and LDS per wave, twice the waves, a shorter exposed last block); two
+    // and LDS per wave, 3 resident waves per SIMD instead of 2 at head_dim
+    // 128, a shorter exposed last block), but 3-15 % slower for fixed
+    // partitions over ragged batches, whose longest sequences' waves hold the
+    // most blocks (the CSR rule gives those the balanced schedule).  Two
     // 512-byte-row pages per block (for 32-token P.V MFMAs) measured slower
     // still: the doubled load registers push the kernel to one wave per SIMD
     // with AGPR spills.
