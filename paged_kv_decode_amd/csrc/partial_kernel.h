@@ -3,7 +3,8 @@
 //
 // Partial kernel: one workgroup of NW wave64s per (partition, KV head,
 // sequence).  The partition's pages are dealt to the waves in blocks of NB
-// pages (8 KiB of K and 8 KiB of V per block).  For each block a wave
+// pages (4 KiB of K and 4 KiB of V per block where a page allows it; one
+// 8 KiB page at head_dim 256).  For each block a wave
 //   1. reads the block's page ids from a page-id vector (one scalar readlane
 //      per page) and issues 16-byte loads of whole 128-byte lines of every K
 //      and V row of those pages;

@@ -408,7 +408,7 @@ size_t partial_lds_bytes(const pa_decode_desc& d, const pa_decode_plan& plan)
     const int G = template_group(d.num_q_heads / d.num_kv_heads);
     const int gp4 = (G + 3) / 4 * 4;
     const int nw = plan.waves_per_group;
-    // per wave: the block's K and V tiles (8 KiB each)
+    // per wave: the block's K and V tiles (4-8 KiB each)
     const size_t ktile = size_t(plan.pages_per_block) * kPageSize * 16 *
                          size_t(tile_row_slots(d.head_dim, d.dtype)) / sizeof(float);
     const size_t loop =

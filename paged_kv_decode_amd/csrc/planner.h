@@ -38,8 +38,10 @@ constexpr int kMaxGridYZ = 65535;
 // Bytes per element of a PA_DTYPE_* code (0 when unknown).
 int dtype_bytes(int dtype);
 
-// Pages of K (and of V) one wave holds in flight per step: 8 KiB of K and
-// 8 KiB of V per wave, i.e. 512 bytes of one token row times 16 rows.
+// Pages of K (and of V) one wave holds in flight per step: 256 bytes of one
+// token row times 16 rows, i.e. 4 KiB of K and 4 KiB of V per wave, clamped to
+// 1 .. 4 pages (one page of 3 KiB at head_dim 96 with 2-byte types, one of
+// 8 KiB at head_dim 256).
 int pages_per_block(int head_dim, int dtype);
 
 // 16-byte slots per key row in the kernel's LDS tiles: the row's chunks,
