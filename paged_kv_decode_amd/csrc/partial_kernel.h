@@ -1562,13 +1562,11 @@ hipError_t launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t strea
     return hipGetLastError();
 }
 
-// Pages per block: 4 KiB of K per block where a page allows it (the same
-// rule as the planner's pages_per_block).
+// Pages per block: the planner's rule (pages_per_block_for_row).
 template <int DT, int D>
 constexpr int pages_per_block_t()
 {
-    constexpr int EB = Elt<DT>::bytes;
-    return (256 / (D * EB)) < 1 ? 1 : ((256 / (D * EB)) > 4 ? 4 : 256 / (D * EB));
+    return pages_per_block_for_row(D * Elt<DT>::bytes);
 }
 
 template <bool BAL, int DT, int D, int G>

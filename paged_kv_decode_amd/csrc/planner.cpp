@@ -30,8 +30,7 @@ int pages_per_block(int head_dim, int dtype)
     // 512-byte-row pages per block (for 32-token P.V MFMAs) measured slower
     // still: the doubled load registers push the kernel to one wave per SIMD
     // with AGPR spills.
-    int row = head_dim * dtype_bytes(dtype);
-    return std::max(1, std::min(4, 256 / row));
+    return pages_per_block_for_row(head_dim * dtype_bytes(dtype));
 }
 
 int tile_row_slots(int head_dim, int dtype)

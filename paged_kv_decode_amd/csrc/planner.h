@@ -38,10 +38,15 @@ constexpr int kMaxGridYZ = 65535;
 // Bytes per element of a PA_DTYPE_* code (0 when unknown).
 int dtype_bytes(int dtype);
 
-// Pages of K (and of V) one wave holds in flight per step: 256 bytes of one
-// token row times 16 rows, i.e. 4 KiB of K and 4 KiB of V per wave, clamped to
-// 1 .. 4 pages (one page of 3 KiB at head_dim 96 with 2-byte types, one of
-// 8 KiB at head_dim 256).
+// Pages of K (and of V) one wave holds in flight per step, from the bytes of
+// one key row: 256 bytes of a token row times 16 rows, i.e. 4 KiB of K and
+// 4 KiB of V per wave, clamped to 1 .. 4 pages (one page of 3 KiB at head_dim
+// 96 with 2-byte types, one of 8 KiB at head_dim 256).  The planner and the
+// partial kernel's template both take it from here.
+constexpr int pages_per_block_for_row(int row_bytes)
+{
+    return row_bytes <= 0 || 256 / row_bytes < 1 ? 1 : (256 / row_bytes > 4 ? 4 : 256 / row_bytes);
+}
 int pages_per_block(int head_dim, int dtype);
 
 // 16-byte slots per key row in the kernel's LDS tiles: the row's chunks,
