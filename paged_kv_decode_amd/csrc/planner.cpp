@@ -263,68 +263,124 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, const Plan
     const int per_cu = (d.rotary_mode == 1 && batch > 1) ? 8 : 4;
     const int64_t target = std::min<int64_t>(capacity, int64_t(num_cus) * per_cu);
 
-    int nw = workgroup_waves(d);
-    int64_t S;
+    // The layout for partition size S: partitions, the waves sharing one
+    // partition, the waves per workgroup and the grid.
+    struct Layout {
+        bool ok;
+        int64_t S, P;
+        bool split;
+        int wpp, nw, slots;
+        int64_t gx;
+    };
+    const int nw0 = workgroup_waves(d);
+    auto layout = [&](int64_t S) {
+        Layout L = {};
+        int64_t P;
+        if (max_context_len == 0) {
+            P = 1;
+        } else if (windowed) {
+            // A window's partitions sit on multiples of S, so its visible
+            // range can touch one partition more than visible / S.
+            P = std::min(ceil_div(max_context_len, S), ceil_div(visible, S) + 1);
+        } else {
+            P = ceil_div(max_context_len, S);
+        }
+        P = std::max<int64_t>(P, 1);
+        if (P > 65535 * int64_t(kMaxWavesPerGroup))
+            return L;
+        const bool split = P > 1;
+        if (!split && partition_size == 0 && max_context_len > 0) {
+            // The unsplit path covers the whole context with one workgroup.
+            S = ceil_div(max_context_len, ps) * ps;
+        }
+        // Waves sharing one partition: the count (1, 2 or 4, at most one per
+        // block of the partition) whose grid total is closest to `target` and
+        // fits in one round of resident waves.
+        const int64_t blocks = ceil_div(
+            ceil_div(std::min<int64_t>(S, std::max<int64_t>(visible, 1)), ps) + (windowed ? 1 : 0), nb);
+        int wpp = 1;
+        {
+            int64_t best = -1;
+            for (int cand = 1; cand <= nw0; cand *= 2) {
+                if (cand > 1 && (cand > blocks || units * P * cand > capacity)) break;
+                const int64_t dist = std::abs(units * P * cand - target);
+                if (best < 0 || dist < best) {
+                    best = dist;
+                    wpp = cand;
+                }
+            }
+        }
+        if (!split)
+            wpp = int(std::min<int64_t>(nw0, std::max<int64_t>(1, blocks)));  // one partition: all waves on it
+        // Experiments only: an override of the choice.
+        if (tune.waves_per_partition > 0) wpp = std::min(tune.waves_per_partition, nw0);
+        // A grid with fewer partitions than two per compute unit gets one
+        // partition per workgroup, so that its workgroups spread over the
+        // compute units instead of sharing a few.
+        int nw = nw0;
+        if (!split || units * P < int64_t(num_cus) * 2)
+            nw = wpp;
+        // Experiments only: an override of the workgroup size (a multiple of
+        // the waves per partition, so that the workgroup splits into whole
+        // slots).
+        if (tune.waves_per_group > 0 && tune.waves_per_group >= wpp && tune.waves_per_group % wpp == 0)
+            nw = tune.waves_per_group;
+        L.ok = true;
+        L.S = S;
+        L.P = P;
+        L.split = split;
+        L.wpp = wpp;
+        L.nw = nw;
+        L.slots = nw / wpp;
+        L.gx = ceil_div(P, L.slots);
+        return L;
+    };
+    Layout L;
     if (partition_size > 0) {
-        S = partition_size;
+        L = layout(partition_size);
     } else {
         // Pages per wave so that `target` waves cover the work, a
-        // workgroup's waves (nw, fewer than four only for head_dim-256
+        // workgroup's waves (nw0, fewer than four only for head_dim-256
         // rotary) sharing a partition; at least one page per wave and at
         // most 64.
         int64_t ppw = std::max<int64_t>(1, ceil_div(units * vis_pages, target));
         ppw = std::min<int64_t>(ppw, 64);
-        S = int64_t(nw) * ppw * ps;
-    }
-    int64_t P;
-    if (max_context_len == 0) {
-        P = 1;
-    } else if (windowed) {
-        P = std::min(ceil_div(max_context_len, S), ceil_div(visible, S) + 1);
-    } else {
-        P = ceil_div(max_context_len, S);
-    }
-    P = std::max<int64_t>(P, 1);
-    if (P > 65535 * int64_t(kMaxWavesPerGroup))
-        return PA_DECODE_UNSUPPORTED;
-    const bool split = P > 1;
-    if (!split && partition_size == 0 && max_context_len > 0) {
-        // The unsplit path covers the whole context with one workgroup.
-        S = ceil_div(max_context_len, ps) * ps;
-    }
-
-    // Waves sharing one partition: the count (1, 2 or 4, at most one per
-    // block of the partition) whose grid total is closest to `target` and
-    // fits in one round of resident waves.
-    const int64_t blocks =
-        ceil_div(ceil_div(std::min<int64_t>(S, std::max<int64_t>(visible, 1)), ps) + (windowed ? 1 : 0), nb);
-    int wpp = 1;
-    {
-        int64_t best = -1;
-        for (int cand = 1; cand <= nw; cand *= 2) {
-            if (cand > 1 && (cand > blocks || units * P * cand > capacity)) break;
-            const int64_t dist = std::abs(units * P * cand - target);
-            if (best < 0 || dist < best) {
-                best = dist;
-                wpp = cand;
+        L = layout(int64_t(nw0) * ppw * ps);
+        // The partition count rounds up, so the grid can end a little past
+        // one workgroup per compute unit (at one wave per SIMD), which then
+        // doubles up some units: measured on MI355X, those units set the
+        // kernel's end (head_dim 256 window at batch 8, 288 workgroups: 35.0
+        // us per step against 29.6 at 256; head_dim 64 at 88k tokens, 264
+        // workgroups: 59.4 against 46.5).  So among up to twice the pages
+        // per wave (at most 256), take the layout with the least work on the
+        // busiest unit: rounds of workgroups per unit (as many at once as the
+        // wave target per unit allows) times pages per wave.
+        const int64_t unit_waves = std::max<int64_t>(1, target / num_cus);
+        auto cost = [&](const Layout& x) {
+            const int64_t per_unit = std::max<int64_t>(1, unit_waves / x.nw);
+            const int64_t wgs = x.gx * d.num_kv_heads * std::max(batch, 1);
+            return ceil_div(wgs, int64_t(num_cus) * per_unit) * ceil_div(x.S / ps, x.wpp);
+        };
+        if (L.ok && L.split) {
+            int64_t best = cost(L);
+            const int64_t last = std::min<int64_t>(256, 2 * ppw);
+            for (int64_t q = ppw + 1; q <= last; ++q) {
+                const Layout c = layout(int64_t(nw0) * q * ps);
+                if (!c.ok || !c.split)
+                    break;
+                const int64_t k = cost(c);
+                if (k < best) {
+                    best = k;
+                    L = c;
+                }
             }
         }
     }
-    if (!split)
-        wpp = int(std::min<int64_t>(nw, std::max<int64_t>(1, blocks)));  // one partition: all waves on it
-    // Experiments only: an override of the choice.
-    if (tune.waves_per_partition > 0) wpp = std::min(tune.waves_per_partition, nw);
-    // A grid with fewer partitions than two per compute unit gets one
-    // partition per workgroup, so that its workgroups spread over the
-    // compute units instead of sharing a few.
-    if (!split || units * P < int64_t(num_cus) * 2)
-        nw = wpp;
-    // Experiments only: an override of the workgroup size (a multiple of the
-    // waves per partition, so that the workgroup splits into whole slots).
-    if (tune.waves_per_group > 0 && tune.waves_per_group >= wpp && tune.waves_per_group % wpp == 0)
-        nw = tune.waves_per_group;
-    const int slots = nw / wpp;
-    const int64_t gx = ceil_div(P, slots);
+    if (!L.ok)
+        return PA_DECODE_UNSUPPORTED;
+    const int64_t S = L.S, P = L.P, gx = L.gx;
+    const bool split = L.split;
+    const int wpp = L.wpp, nw = L.nw;
     if (gx > 65535)
         return PA_DECODE_UNSUPPORTED;
 

@@ -108,6 +108,12 @@ CONFIGS["llama8b_ctx32k_f16"] = Workload(
     name="llama8b_ctx32k_f16", batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128,
     dtype=torch.float16, context_lens=[32768], num_pages=2048, seed=8)
 
+# The windowed head_dim-256 shape at batch 8 (a window's partitions sit on
+# multiples of S, so the planner sizes them with one partition to spare).
+CONFIGS["d256_window4096_b8_bf16"] = dataclasses.replace(
+    CONFIGS["d256_window4096_bf16"], name="d256_window4096_b8_bf16", batch=8,
+    context_lens=[8192] * 8, num_pages=4096, seed=9)
+
 # Rotary embedding in the kernel (rotary_mode 1; TVM PR #20426, "Correctness"),
 # with the frequency base 500000 of the Llama 3.x models the PR measures.
 for _base in ("llama1b_ctx3060_f16", "llama8b_b16_ragged_f16", "ctx100k_gqa6_f16",
@@ -119,10 +125,11 @@ for _base in ("llama1b_ctx3060_f16", "llama8b_b16_ragged_f16", "ctx100k_gqa6_f16
 # The five workloads in the order they are usually listed.
 CONFIG_ORDER = ["tiny_gqa4_f32", "llama1b_ctx3060_f16", "llama8b_b16_ragged_f16",
                 "d256_window4096_bf16", "ctx100k_gqa6_f16"]
-# Further shapes (head_dim 96; rotary embedding), measured but not part of the five.
+# Further shapes (head_dim 96; rotary embedding; a larger windowed batch), measured but not
+# part of the five.
 EXTRA_ORDER = ["d96_b16_ragged_f16", "d96_ctx32k_f16", "llama8b_ctx32k_f16",
                "llama1b_ctx3060_rope_f16", "llama8b_b16_ragged_rope_f16",
-               "ctx100k_gqa6_rope_f16", "llama8b_ctx32k_rope_f16"]
+               "ctx100k_gqa6_rope_f16", "llama8b_ctx32k_rope_f16", "d256_window4096_b8_bf16"]
 
 
 @dataclasses.dataclass

@@ -379,3 +379,41 @@ def test_plans_fill_their_wave_target_with_two_wave_workgroups(dtype, waves_per_
     target = 256 * min(waves_per_cu, 8)
     assert target * 0.9 <= waves <= target
     assert covered(p, 8192, 0)
+
+
+@pytest.mark.parametrize("batch,hq,hkv,D,ctx,win,wpc,old_wgs", [
+    (3, 8, 1, 64, 32768, 0, 16, 258),
+    (6, 8, 2, 128, 16384, 0, 12, 264),
+    (12, 8, 1, 64, 88064, 0, 16, 264),
+    (4, 32, 8, 128, 8192, 4096, 12, 288),
+    (8, 8, 4, 256, 8192, 4096, 8, 288),
+])
+def test_default_plans_keep_one_workgroup_per_compute_unit(batch, hq, hkv, D, ctx, win, wpc, old_wgs):
+    """Where rounding the partition count up would end the grid a little
+    past one 4-wave workgroup per compute unit (old_wgs on 256 units), the
+    planner takes a few more pages per wave instead, so that no unit runs
+    two: at most 256 workgroups, and the wave count stays near the target."""
+    dt = B.PA_DTYPE_BF16 if D == 256 else B.PA_DTYPE_F16
+    d = B.PaDecodeDesc(num_q_heads=hq, num_kv_heads=hkv, head_dim=D, page_size=16, dtype=dt,
+                       max_batch=64, max_context_len=1 << 20, device=0)
+    p = B.pa_decode_plan_query(d, 256, wpc, batch, ctx, win, 0)
+    wgs = p.grid_partial[0] * p.grid_partial[1] * p.grid_partial[2]
+    assert p.split == 1 and p.waves_per_group == 4
+    assert 256 * 3 // 4 <= wgs <= 256 < old_wgs
+    # every visible page is still covered
+    visible = min(ctx, win) if win else ctx
+    assert p.num_partitions * p.partition_size >= visible
+
+
+@pytest.mark.parametrize("name", ["llama1b_ctx3060_f16", "d256_window4096_bf16"])
+def test_default_plans_of_the_benchmark_shapes_are_unchanged(name):
+    """The 3060-token and windowed head_dim-256 plans (measured best in
+    their sweeps) are what the grid rule leaves them."""
+    w = W.CONFIGS[name]
+    d = B.make_desc(w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype, max_batch=64,
+                    max_context_len=1 << 20)
+    p = B.pa_decode_plan_query(d, 256, 16 if w.head_dim == 64 else 8, w.batch,
+                               max(w.context_lens), w.window, 0)
+    expect = {"llama1b_ctx3060_f16": (128, 24, [24, 8, 1]),
+              "d256_window4096_bf16": (320, 14, [14, 4, 4])}[name]
+    assert (p.partition_size, p.num_partitions, list(p.grid_partial)) == expect

@@ -357,3 +357,11 @@ def test_aliased_pages_in_the_dense_table():
     pt[1, :40] = pt[0, :40]          # 640 shared tokens, then its own pages
     pt[2, :25] = pt[0, :25]          # the whole of sequence 2 is a prefix of sequence 0
     _check(dataclasses.replace(p, page_table=pt), what="aliased pages")
+
+
+def test_windowed_batch8_full_size():
+    """The windowed head_dim-256 shape at batch 8, whose partitions the
+    planner sizes with one to spare for an unaligned window start (640
+    tokens, 8 partitions), at full size against the oracle."""
+    p = W.generate(W.CONFIGS["d256_window4096_b8_bf16"])
+    _check(p, what="d256 window batch 8")
