@@ -114,6 +114,14 @@ CONFIGS["d256_window4096_b8_bf16"] = dataclasses.replace(
     CONFIGS["d256_window4096_bf16"], name="d256_window4096_b8_bf16", batch=8,
     context_lens=[8192] * 8, num_pages=4096, seed=9)
 
+# Uniform serving-style batches of Llama-3.1-8B heads (fixed partitions).
+CONFIGS["llama8b_b64_ctx1000_f16"] = Workload(
+    name="llama8b_b64_ctx1000_f16", batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
+    dtype=torch.float16, context_lens=[1000] * 64, num_pages=64 * 63, seed=10)
+CONFIGS["llama8b_b32_ctx2048_f16"] = Workload(
+    name="llama8b_b32_ctx2048_f16", batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128,
+    dtype=torch.float16, context_lens=[2048] * 32, num_pages=32 * 128, seed=11)
+
 # Rotary embedding in the kernel (rotary_mode 1; TVM PR #20426, "Correctness"),
 # with the frequency base 500000 of the Llama 3.x models the PR measures.
 for _base in ("llama1b_ctx3060_f16", "llama8b_b16_ragged_f16", "ctx100k_gqa6_f16",
@@ -125,11 +133,12 @@ for _base in ("llama1b_ctx3060_f16", "llama8b_b16_ragged_f16", "ctx100k_gqa6_f16
 # The five workloads in the order they are usually listed.
 CONFIG_ORDER = ["tiny_gqa4_f32", "llama1b_ctx3060_f16", "llama8b_b16_ragged_f16",
                 "d256_window4096_bf16", "ctx100k_gqa6_f16"]
-# Further shapes (head_dim 96; rotary embedding; a larger windowed batch), measured but not
-# part of the five.
+# Further shapes (head_dim 96; rotary embedding; a larger windowed batch; uniform
+# serving batches), measured but not part of the five.
 EXTRA_ORDER = ["d96_b16_ragged_f16", "d96_ctx32k_f16", "llama8b_ctx32k_f16",
                "llama1b_ctx3060_rope_f16", "llama8b_b16_ragged_rope_f16",
-               "ctx100k_gqa6_rope_f16", "llama8b_ctx32k_rope_f16", "d256_window4096_b8_bf16"]
+               "ctx100k_gqa6_rope_f16", "llama8b_ctx32k_rope_f16", "d256_window4096_b8_bf16",
+               "llama8b_b64_ctx1000_f16", "llama8b_b32_ctx2048_f16"]
 
 
 @dataclasses.dataclass
