@@ -365,3 +365,18 @@ def test_windowed_batch8_full_size():
     tokens, 8 partitions), at full size against the oracle."""
     p = W.generate(W.CONFIGS["d256_window4096_b8_bf16"])
     _check(p, what="d256 window batch 8")
+
+
+@pytest.mark.parametrize("D,dtype,hkv,G,lens,window", [
+    (64, torch.float16, 1, 8, [32768] * 3, 0),                      # S 448, 222 workgroups
+    (128, torch.float16, 2, 4, [16384, 9000, 16384, 1, 16384, 12345], 0),
+    (128, torch.bfloat16, 8, 4, [8192, 8192, 7000, 8192], 4096),     # S 640, 256 workgroups
+    (96, torch.float16, 8, 2, [25314, 100, 20000, 25314, 17], 0),
+])
+def test_layouts_of_the_grid_rule(D, dtype, hkv, G, lens, window):
+    """Shapes where the planner takes more pages per wave than its first
+    count so that the grid stays within one workgroup per compute unit: the
+    partitions it then draws still give the oracle's result."""
+    w = W.custom(batch=len(lens), num_q_heads=G * hkv, num_kv_heads=hkv, head_dim=D, dtype=dtype,
+                 context_lens=lens, seed=940 + D + hkv, window=window)
+    _check(W.generate(w), what="grid rule D=%d hkv=%d B=%d" % (D, hkv, len(lens)))
