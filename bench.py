@@ -486,7 +486,7 @@ def main():
     ap.add_argument("--workload", default="llama1b_ctx3060_f16",
                     choices=W.CONFIG_ORDER + W.EXTRA_ORDER)
     ap.add_argument("--also", default="ctx100k_gqa6_f16,llama8b_b16_ragged_f16,d256_window4096_bf16,"
-                    "llama8b_ctx32k_rope_f16",
+                    "llama8b_ctx32k_rope_f16,llama8b_b64_ctx1000_f16",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--also-steps", type=int, default=300)
     ap.add_argument("--replicas", type=int, default=None)
