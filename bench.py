@@ -810,7 +810,8 @@ def copy_probe(nbytes, steps, warmup):
 # Profiling evidence: the rocprofv3 runs behind profiles/ and their summary.
 # ---------------------------------------------------------------------------
 PROFILED = ["llama1b_ctx3060_f16", "llama8b_b16_ragged_f16", "d256_window4096_bf16",
-            "ctx100k_gqa6_f16", "llama8b_ctx32k_rope_f16", "ctx100k_gqa6_rope_f16"]
+            "ctx100k_gqa6_f16", "llama8b_ctx32k_rope_f16", "ctx100k_gqa6_rope_f16",
+            "llama8b_b64_ctx1000_f16"]
 COPY_BYTES = 256 << 20
 # Counter passes of every profiled workload (one rocprofv3 --pmc run each; at
 # most 8 SQ and 4 TCC counters per run).
