@@ -320,6 +320,22 @@ int make_plan(const pa_decode_desc& d, int num_cus, int waves_per_cu, const Plan
         int nw = nw0;
         if (!split || units * P < int64_t(num_cus) * 2)
             nw = wpp;
+        // head_dim 256, a grid of 4-wave partitions a little past one per
+        // compute unit: two waves per partition and two partitions per
+        // workgroup instead, when that fits one workgroup per unit.  The
+        // doubled-up units run two waves per SIMD, and at head_dim 256 (8 KiB
+        // K and V blocks) a unit streams no faster with eight waves than with
+        // four; measured on MI355X with fixed partition sizes, 13-17 % faster
+        // per step (batch 2 x 32k tokens, S 1008: 63.1 against 52.6 us;
+        // batch 4 x 8k, S 496: 33.8 against 28.9; window 4096 at batch 8,
+        // S 512: 33.8 against 29.4).  Head_dim 64 and 128 gain from the
+        // second wave per SIMD and keep four waves per partition (1-6 %).
+        if (d.head_dim == 256 && split && nw0 == 4 && wpp == 4 && tune.waves_per_partition <= 0 &&
+            tune.waves_per_group <= 0 && units * P > num_cus && units * P < int64_t(num_cus) * 2 &&
+            units * ceil_div(P, 2) <= num_cus) {
+            wpp = 2;
+            nw = 4;
+        }
         // Experiments only: an override of the workgroup size (a multiple of
         // the waves per partition, so that the workgroup splits into whole
         // slots).

@@ -417,3 +417,26 @@ def test_default_plans_of_the_benchmark_shapes_are_unchanged(name):
     expect = {"llama1b_ctx3060_f16": (128, 24, [24, 8, 1]),
               "d256_window4096_bf16": (320, 14, [14, 4, 4])}[name]
     assert (p.partition_size, p.num_partitions, list(p.grid_partial)) == expect
+
+
+@pytest.mark.parametrize("hq,batch,ctx,S,window,dtype,P", [
+    (8, 4, 8192, 496, 0, B.PA_DTYPE_BF16, 17),
+    (24, 2, 32768, 1008, 0, B.PA_DTYPE_F16, 33),
+    (8, 8, 8192, 512, 4096, B.PA_DTYPE_BF16, 9),
+])
+def test_head_dim_256_fixed_partitions_past_one_workgroup_per_unit(hq, batch, ctx, S, window, dtype, P):
+    """head_dim 256 with a caller's partition size whose 4-wave partitions
+    would number a little more than the 256 compute units: two waves per
+    partition, two partitions per 4-wave workgroup, within one workgroup
+    per unit.  The same counts at head_dim 128 keep four waves per
+    partition."""
+    d = B.PaDecodeDesc(num_q_heads=hq, num_kv_heads=4, head_dim=256, page_size=16, dtype=dtype,
+                       max_batch=64, max_context_len=1 << 20, device=0)
+    p = B.pa_decode_plan_query(d, 256, 8, batch, ctx, window, S)
+    wgs = p.grid_partial[0] * p.grid_partial[1] * p.grid_partial[2]
+    assert p.num_partitions == P and 256 < 4 * batch * P < 512
+    assert (p.waves_per_partition, p.waves_per_group) == (2, 4) and wgs <= 256
+    d128 = B.PaDecodeDesc(num_q_heads=hq, num_kv_heads=4, head_dim=128, page_size=16,
+                          dtype=B.PA_DTYPE_F16, max_batch=64, max_context_len=1 << 20, device=0)
+    q = B.pa_decode_plan_query(d128, 256, 12, batch, ctx, window, S)
+    assert q.num_partitions == P and q.waves_per_partition == 4

@@ -380,3 +380,11 @@ def test_layouts_of_the_grid_rule(D, dtype, hkv, G, lens, window):
     w = W.custom(batch=len(lens), num_q_heads=G * hkv, num_kv_heads=hkv, head_dim=D, dtype=dtype,
                  context_lens=lens, seed=940 + D + hkv, window=window)
     _check(W.generate(w), what="grid rule D=%d hkv=%d B=%d" % (D, hkv, len(lens)))
+
+
+def test_head_dim_256_two_partitions_per_workgroup():
+    """head_dim 256, a fixed partition size whose partitions the planner
+    packs two to a workgroup with two waves each: the oracle's result."""
+    w = W.custom(batch=4, num_q_heads=8, num_kv_heads=4, head_dim=256, dtype=torch.bfloat16,
+                 context_lens=[8192, 8000, 8192, 5000], seed=961)
+    _check(W.generate(w), S=496, what="d256 fixed S 496")
