@@ -440,3 +440,46 @@ def test_head_dim_256_fixed_partitions_past_one_workgroup_per_unit(hq, batch, ct
                           dtype=B.PA_DTYPE_F16, max_batch=64, max_context_len=1 << 20, device=0)
     q = B.pa_decode_plan_query(d128, 256, 12, batch, ctx, window, S)
     assert q.num_partitions == P and q.waves_per_partition == 4
+
+
+def test_plan_invariants_on_random_shapes():
+    """Seeded random shapes (head_dim, dtype, heads, batch, context bound,
+    window, automatic or fixed partition size, compute units and resident
+    waves): every plan covers every context length up to its bound, its
+    grid and workgroup sizes are consistent, its partitions are whole pages,
+    and an automatic plan never takes more than 256 pages per wave."""
+    import random
+    r = random.Random(20261203)
+    for _ in range(400):
+        D = r.choice([64, 96, 128, 256])
+        dt = r.choice([B.PA_DTYPE_F16, B.PA_DTYPE_BF16] + ([B.PA_DTYPE_F32] if D == 64 else []))
+        hkv = r.choice([1, 2, 4, 8])
+        G = r.choice([1, 2, 4, 6, 8])
+        batch = r.choice([1, 2, 3, 5, 8, 12, 16, 24, 48])
+        max_ctx = r.choice([1, 17, 300, 3060, r.randint(1, 40000), r.randint(40000, 200000)])
+        window = r.choice([0, 0, r.randint(1, 5000)])
+        S = r.choice([0, 0, 16 * r.randint(1, 64)])
+        cus = r.choice([256, 304, 80])
+        wpc = r.choice([4, 8, 12, 16])
+        d = B.make_desc(G * hkv, hkv, D, dt, max_batch=64, max_context_len=1 << 20)
+        p = B.pa_decode_plan_query(d, cus, wpc, batch, max_ctx, window, S)
+        what = (D, dt, hkv, G, batch, max_ctx, window, S, cus, wpc, p.as_dict())
+        assert p.partition_size > 0 and p.partition_size % 16 == 0, what
+        if S:
+            assert p.partition_size == S, what
+        elif p.split:
+            assert p.partition_size <= 4 * 256 * 16, what
+        for n in {0, 1, max_ctx // 3, max_ctx - 1, max_ctx}:
+            if 0 <= n <= max_ctx:
+                assert covered(p, n, window), what
+        assert p.split == (1 if p.num_partitions > 1 else 0), what
+        assert p.waves_per_partition in (1, 2, 4), what
+        assert p.waves_per_group % p.waves_per_partition == 0, what
+        slots = p.waves_per_group // p.waves_per_partition
+        assert p.grid_partial[0] == -(-p.num_partitions // slots), what
+        assert list(p.grid_partial[1:]) == [hkv, batch], what
+        assert p.block_partial == 64 * p.waves_per_group, what
+        if p.split:
+            assert p.workspace_bytes >= batch * G * hkv * p.num_partitions * (D + 2) * 4, what
+        else:
+            assert p.workspace_bytes == 0, what
